@@ -1,0 +1,126 @@
+"""FP8 e4m3 codec and per-tile quantiser.
+
+Follows the FPSAttention summary page, "Approach": FP8 quantisation and block
+sparsity share one 3D tile granularity. The pages name neither the FP8 format
+nor the rounding; readings taken:
+  * format: OCP FP8 E4M3 ("fn"): 1 sign, 4 exponent bits (bias 7), 3 mantissa
+    bits, subnormals, no infinities, S.1111.111 is NaN, largest finite 448;
+  * one scale per (tensor, batch, head, tile) over every channel of the
+    tile's real tokens; a = absmax, stored scale = fl32(a / 448);
+  * codes: inv = fl32(448 / a), y = fl32(x * inv), code = round-to-nearest-
+    even of y to e4m3, saturating at +-448; the sign bit follows the fp32
+    sign bit (so negative values that round to zero give 0x80);
+  * a = 0 gives scale 0 and all-zero codes;
+  * dequantised value = decode(code) * scale.
+All quantiser arithmetic is float32 on purpose: the reading fixes the
+operation sequence in fp32, which makes the codes exactly reproducible.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layout import Layout, token_order
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of one e4m3 code, straight from the bit-field definition."""
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    sign = -1.0 if s else 1.0
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def decode_table() -> np.ndarray:
+    """All 256 code values (float64; NaN for the two NaN codes)."""
+    return np.array([e4m3_decode(c) for c in range(256)])
+
+
+_POS = np.array([e4m3_decode(c) for c in range(0x7F)])   # codes 0x00..0x7E, ascending
+
+
+def e4m3_encode(x) -> int:
+    """Round one float32 value to the nearest e4m3 code (ties to even), saturating."""
+    x = np.float32(x)
+    if np.isnan(x):
+        return 0x7F
+    neg = bool(np.signbit(x))
+    a = float(abs(x))
+    if a >= E4M3_MAX:
+        code = 0x7E
+    else:
+        hi = int(np.searchsorted(_POS, a, side="left"))     # _POS[hi] >= a
+        if _POS[hi] == a:
+            code = hi
+        else:
+            lo = hi - 1
+            dlo, dhi = a - _POS[lo], _POS[hi] - a
+            if dlo < dhi:
+                code = lo
+            elif dhi < dlo:
+                code = hi
+            else:                      # exact midpoint: even mantissa wins
+                code = lo if (lo & 1) == 0 else hi
+    return code | (0x80 if neg else 0)
+
+
+def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
+    """Vectorised form of e4m3_encode over a float32 array (same rule)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    neg = np.signbit(y)
+    hi = np.searchsorted(_POS, np.minimum(a, E4M3_MAX), side="left")
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS[lo]
+    dhi = _POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1))
+    code = np.where(_POS[hi] == a, hi, np.where(pick_hi, hi, lo))
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    code = np.where(np.isnan(y), 0x7F, code | np.where(neg, 0x80, 0))
+    return code.astype(np.uint8)
+
+
+def quantize_tiles(x_tiled: np.ndarray, lay: Layout):
+    """Per-tile e4m3 quantisation of a tiled tensor [B, heads, N_pad, d].
+
+    Returns (codes uint8 [B, heads, N_pad, d], scales float32 [B, heads, n_tiles]).
+    """
+    order = token_order(lay).reshape(lay.n_tiles, lay.tile_tokens)
+    B = x_tiled.shape[0]
+    C, d = lay.tile_tokens, lay.head_dim
+    x = np.asarray(x_tiled, dtype=np.float32).reshape(B, lay.heads, lay.n_tiles, C, d)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros((B, lay.heads, lay.n_tiles), dtype=np.float32)
+    f448 = np.float32(E4M3_MAX)
+    for t in range(lay.n_tiles):
+        real = order[t] >= 0
+        xt = x[:, :, t][:, :, real]                        # [B, heads, n_real, d]
+        amax = np.abs(xt).max(axis=(2, 3)).astype(np.float32)   # [B, heads]
+        for b in range(B):
+            for h in range(lay.heads):
+                a = amax[b, h]
+                if a == 0:
+                    continue
+                inv = np.float32(f448 / a)
+                y = (x[b, h, t] * inv).astype(np.float32)
+                y[~real] = 0.0
+                codes[b, h, t] = e4m3_encode_array(y)
+                scales[b, h, t] = np.float32(a / f448)
+    return codes.reshape(B, lay.heads, lay.n_padded, d), scales
+
+
+def dequantize_tiles(codes: np.ndarray, scales: np.ndarray, lay: Layout) -> np.ndarray:
+    """decode(code) * scale, in float64, [B, heads, N_pad, d]."""
+    table = decode_table()
+    B = codes.shape[0]
+    v = table[codes.astype(np.int64)].reshape(B, lay.heads, lay.n_tiles, lay.tile_tokens,
+                                              lay.head_dim)
+    v = v * scales.astype(np.float64)[:, :, :, None, None]
+    return v.reshape(B, lay.heads, lay.n_padded, lay.head_dim)

@@ -1,0 +1,99 @@
+"""Pins for the oracle's token layout (permute / unpermute)."""
+import numpy as np
+import pytest
+
+from oracle import layout as L
+from oracle.layout import Layout
+from synth import CONFIGS
+from tests.conftest import read_golden
+
+
+def _layout_of(cfg, heads=None, d=None):
+    return Layout(T=cfg.T, H=cfg.H, W=cfg.W, heads=heads or cfg.heads, head_dim=d or cfg.head_dim,
+                  kind=cfg.kind, tile=cfg.tile, stride=cfg.stride)
+
+
+@pytest.mark.parametrize("line", read_golden("permute_orders.txt"))
+def test_golden_orders(line):
+    spec, expected = line.split(":")
+    f = spec.split()
+    kind = f[0]
+    T, H, W, tt, th, tw, sh, sw = map(int, f[1:])
+    lay = Layout(T=T, H=H, W=W, heads=1, head_dim=1, kind=kind, tile=(tt, th, tw), stride=(sh, sw))
+    assert L.token_order(lay).tolist() == [int(x) for x in expected.split()]
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_order_is_bijection_on_real_tokens(name):
+    cfg = CONFIGS[name]
+    lay = _layout_of(cfg)
+    order = L.token_order(lay)
+    real = order[order >= 0]
+    assert np.array_equal(np.sort(real), np.arange(lay.n_tokens))
+    assert order.size == lay.n_padded
+    assert lay.n_padded % lay.tile_tokens == 0
+
+
+def test_padded_sizes_of_workloads():
+    # padded token counts implied by padding each axis to the tile extent
+    expect = {"tiny_window_f32": (256, 8), "topk32_16x32x32": (16384, 256),
+              "window_480p": (39936, 624), "skiparse_768p": (80640, 1260),
+              "fp8_topp_720p": (92160, 1440)}
+    for name, (npad, ntiles) in expect.items():
+        lay = _layout_of(CONFIGS[name])
+        assert (lay.n_padded, lay.n_tiles) == (npad, ntiles), name
+
+
+@pytest.mark.parametrize("name", ["tiny_window_f32", "window_480p", "fp8_topp_720p"])
+def test_tile3d_positions_fall_in_their_tile_box(name):
+    # independent derivation: tiled position p sits in tile p // C, whose box is
+    # [a*tt, a*tt+tt) x [b*th, ...) x [c*tw, ...); within-tile offset is row-major
+    cfg = CONFIGS[name]
+    lay = _layout_of(cfg)
+    order = L.token_order(lay)
+    tt, th, tw = lay.tile
+    nt, nh, nw = lay.tile_grid
+    C = lay.tile_tokens
+    rng = np.random.default_rng(0)
+    for p in rng.integers(0, lay.n_padded, size=2000):
+        tile, off = divmod(int(p), C)
+        a, rem = divmod(tile, nh * nw)
+        b, c = divmod(rem, nw)
+        i, rem = divmod(off, th * tw)
+        j, k = divmod(rem, tw)
+        t, h, w = a * tt + i, b * th + j, c * tw + k
+        if t < lay.T and h < lay.H and w < lay.W:
+            assert order[p] == (t * lay.H + h) * lay.W + w
+        else:
+            assert order[p] == -1
+
+
+def test_skiparse_groups_hold_one_residue():
+    cfg = CONFIGS["skiparse_768p"]
+    lay = _layout_of(cfg)
+    order = L.token_order(lay)
+    per_group = lay.tiles_per_group * lay.tile_tokens
+    assert lay.tiles_per_group == 315 and per_group == 20160
+    for g in range(4):
+        toks = order[g * per_group:(g + 1) * per_group]
+        toks = toks[toks >= 0]
+        h = (toks // lay.W) % lay.H
+        w = toks % lay.W
+        assert np.all(h % 2 == g // 2) and np.all(w % 2 == g % 2)
+        assert np.all(np.diff(toks) > 0)      # row-major inside the group
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_permute_unpermute_identity_and_zero_pads(name):
+    cfg = CONFIGS[name]
+    lay = _layout_of(cfg, heads=2, d=8)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, lay.n_tokens, 2, 8)).astype(np.float32)
+    xt = L.permute(x, lay)
+    assert xt.shape == (2, 2, lay.n_padded, 8)
+    order = L.token_order(lay)
+    assert np.all(xt[:, :, order < 0, :] == 0)
+    assert np.array_equal(L.unpermute(xt, lay), x)
+    # spot check the gather direction on a few positions
+    for p in np.nonzero(order >= 0)[0][:50]:
+        assert np.array_equal(xt[1, 0, p], x[1, order[p], 0])
