@@ -1,0 +1,190 @@
+"""Block-sparse video attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of libvsa.so (include/vsa.h). Every step
+of the computation runs in the library's HIP kernels; this module only turns
+torch tensors into device pointers, allocates outputs with torch and passes
+torch's current HIP stream. There is no CPU fallback: if the library is not
+built, importing the binding raises.
+
+Pages the operations follow: "FPSAttention: Training-Aware FP8 and Sparsity
+Co-Design for Fast Video Diffusion" (Approach), the "OSP-Next" model card
+(Model Summary), "Faster Video Diffusion with Trainable Sparse Attention"
+(Research Type row) and the FVAttn summary.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_SKIPARSE2D, VSA_TILE3D,
+                   VsaError, VsaLayout, VsaLayoutInfo, check, lib)
+
+__all__ = [
+    "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
+    "quant_fp8_tiles", "block_sparse_attn_fwd", "VsaError", "EXPORTED",
+    "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_TILE3D", "VSA_SKIPARSE2D",
+]
+
+
+@dataclass(frozen=True)
+class Layout:
+    """Mirror of vsa_layout. kind: "tile3d" or "skiparse2d"."""
+    T: int
+    H: int
+    W: int
+    heads: int
+    head_dim: int
+    kind: str = "tile3d"
+    tile: Tuple[int, int, int] = (4, 4, 4)
+    stride: Tuple[int, int] = (2, 2)
+    batch: int = 1
+
+    def c(self) -> VsaLayout:
+        return VsaLayout(self.batch, self.heads, self.head_dim, self.T, self.H, self.W,
+                         VSA_SKIPARSE2D if self.kind == "skiparse2d" else VSA_TILE3D,
+                         self.tile[0], self.tile[1], self.tile[2], self.stride[0], self.stride[1])
+
+
+def layout_info(lay: Layout) -> VsaLayoutInfo:
+    info = VsaLayoutInfo()
+    c = lay.c()
+    check(lib().vsa_layout_query(ctypes.byref(c), ctypes.byref(info)))
+    return info
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DT = {torch.float32: VSA_F32, torch.bfloat16: VSA_BF16}
+
+
+def tile_permute(lay: Layout, src: torch.Tensor, inverse: bool = False,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Natural [B, T*H*W, heads, d] <-> tiled [B, heads, n_padded, d] (vsa_tile_permute)."""
+    info = layout_info(lay)
+    if out is None:
+        shape = ((lay.batch, info.n_tokens, lay.heads, lay.head_dim) if inverse
+                 else (lay.batch, lay.heads, info.n_padded, lay.head_dim))
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    c = lay.c()
+    check(lib().vsa_tile_permute(ctypes.byref(c), _DT.get(src.dtype, -1), _ptr(src), _ptr(out),
+                                 1 if inverse else 0, _stream(stream)))
+    return out
+
+
+def build_mask_window(lay: Layout, radius: Tuple[int, int, int], max_kv: Optional[int] = None,
+                      device="cuda", stream=None):
+    """Head-invariant fixed lists (vsa_build_mask_window): (kv_idx [n_tiles, max_kv], kv_cnt)."""
+    info = layout_info(lay)
+    if max_kv is None:
+        max_kv = info.n_tiles
+    kv_idx = torch.empty((info.n_tiles, max_kv), dtype=torch.int32, device=device)
+    kv_cnt = torch.empty((info.n_tiles,), dtype=torch.int32, device=device)
+    c = lay.c()
+    check(lib().vsa_build_mask_window(ctypes.byref(c), int(radius[0]), int(radius[1]),
+                                      int(radius[2]), int(max_kv), _ptr(kv_idx), _ptr(kv_cnt),
+                                      _stream(stream)))
+    return kv_idx, kv_cnt
+
+
+def topk_workspace_bytes(lay: Layout) -> int:
+    c = lay.c()
+    return int(lib().vsa_build_mask_topk_workspace(ctypes.byref(c)))
+
+
+def build_mask_topk(lay: Layout, q_tiled: torch.Tensor, k_tiled: torch.Tensor,
+                    coarse_scale: Optional[float] = None, top_k: int = 0, top_p: float = 0.0,
+                    k_floor: int = 0, max_kv: Optional[int] = None, want_scores: bool = False,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """Routed lists per (b, head) (vsa_build_mask_topk): (kv_idx, kv_cnt, scores or None)."""
+    info = layout_info(lay)
+    n = info.n_tiles
+    if coarse_scale is None:
+        coarse_scale = 1.0 / math.sqrt(lay.head_dim)
+    if max_kv is None:
+        max_kv = n if top_p > 0 else min(top_k, n)
+    dev = q_tiled.device
+    kv_idx = torch.empty((lay.batch, lay.heads, n, max_kv), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty((lay.batch, lay.heads, n), dtype=torch.int32, device=dev)
+    scores = torch.empty((lay.batch, lay.heads, n, n), dtype=torch.float32, device=dev) \
+        if want_scores else None
+    need = topk_workspace_bytes(lay)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    c = lay.c()
+    check(lib().vsa_build_mask_topk(ctypes.byref(c), _ptr(q_tiled), _ptr(k_tiled),
+                                    float(coarse_scale), int(top_k), float(top_p), int(k_floor),
+                                    int(max_kv), _ptr(kv_idx), _ptr(kv_cnt), _ptr(scores),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return kv_idx, kv_cnt, scores
+
+
+def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None):
+    """Per-tile e4m3 codes (uint8, same shape) and scales [B, heads, n_tiles] (vsa_quant_fp8_tiles)."""
+    info = layout_info(lay)
+    codes = torch.empty(x_tiled.shape, dtype=torch.uint8, device=x_tiled.device)
+    scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32,
+                         device=x_tiled.device)
+    c = lay.c()
+    check(lib().vsa_quant_fp8_tiles(ctypes.byref(c), _ptr(x_tiled), _ptr(codes), _ptr(scales),
+                                    _stream(stream)))
+    return codes, scales
+
+
+def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          kv_idx: Optional[torch.Tensor] = None,
+                          kv_cnt: Optional[torch.Tensor] = None,
+                          softmax_scale: Optional[float] = None,
+                          scales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                          want_lse: bool = False, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, stream=None):
+    """Block-sparse attention forward (vsa_block_sparse_attn_fwd).
+
+    q/k/v tiled; float32 -> float32 out, bfloat16 -> bfloat16 out, uint8 e4m3
+    codes (with ``scales`` = (q_scale, k_scale, v_scale)) -> bfloat16 out.
+    kv_idx 2-D [n_tiles, max_kv] = one shared table; 4-D [B, heads, n_tiles,
+    max_kv] = per-(b, head) lists; None = dense. Returns (out, lse or None).
+    """
+    info = layout_info(lay)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    if q.dtype == torch.uint8:
+        dtype, odt = VSA_FP8_E4M3, torch.bfloat16
+        if scales is None:
+            raise ValueError("fp8 codes need (q_scale, k_scale, v_scale)")
+    else:
+        dtype, odt = _DT.get(q.dtype, -1), q.dtype
+    if out is None:
+        out = torch.empty((lay.batch, lay.heads, info.n_padded, lay.head_dim), dtype=odt,
+                          device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((lay.batch, lay.heads, info.n_padded), dtype=torch.float32,
+                          device=q.device)
+    if kv_idx is not None:
+        max_kv = kv_idx.shape[-1]
+        list_mode = 0 if kv_idx.dim() == 2 else 1
+    else:
+        max_kv, list_mode = 0, 0
+    qs, ks, vs = scales if scales is not None else (None, None, None)
+    c = lay.c()
+    check(lib().vsa_block_sparse_attn_fwd(
+        ctypes.byref(c), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs),
+        _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode, float(softmax_scale), _ptr(out),
+        _ptr(lse), _stream(stream)))
+    return out, lse

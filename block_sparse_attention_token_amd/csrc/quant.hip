@@ -1,0 +1,108 @@
+// S5: per-tile fp8 e4m3 quantiser (FPSAttention, Approach: FP8 quantisation
+// on the same 3D tiles as the block sparsity).
+//
+// Per (batch, head, tile): a = absmax over real rows and all channels,
+// scale = fl32(a / 448), code = RNE_e4m3(fl32(x * fl32(448 / a))) saturating
+// at +-448, sign taken from the fp32 sign bit. Every step is a correctly
+// rounded fp32 operation or exact integer work, so codes are reproducible
+// bit for bit.
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// OCP E4M3 encode of one fp32 value, round to nearest even, saturating.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;                                   // NaN
+  } else if (a >= 0x43E00000u) {                    // |y| >= 448 (and inf): saturate
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {                    // |y| >= 2^-6: normal e4m3
+    // keep exponent + 3 mantissa bits, round the 20 dropped bits to nearest even
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);                         // rebias 127 -> 7
+  } else {                                          // subnormal: multiples of 2^-9
+    const float m = rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE to integer
+    code = (uint32_t)m;                             // 0..8 (8 is the smallest normal)
+  }
+  return code | sign;
+}
+
+__global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint4* __restrict__ x,
+                                                         uint2* __restrict__ codes,
+                                                         float* __restrict__ scales) {
+  const int tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int b = blockIdx.z;
+  const int chunks = L.d >> 3;                      // 8 bf16 per 16-byte chunk
+  const int total = L.C * chunks;
+  const long long row0 = (long long)(b * L.heads + head) * L.n_padded + (long long)tile * L.C;
+  const TileValid tv = tile_valid(L, tile);
+
+  __shared__ float red[kThreads / 64];
+  float amax = 0.0f;
+  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+    const int r = idx / chunks;
+    if (!row_is_real(L, tv, r)) continue;
+    const uint4 w = x[(row0 + r) * chunks + (idx - r * chunks)];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(bf16_lo(ws[e])));
+      amax = fmaxf(amax, fabsf(bf16_hi(ws[e])));
+    }
+  }
+  // wavefront then workgroup max (max is order-independent, so exact)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  float a = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+
+  const float inv = (a > 0.0f) ? __fdiv_rn(448.0f, a) : 0.0f;
+  if (threadIdx.x == 0) {
+    scales[(long long)(b * L.heads + head) * L.n_tiles + tile] =
+        (a > 0.0f) ? __fdiv_rn(a, 448.0f) : 0.0f;
+  }
+  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+    const int r = idx / chunks;
+    const long long off = (row0 + r) * chunks + (idx - r * chunks);
+    if (a == 0.0f || !row_is_real(L, tv, r)) {
+      codes[off] = make_uint2(0u, 0u);
+      continue;
+    }
+    const uint4 w = x[off];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
+      const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
+      packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
+    }
+    codes[off] = make_uint2(packed[0], packed[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
+                            hipStream_t s) {
+  dim3 grid(L.n_tiles, L.heads, L.B);
+  hipLaunchKernelGGL(quant_kernel, grid, dim3(kThreads), 0, s, L, static_cast<const uint4*>(x),
+                     reinterpret_cast<uint2*>(codes), scales);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

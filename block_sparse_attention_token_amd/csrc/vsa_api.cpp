@@ -1,0 +1,274 @@
+// C ABI of libvsa: argument checks, layout derivation and kernel dispatch.
+// Every check runs before any launch, so an error return means nothing was
+// written. Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+
+#include <algorithm>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/vsa.h"
+#include "vsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vsa_status fail(vsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+vsa_status fail(vsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+vsa_status ok() {
+  g_last_error.clear();
+  return VSA_OK;
+}
+
+vsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(VSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Derive every size of a layout; returns VSA_OK or an error (message set).
+vsa_status derive(const vsa_layout* lay, vsa::DevLayout* L, vsa_layout_info* info) {
+  if (!lay) return fail(VSA_ERR_INVALID, "layout is NULL");
+  if (lay->batch < 1 || lay->heads < 1 || lay->head_dim < 1)
+    return fail(VSA_ERR_INVALID, "batch, heads and head_dim must be >= 1");
+  if (lay->T < 1 || lay->H < 1 || lay->W < 1) return fail(VSA_ERR_INVALID, "T, H, W must be >= 1");
+  if (lay->tile_t < 1 || lay->tile_h < 1 || lay->tile_w < 1)
+    return fail(VSA_ERR_INVALID, "tile extents must be >= 1");
+  const long long C = (long long)lay->tile_t * lay->tile_h * lay->tile_w;
+  const long long n_tokens = (long long)lay->T * lay->H * lay->W;
+  if (C > 4096) return fail(VSA_ERR_INVALID, "tile of %lld tokens exceeds 4096", C);
+  vsa::DevLayout d{};
+  d.B = lay->batch;
+  d.heads = lay->heads;
+  d.d = lay->head_dim;
+  d.T = lay->T;
+  d.H = lay->H;
+  d.W = lay->W;
+  d.kind = lay->kind;
+  d.tt = lay->tile_t;
+  d.th = lay->tile_h;
+  d.tw = lay->tile_w;
+  d.sh = 1;
+  d.sw = 1;
+  d.C = (int)C;
+  d.n_tokens = n_tokens;
+  long long n_tiles;
+  if (lay->kind == VSA_TILE3D) {
+    d.ntt = (lay->T + lay->tile_t - 1) / lay->tile_t;
+    d.nth = (lay->H + lay->tile_h - 1) / lay->tile_h;
+    d.ntw = (lay->W + lay->tile_w - 1) / lay->tile_w;
+    n_tiles = (long long)d.ntt * d.nth * d.ntw;
+    d.tiles_per_group = (int)n_tiles;
+    d.group_len = (int)n_tokens;
+  } else if (lay->kind == VSA_SKIPARSE2D) {
+    if (lay->stride_h < 1 || lay->stride_w < 1)
+      return fail(VSA_ERR_INVALID, "Skiparse strides must be >= 1");
+    if (lay->H % lay->stride_h || lay->W % lay->stride_w)
+      return fail(VSA_ERR_INVALID, "Skiparse needs H %% stride_h == 0 and W %% stride_w == 0");
+    d.sh = lay->stride_h;
+    d.sw = lay->stride_w;
+    const long long glen = (long long)lay->T * (lay->H / d.sh) * (lay->W / d.sw);
+    const long long tpg = (glen + C - 1) / C;
+    n_tiles = tpg * d.sh * d.sw;
+    d.tiles_per_group = (int)tpg;
+    d.group_len = (int)glen;
+  } else {
+    return fail(VSA_ERR_INVALID, "unknown layout kind %d", lay->kind);
+  }
+  if (n_tiles > (1 << 22)) return fail(VSA_ERR_INVALID, "too many tiles (%lld)", n_tiles);
+  d.n_tiles = (int)n_tiles;
+  d.n_padded = n_tiles * C;
+  // element offsets are computed in 64-bit; indices of rows per (b, head) fit 32-bit
+  if (d.n_padded >= (1ll << 31) || n_tokens >= (1ll << 31))
+    return fail(VSA_ERR_INVALID, "grid too large");
+  if (L) *L = d;
+  if (info) {
+    info->n_tokens = n_tokens;
+    info->n_padded = d.n_padded;
+    info->n_tiles = d.n_tiles;
+    info->tile_tokens = d.C;
+    info->n_groups = lay->kind == VSA_SKIPARSE2D ? d.sh * d.sw : 1;
+    info->tiles_per_group = d.tiles_per_group;
+    info->group_len = d.group_len;
+    info->tiles_t = lay->kind == VSA_TILE3D ? d.ntt : 0;
+    info->tiles_h = lay->kind == VSA_TILE3D ? d.nth : 0;
+    info->tiles_w = lay->kind == VSA_TILE3D ? d.ntw : 0;
+  }
+  return VSA_OK;
+}
+
+int longest_window_list(const vsa::DevLayout& L, int rt, int rh, int rw) {
+  if (rt < 0 || rh < 0 || rw < 0) return L.n_tiles;
+  if (L.kind == VSA_SKIPARSE2D) return L.tiles_per_group;
+  auto ax = [](int n, int r) { return (int)std::min<long long>(2ll * r + 1, n); };
+  return ax(L.ntt, rt) * ax(L.nth, rh) * ax(L.ntw, rw);
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_layout_query(const vsa_layout* layout, vsa_layout_info* info) {
+  if (!info) return fail(VSA_ERR_INVALID, "info is NULL");
+  const vsa_status st = derive(layout, nullptr, info);
+  return st == VSA_OK ? ok() : st;
+}
+
+vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void* src, void* dst,
+                            int32_t inverse, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!src || !dst) return fail(VSA_ERR_INVALID, "src and dst must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  int esize;
+  if (dtype == VSA_F32) esize = 4;
+  else if (dtype == VSA_BF16) esize = 2;
+  else return fail(VSA_ERR_UNSUPPORTED, "permute supports VSA_F32 and VSA_BF16 only");
+  if ((L.d * esize) % 16) return fail(VSA_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+  if (L.n_tiles > 65535 * 64 || L.heads > 65535 || L.B > 65535)
+    return fail(VSA_ERR_UNSUPPORTED, "grid too large for one launch");
+  return hip_status(vsa::launch_permute(L, esize, src, dst, inverse ? 1 : 0,
+                                        static_cast<hipStream_t>(stream)), "vsa_tile_permute");
+}
+
+vsa_status vsa_build_mask_window(const vsa_layout* layout, int32_t rt, int32_t rh, int32_t rw,
+                                 int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!kv_idx || !kv_cnt) return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must be non-NULL");
+  const int need = longest_window_list(L, rt, rh, rw);
+  if (max_kv < need) return fail(VSA_ERR_INVALID, "max_kv %d < longest list %d", max_kv, need);
+  return hip_status(vsa::launch_mask_window(L, rt, rh, rw, max_kv, kv_idx, kv_cnt,
+                                            static_cast<hipStream_t>(stream)),
+                    "vsa_build_mask_window");
+}
+
+size_t vsa_build_mask_topk_workspace(const vsa_layout* layout) {
+  vsa::DevLayout L;
+  if (derive(layout, &L, nullptr) != VSA_OK) return 0;
+  return vsa::route_workspace_bytes(L);
+}
+
+vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, const void* k_tiled,
+                               float coarse_scale, int32_t top_k, float top_p, int32_t k_floor,
+                               int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!q_tiled || !k_tiled || !kv_idx || !kv_cnt)
+    return fail(VSA_ERR_INVALID, "q_tiled, k_tiled, kv_idx and kv_cnt must be non-NULL");
+  if (!aligned16(q_tiled) || !aligned16(k_tiled)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (L.n_tiles > 4096) return fail(VSA_ERR_UNSUPPORTED, "routing supports at most 4096 tiles");
+  if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "routing needs head_dim <= 256, multiple of 8");
+  if (!isfinite(coarse_scale)) return fail(VSA_ERR_INVALID, "coarse_scale must be finite");
+  if (!(top_p <= 1.0f) || isnan(top_p)) return fail(VSA_ERR_INVALID, "top_p must be <= 1");
+  if (top_p > 0.0f) {
+    if (k_floor < 0) return fail(VSA_ERR_INVALID, "k_floor must be >= 0");
+    if (max_kv < L.n_tiles) return fail(VSA_ERR_INVALID, "top-p needs max_kv >= n_tiles (%d)", L.n_tiles);
+  } else {
+    if (top_k < 1) return fail(VSA_ERR_INVALID, "top_k must be >= 1 when top_p <= 0");
+    const int need = std::min(top_k, L.n_tiles);
+    if (max_kv < need) return fail(VSA_ERR_INVALID, "max_kv %d < %d", max_kv, need);
+  }
+  if (L.B * L.heads > 65535) return fail(VSA_ERR_UNSUPPORTED, "batch * heads too large");
+  const size_t need_ws = vsa::route_workspace_bytes(L);
+  if (!workspace || workspace_bytes < need_ws)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need_ws);
+  return hip_status(vsa::launch_route(L, q_tiled, k_tiled, coarse_scale, top_k, top_p, k_floor,
+                                      max_kv, kv_idx, kv_cnt, scores, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                    "vsa_build_mask_topk");
+}
+
+vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                               float* scales, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!x_tiled || !codes || !scales) return fail(VSA_ERR_INVALID, "x_tiled, codes and scales must be non-NULL");
+  if (!aligned16(x_tiled) || ((uintptr_t)codes & 7u)) return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (L.d % 8) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large");
+  return hip_status(vsa::launch_quant_fp8(L, x_tiled, codes, scales, static_cast<hipStream_t>(stream)),
+                    "vsa_quant_fp8_tiles");
+}
+
+vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
+                                     const void* k, const void* v, const float* q_scale,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_kv,
+                                     int32_t list_mode, float softmax_scale, void* out, float* lse,
+                                     void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !out) return fail(VSA_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr))
+    return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
+  if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
+  if (list_mode != 0 && list_mode != 1) return fail(VSA_ERR_INVALID, "list_mode must be 0 or 1");
+  if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
+  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3)
+    return fail(VSA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype == VSA_FP8_E4M3) {
+    if (!q_scale || !k_scale || !v_scale) return fail(VSA_ERR_INVALID, "fp8 needs q_scale, k_scale and v_scale");
+    if (L.C != 64 || L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "fp8 attention needs 64-token tiles and head_dim 128");
+  } else {
+    if (L.C != 32 && L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
+    if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
+  }
+  const long long work = (long long)L.B * L.heads * L.n_tiles;
+  if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  vsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = kv_idx ? max_kv : L.n_tiles;
+  a.list_mode = list_mode;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(vsa::launch_attn(L, dtype, a, static_cast<hipStream_t>(stream)),
+                    "vsa_block_sparse_attn_fwd");
+}
+
+const char* vsa_status_string(int32_t status) {
+  switch (status) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_INVALID: return "VSA_ERR_INVALID";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+    case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
+    case VSA_ERR_HIP: return "VSA_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* vsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* vsa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

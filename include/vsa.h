@@ -1,0 +1,211 @@
+/*
+ * vsa.h - C ABI of the block-sparse video attention library (libvsa.so).
+ *
+ * The library computes block-sparse self-attention over the 3D latent token
+ * grid (T x H x W) of a video diffusion transformer on AMD Instinct MI355X
+ * (gfx950). Tokens are regrouped into tiles, a per-query-tile list of key
+ * tiles is built (fixed window / Skiparse-2D pattern, or adaptive top-k /
+ * top-p routing over mean-pooled tiles), and a flash-style forward pass
+ * visits only the listed key/value tiles, in bf16 or in fp8 e4m3 with one
+ * scale per tile.
+ *
+ * Sources of each operation (titles and sections of the pages that define
+ * the method):
+ *   - "FPSAttention: Training-Aware FP8 and Sparsity Co-Design for Fast Video
+ *     Diffusion", Approach: FP8 quantisation and block sparsity on one shared
+ *     3D tile granularity; sliding tile windows.
+ *   - "OSP-Next" model card, Model Summary: Skiparse-2D, a fixed strided
+ *     sparse pattern applied along H and W, mixed with full attention.
+ *   - "Faster Video Diffusion with Trainable Sparse Attention" (VSA),
+ *     Research Type row: adaptive selection of key blocks per query block.
+ *   - "FVAttn" summary: Top-p routing with a Top-k safety floor over
+ *     video-aware blocks, per head.
+ *
+ * Conventions shared by every call:
+ *   - Ownership: every buffer is allocated and owned by the caller. Tensor
+ *     arguments are DEVICE pointers; vsa_layout / vsa_layout_info are HOST
+ *     structs passed by pointer and only read during the call. The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream). Calls
+ *     only enqueue work on it and never synchronise.
+ *   - Errors: every argument check runs on the host before any launch, so a
+ *     call that returns an error has written nothing. A failed launch returns
+ *     VSA_ERR_HIP. vsa_last_error() gives a thread-local message for the last
+ *     failing call on the calling thread.
+ *   - Layouts: tensors are dense and row-major in the shapes given below, and
+ *     base pointers must be 16-byte aligned.
+ *   - Natural order: token n = (t * H + h) * W + w. Tiled order: see
+ *     vsa_tile_permute.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----- status codes ------------------------------------------------------- */
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_INVALID = 1,      /* a null pointer, a bad size or an inconsistent argument */
+  VSA_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels implement */
+  VSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  VSA_ERR_HIP = 4           /* the HIP runtime reported an error on launch */
+} vsa_status;
+
+/* ----- element types ------------------------------------------------------ */
+typedef enum vsa_dtype {
+  VSA_F32 = 0,       /* IEEE float32 */
+  VSA_BF16 = 1,      /* bfloat16 */
+  VSA_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn": bias 7, max 448, no inf) codes + fp32 tile scales */
+} vsa_dtype;
+
+/* ----- token layouts ------------------------------------------------------ */
+typedef enum vsa_layout_kind {
+  /* 3D tiles of tile_t x tile_h x tile_w tokens. Each axis is padded at its
+   * high end to a multiple of the tile extent; tiles are numbered row-major
+   * over tile coordinates, tokens row-major (t, h, w) inside a tile. */
+  VSA_TILE3D = 0,
+  /* Skiparse-2D residue groups: token (t, h, w) belongs to group
+   * g = (h mod stride_h) * stride_w + (w mod stride_w). Groups are stored one
+   * after another, each row-major over (t, h / stride_h, w / stride_w), and
+   * cut into chunks of tile_t * tile_h * tile_w tokens; a group's last chunk
+   * is padded. Requires H % stride_h == 0 and W % stride_w == 0. */
+  VSA_SKIPARSE2D = 1
+} vsa_layout_kind;
+
+typedef struct vsa_layout {
+  int32_t batch;      /* B >= 1 */
+  int32_t heads;      /* attention heads >= 1 */
+  int32_t head_dim;   /* d */
+  int32_t T, H, W;    /* latent grid, each >= 1 */
+  int32_t kind;       /* vsa_layout_kind */
+  int32_t tile_t, tile_h, tile_w;  /* tile extents (>= 1); tile tokens = product */
+  int32_t stride_h, stride_w;      /* Skiparse strides (>= 1); ignored for VSA_TILE3D */
+} vsa_layout;
+
+typedef struct vsa_layout_info {
+  int64_t n_tokens;        /* T * H * W */
+  int64_t n_padded;        /* n_tiles * tile_tokens: rows of a tiled tensor per (b, head) */
+  int32_t n_tiles;         /* tiles per (b, head) */
+  int32_t tile_tokens;     /* tile_t * tile_h * tile_w */
+  int32_t n_groups;        /* Skiparse residue groups (1 for VSA_TILE3D) */
+  int32_t tiles_per_group; /* tiles of one group (n_tiles for VSA_TILE3D) */
+  int32_t group_len;       /* real tokens of one group (n_tokens for VSA_TILE3D) */
+  int32_t tiles_t, tiles_h, tiles_w; /* 3D tile grid (VSA_TILE3D; zeros otherwise) */
+} vsa_layout_info;
+
+/* Derives the padded sizes of a layout (host only, no GPU work).
+ * Returns VSA_ERR_INVALID for non-positive sizes or a Skiparse grid that the
+ * strides do not divide. */
+vsa_status vsa_layout_query(const vsa_layout* layout, vsa_layout_info* info);
+
+/* ----- S1 / S7: tile permutation -------------------------------------------
+ * FPSAttention, Approach (shared 3D tile granularity); FVAttn summary
+ * (video-aware block organisation); OSP-Next card, Model Summary (Skiparse
+ * groups along H and W).
+ *   inverse == 0: src natural [B, T*H*W, heads, d] -> dst tiled [B, heads, n_padded, d];
+ *                 pad rows of dst are written as zeros.
+ *   inverse != 0: src tiled [B, heads, n_padded, d] -> dst natural [B, T*H*W, heads, d];
+ *                 pad rows of src are ignored.
+ * dtype: VSA_F32 or VSA_BF16 (d * element size must be a multiple of 16 bytes).
+ * The result is a pure data movement: bit-exact. src and dst must not overlap. */
+vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void* src, void* dst,
+                            int32_t inverse, void* stream);
+
+/* ----- S2: fixed block masks -------------------------------------------------
+ * FPSAttention, Approach and window ablation (sliding tile window);
+ * OSP-Next card, Model Summary (Skiparse-2D; full-attention layers).
+ * Writes one head-invariant list per query tile:
+ *   kv_idx int32 [n_tiles, max_kv]: ascending key-tile indices (slots past the
+ *                                   count are left untouched),
+ *   kv_cnt int32 [n_tiles].
+ * VSA_TILE3D: key tile kept iff |delta| <= (rt, rh, rw) per axis in tile
+ *   coordinates, clipped at the grid edge.
+ * VSA_SKIPARSE2D: every tile of the query tile's residue group (radii unused).
+ * Any negative radius: dense, every tile listed.
+ * VSA_ERR_INVALID if max_kv is smaller than the longest list. */
+vsa_status vsa_build_mask_window(const vsa_layout* layout, int32_t rt, int32_t rh, int32_t rw,
+                                 int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, void* stream);
+
+/* ----- S3 / S4: adaptive routing ---------------------------------------------
+ * VSA page, Research Type row (coarse selection of key blocks per query
+ * block); FVAttn summary (Top-p routing with a Top-k safety floor, per head).
+ *   q_tiled, k_tiled: bf16 [B, heads, n_padded, d] (output of vsa_tile_permute).
+ * Steps, per (b, head):
+ *   pooled tile means over real (non-pad) tokens, in fp32;
+ *   s_ij = coarse_scale * <qbar_i, kbar_j>;
+ *   top_p <= 0: keep the top_k highest-scoring key tiles (ties: lower index);
+ *   top_p  > 0: p_ij = softmax_j(s_ij); keep the shortest prefix of the
+ *               descending order whose mass reaches top_p, then at least
+ *               k_floor tiles (capped at n_tiles); top_k is unused.
+ * Outputs: kv_idx int32 [B, heads, n_tiles, max_kv] ascending, kv_cnt int32
+ *   [B, heads, n_tiles]; scores (optional, may be NULL) float [B, heads,
+ *   n_tiles, n_tiles] holding s_ij.
+ * workspace: device memory of at least vsa_build_mask_topk_workspace() bytes.
+ * Limits: n_tiles <= 4096, head_dim <= 256 and a multiple of 8.
+ * VSA_ERR_INVALID if max_kv < the largest possible count (top_k, or n_tiles
+ * for top-p). */
+vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, const void* k_tiled,
+                               float coarse_scale, int32_t top_k, float top_p, int32_t k_floor,
+                               int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes vsa_build_mask_topk needs for this layout (0 on a bad layout). */
+size_t vsa_build_mask_topk_workspace(const vsa_layout* layout);
+
+/* ----- S5: per-tile fp8 quantiser ---------------------------------------------
+ * FPSAttention, Approach (FP8 on the same 3D tiles as the sparsity).
+ *   x_tiled bf16 [B, heads, n_padded, d] -> codes uint8 [B, heads, n_padded, d]
+ *   (OCP E4M3) and scales float [B, heads, n_tiles].
+ * Per (b, head, tile): a = absmax over real tokens and all d channels;
+ *   scale = fl32(a / 448); code = RNE_e4m3(fl32(x * fl32(448 / a))), saturating;
+ *   a == 0 gives scale 0 and zero codes; pad rows get code 0.
+ * Bit-exact: the operation sequence is fixed in fp32. */
+vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                               float* scales, void* stream);
+
+/* ----- S6: block-sparse attention forward --------------------------------------
+ * The flash-style, FlashAttention-compatible sparse attention every page
+ * builds on (OSP-Next wiki TL;DR; FPSAttention, Approach; VSA, Research
+ * Type row; FVAttn summary). For every real query token i of query tile Q:
+ *   O_i = sum_{j in A(i)} exp(sigma q_i.k_j) v_j / sum_{j in A(i)} exp(sigma q_i.k_j)
+ * with A(i) the real key tokens of the key tiles listed for Q.
+ *   q, k, v: tiled [B, heads, n_padded, d]
+ *     dtype VSA_F32: float inputs (rounded to bf16 for the products), float out;
+ *     dtype VSA_BF16: bf16 in, bf16 out;
+ *     dtype VSA_FP8_E4M3: uint8 codes in with q_scale / k_scale / v_scale
+ *       float [B, heads, n_tiles] from vsa_quant_fp8_tiles; bf16 out.
+ *   kv_idx / kv_cnt: lists as written by vsa_build_mask_window (list_mode 0:
+ *     one table [n_tiles, max_kv] shared by every batch and head) or by
+ *     vsa_build_mask_topk (list_mode 1: [B, heads, n_tiles, max_kv]).
+ *     Both NULL: dense attention (every tile). Indices must lie in
+ *     [0, n_tiles) and counts in [0, max_kv]; the kernel does not re-check them.
+ *   out: [B, heads, n_padded, d]; pad query rows and rows with an empty list
+ *     are written as 0.
+ *   lse (optional, may be NULL): float [B, heads, n_padded], natural-log
+ *     sum_{j in A(i)} exp(sigma q_i.k_j); -inf for pad rows and empty lists.
+ * Supported: tile_tokens in {32, 64}; head_dim in {64, 128}; VSA_FP8_E4M3
+ * needs tile_tokens 64 and head_dim 128. */
+vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
+                                     const void* k, const void* v, const float* q_scale,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_kv,
+                                     int32_t list_mode, float softmax_scale, void* out, float* lse,
+                                     void* stream);
+
+/* ----- diagnostics --------------------------------------------------------- */
+const char* vsa_status_string(int32_t status);
+/* Message for the last failing call on this thread ("" if none). */
+const char* vsa_last_error(void);
+/* Library version, "major.minor.patch". */
+const char* vsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H_ */

@@ -90,6 +90,7 @@ def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
 def quantize_tiles(x_tiled: np.ndarray, lay: Layout):
     """Per-tile e4m3 quantisation of a tiled tensor [B, heads, N_pad, d].
 
+    Loops over tiles; each step is vectorised over (batch, head) only.
     Returns (codes uint8 [B, heads, N_pad, d], scales float32 [B, heads, n_tiles]).
     """
     order = token_order(lay).reshape(lay.n_tiles, lay.tile_tokens)
@@ -101,18 +102,17 @@ def quantize_tiles(x_tiled: np.ndarray, lay: Layout):
     f448 = np.float32(E4M3_MAX)
     for t in range(lay.n_tiles):
         real = order[t] >= 0
-        xt = x[:, :, t][:, :, real]                        # [B, heads, n_real, d]
-        amax = np.abs(xt).max(axis=(2, 3)).astype(np.float32)   # [B, heads]
-        for b in range(B):
-            for h in range(lay.heads):
-                a = amax[b, h]
-                if a == 0:
-                    continue
-                inv = np.float32(f448 / a)
-                y = (x[b, h, t] * inv).astype(np.float32)
-                y[~real] = 0.0
-                codes[b, h, t] = e4m3_encode_array(y)
-                scales[b, h, t] = np.float32(a / f448)
+        blk = x[:, :, t]                                       # [B, heads, C, d]
+        amax = np.abs(blk[:, :, real, :]).max(axis=(2, 3)).astype(np.float32)
+        nz = amax > 0
+        safe = np.where(nz, amax, np.float32(1.0)).astype(np.float32)
+        inv = np.where(nz, f448 / safe, np.float32(0.0)).astype(np.float32)   # fp32 divide
+        y = (blk * inv[:, :, None, None]).astype(np.float32)                  # fp32 multiply
+        y[:, :, ~real, :] = 0.0
+        c = e4m3_encode_array(y)
+        c[~nz] = 0
+        codes[:, :, t] = c
+        scales[:, :, t] = np.where(nz, safe / f448, np.float32(0.0)).astype(np.float32)
     return codes.reshape(B, lay.heads, lay.n_padded, d), scales
 
 

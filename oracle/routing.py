@@ -51,7 +51,7 @@ def coarse_scores(qbar: np.ndarray, kbar: np.ndarray, coarse_scale: float) -> np
     -inf where key tile j has no real token; a whole row is NaN where query
     tile i has no real token.
     """
-    s = coarse_scale * np.einsum("bhid,bhjd->bhij", qbar, kbar)
+    s = coarse_scale * np.matmul(qbar, np.swapaxes(kbar, -1, -2))
     bad_key = np.isnan(kbar).any(axis=-1)                 # [B, heads, n_tiles]
     bad_query = np.isnan(qbar).any(axis=-1)
     s = np.where(bad_key[:, :, None, :], -np.inf, s)
@@ -122,3 +122,44 @@ def route(q_tiled: np.ndarray, k_tiled: np.ndarray, lay: Layout, coarse_scale: f
     s = coarse_scores(qbar, kbar, coarse_scale)
     # a query tile without real tokens has NaN pooled values -> NaN scores row
     return select_lists(s, top_k=top_k, top_p=top_p, k_floor=k_floor), s
+
+
+def select_lists_vectorized(scores: np.ndarray, top_k: int = 0, top_p: float = 0.0,
+                            k_floor: int = 0):
+    """Same rule as ``select_lists`` for many rows at once (library sort + cumsum).
+
+    Used for full-size workloads where the per-row Python version is too slow;
+    ``tests/test_oracle_routing.py`` checks that both give identical lists.
+    Returns (idx int32 [..., n, n] ascending and padded with -1, cnt int32 [..., n]).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    lead = s.shape[:-1]
+    n = s.shape[-1]
+    rows = s.reshape(-1, n)
+    R = rows.shape[0]
+    idx = np.full((R, n), -1, dtype=np.int32)
+    cnt = np.zeros(R, dtype=np.int32)
+    col = np.broadcast_to(np.arange(n), rows.shape)
+    finite = np.isfinite(rows)
+    n_valid = finite.sum(axis=1)
+    q_bad = np.isnan(rows).all(axis=1)
+    # descending score, ascending index; non-finite scores go last
+    key = np.where(finite, -rows, np.inf)
+    order = np.lexsort((col, key), axis=-1)
+    for r in range(R):
+        if q_bad[r] or n_valid[r] == 0:
+            continue
+        o = order[r, :n_valid[r]]
+        if top_p > 0.0:
+            v = rows[r, o]
+            w = np.exp(v - v[0])
+            cum = np.cumsum(w / w.sum())
+            hit = np.nonzero(cum >= top_p)[0]
+            c = int(hit[0]) + 1 if hit.size else int(n_valid[r])
+            c = min(max(c, k_floor), int(n_valid[r]))
+        else:
+            c = min(top_k, int(n_valid[r]))
+        keep = np.sort(o[:c])
+        idx[r, :c] = keep
+        cnt[r] = c
+    return idx.reshape(lead + (n,)), cnt.reshape(lead)

@@ -14,6 +14,17 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+@pytest.fixture(autouse=True)
+def _gpu_guard(request):
+    """Skip GPU tests without a GPU; name each GPU test on stderr before it runs."""
+    if request.node.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.skip("no GPU visible")
+        print(f"[gpu-test] {request.node.nodeid}", file=sys.__stderr__, flush=True)
+    yield
+
+
 def read_golden(name):
     """Non-comment, non-empty lines of a golden fixture."""
     with open(os.path.join(GOLDEN, name)) as f:

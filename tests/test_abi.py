@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/vsa.h, derives layouts, and rejects bad arguments before
+any launch (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_token_amd as vsa
+from block_sparse_attention_token_amd import _lib as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared()
+    assert len(names) >= 10
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_version_and_status_strings():
+    L = B.lib()
+    assert L.vsa_version().decode().count(".") == 2
+    assert L.vsa_status_string(0) == b"VSA_OK"
+    assert L.vsa_status_string(3) == b"VSA_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("T,H,W,tile,kind,npad,ntiles", [
+    (4, 8, 8, (2, 4, 4), "tile3d", 256, 8),
+    (21, 30, 52, (4, 4, 4), "tile3d", 39936, 624),
+    (21, 48, 80, (4, 4, 4), "skiparse2d", 80640, 1260),
+    (21, 45, 80, (4, 4, 4), "tile3d", 92160, 1440),
+    (3, 4, 6, (1, 4, 4), "skiparse2d", 128, 8),
+])
+def test_layout_query(T, H, W, tile, kind, npad, ntiles):
+    info = vsa.layout_info(vsa.Layout(T=T, H=H, W=W, heads=2, head_dim=64, tile=tile, kind=kind))
+    assert (info.n_padded, info.n_tiles, info.n_tokens) == (npad, ntiles, T * H * W)
+
+
+def _status(fn, *args):
+    return getattr(B.lib(), fn)(*args)
+
+
+def test_invalid_layouts():
+    for lay in (vsa.Layout(T=0, H=8, W=8, heads=1, head_dim=64),
+                vsa.Layout(T=4, H=8, W=8, heads=0, head_dim=64),
+                vsa.Layout(T=4, H=7, W=8, heads=1, head_dim=64, kind="skiparse2d")):
+        info = B.VsaLayoutInfo()
+        c = lay.c()
+        assert _status("vsa_layout_query", ctypes.byref(c), ctypes.byref(info)) == B.VSA_ERR_INVALID
+        assert B.lib().vsa_last_error() != b""
+    assert _status("vsa_layout_query", None, ctypes.byref(B.VsaLayoutInfo())) == B.VSA_ERR_INVALID
+
+
+def test_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    # permute: null pointers, unsupported dtype, misaligned pointer
+    assert _status("vsa_tile_permute", L, B.VSA_BF16, None, FAKE, 0, None) == B.VSA_ERR_INVALID
+    assert _status("vsa_tile_permute", L, B.VSA_FP8_E4M3, FAKE, FAKE, 0, None) == B.VSA_ERR_UNSUPPORTED
+    assert _status("vsa_tile_permute", L, B.VSA_BF16, ctypes.c_void_p(0x100008), FAKE, 0, None) \
+        == B.VSA_ERR_INVALID
+    # window mask: max_kv below the longest list (75)
+    assert _status("vsa_build_mask_window", L, 1, 2, 2, 74, FAKE, FAKE, None) == B.VSA_ERR_INVALID
+    # routing: missing workspace, bad top_k, too-small max_kv
+    assert _status("vsa_build_mask_topk", L, FAKE, FAKE, ctypes.c_float(0.1), 32,
+                   ctypes.c_float(0.0), 0, 32, FAKE, FAKE, None, None, 0, None) == B.VSA_ERR_WORKSPACE
+    assert _status("vsa_build_mask_topk", L, FAKE, FAKE, ctypes.c_float(0.1), 0,
+                   ctypes.c_float(0.0), 0, 32, FAKE, FAKE, None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
+    assert _status("vsa_build_mask_topk", L, FAKE, FAKE, ctypes.c_float(0.1), 0,
+                   ctypes.c_float(0.9), 16, 600, FAKE, FAKE, None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
+    # attention: one list pointer without the other, bad list_mode, fp8 without scales,
+    # unsupported head_dim / tile size
+    args = [FAKE, FAKE, FAKE, None, None, None]
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, None, 8, 0,
+                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 2,
+                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_FP8_E4M3, *args, FAKE, FAKE, 8, 0,
+                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 0,
+                   ctypes.c_float(float("nan")), FAKE, None, None) == B.VSA_ERR_INVALID
+    lay96 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=96).c()
+    assert _status("vsa_block_sparse_attn_fwd", ctypes.byref(lay96), B.VSA_BF16, *args, None, None,
+                   0, 0, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
+    lay27 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128, tile=(3, 3, 3)).c()
+    assert _status("vsa_block_sparse_attn_fwd", ctypes.byref(lay27), B.VSA_BF16, *args, None, None,
+                   0, 0, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
+    # quantiser: null scales
+    assert _status("vsa_quant_fp8_tiles", L, FAKE, FAKE, None, None) == B.VSA_ERR_INVALID
+
+
+def test_workspace_query():
+    lay = vsa.Layout(T=21, H=45, W=80, heads=40, head_dim=128).c()
+    n = B.lib().vsa_build_mask_topk_workspace(ctypes.byref(lay))
+    assert n >= 40 * 1440 * 1440 * 4
+    bad = vsa.Layout(T=0, H=45, W=80, heads=40, head_dim=128).c()
+    assert B.lib().vsa_build_mask_topk_workspace(ctypes.byref(bad)) == 0

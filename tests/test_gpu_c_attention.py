@@ -1,0 +1,240 @@
+"""GPU parity: block-sparse attention forward against the fp64 oracle.
+
+Both sides get identical key-tile lists: the oracle's lists are uploaded to
+the GPU. Gates: bf16 max-abs 2e-2 and relative L2 1e-2; fp8 relative L2
+5e-2 against the oracle on the unquantised bf16 inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_token_amd as vsa
+from oracle import attention as OA
+from oracle import fp8 as OF
+from oracle import layout as OL
+from oracle import masks as OM
+from oracle import routing as OR
+from synth import CONFIGS
+from tests.gpu_util import (announce, errors, inputs, layouts, lists_to_device, table_from_lists,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2, REL_L2_FP8 = 2e-2, 1e-2, 5e-2
+
+
+def _tiled(cfg, olay, blay, x):
+    return vsa.tile_permute(blay, to_device(x, cfg.dtype)), OL.permute(x, olay).astype(np.float64)
+
+
+def _items(olay, n, seed, must=()):
+    rng = np.random.default_rng(seed)
+    picks = {(0, int(h), int(t)) for h, t in zip(rng.integers(0, olay.heads, n),
+                                                  rng.integers(0, olay.n_tiles, n))}
+    picks |= set(must)
+    return sorted(picks)
+
+
+def _compare(out_gpu, O_ref, lse_gpu, L_ref, olay, items, rel_gate=REL_L2, abs_gate=MAX_ABS):
+    C = olay.tile_tokens
+    g, r, gl, rl = [], [], [], []
+    for b, h, t in items:
+        g.append(out_gpu[b, h, t * C:(t + 1) * C])
+        r.append(O_ref[b, h, t * C:(t + 1) * C])
+        if lse_gpu is not None:
+            gl.append(lse_gpu[b, h, t * C:(t + 1) * C])
+            rl.append(L_ref[b, h, t * C:(t + 1) * C])
+    g, r = np.concatenate(g), np.concatenate(r)
+    mae, rl2 = errors(g, r)
+    print(f"max_abs={mae:.3e} rel_l2={rl2:.3e}")
+    assert mae <= abs_gate and rl2 <= rel_gate, (mae, rl2)
+    if gl:
+        gl, rl = np.concatenate(gl), np.concatenate(rl)
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(gl), fin)
+        assert np.abs(gl[fin] - rl[fin]).max() <= 2e-3
+
+
+def _run_shared(name, radius, n_items, dense=False, seed=0, full=False):
+    cfg = CONFIGS[name]
+    olay, blay = layouts(cfg)
+    q, k, v = inputs(name)
+    sigma = 1.0 / math.sqrt(cfg.head_dim)
+    lists = OM.dense_lists(olay) if dense else OM.window_lists(olay, *radius)
+    idx, cnt = table_from_lists(lists)
+    announce(f"attn {name} radius={radius} dense={dense}")
+    qd, qo = _tiled(cfg, olay, blay, q)
+    kd, ko = _tiled(cfg, olay, blay, k)
+    vd, vo = _tiled(cfg, olay, blay, v)
+    if dense:
+        out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, want_lse=True)
+    else:
+        di, dc = lists_to_device(idx, cnt)
+        out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+    torch.cuda.synchronize()
+    items = None if full else _items(olay, n_items, seed,
+                                     must=[(0, 0, 0), (0, olay.heads - 1, olay.n_tiles - 1)])
+    O, L = OA.attention(qo, ko, vo, olay, OA.shared_lists(lists), sigma, items=items)
+    if items is None:
+        items = [(0, h, t) for h in range(olay.heads) for t in range(olay.n_tiles)]
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
+    return out
+
+
+def test_tiny_f32_full():
+    _run_shared("tiny_window_f32", (1, 1, 1), 0, full=True)
+
+
+def test_window_480p_sampled():
+    _run_shared("window_480p", (1, 2, 2), 150, seed=3)
+
+
+def test_skiparse_768p_sparse_sampled():
+    _run_shared("skiparse_768p", (0, 0, 0), 24, seed=4)
+
+
+def test_skiparse_768p_dense_layer_sampled():
+    _run_shared("skiparse_768p", (0, 0, 0), 10, dense=True, seed=5)
+
+
+def _routed(name, top_k=0, top_p=0.0, k_floor=0):
+    cfg = CONFIGS[name]
+    olay, _ = layouts(cfg)
+    q, k, _ = inputs(name)
+    qb = OR.pool_tiles(OL.permute(q, olay), olay)
+    kb = OR.pool_tiles(OL.permute(k, olay), olay)
+    s = OR.coarse_scores(qb, kb, 1.0 / math.sqrt(cfg.head_dim))
+    return OR.select_lists_vectorized(s, top_k=top_k, top_p=top_p, k_floor=k_floor)
+
+
+def test_topk32_full():
+    cfg = CONFIGS["topk32_16x32x32"]
+    olay, blay = layouts(cfg)
+    q, k, v = inputs(cfg.name)
+    idx, cnt = _routed(cfg.name, top_k=cfg.top_k)
+    idx = np.ascontiguousarray(idx[..., :cfg.top_k])
+    announce(f"attn {cfg.name} routed top-k")
+    qd, qo = _tiled(cfg, olay, blay, q)
+    kd, ko = _tiled(cfg, olay, blay, k)
+    vd, vo = _tiled(cfg, olay, blay, v)
+    di, dc = lists_to_device(idx, cnt)
+    out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+    torch.cuda.synchronize()
+    lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    O, L = OA.attention(qo, ko, vo, olay, lists_fn, 1.0 / math.sqrt(cfg.head_dim))
+    items = [(0, h, t) for h in range(olay.heads) for t in range(olay.n_tiles)]
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
+    # determinism: a second launch is bit-identical
+    out2, _ = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.fixture(scope="module")
+def topp_case():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    cfg = CONFIGS["fp8_topp_720p"]
+    olay, blay = layouts(cfg)
+    q, k, v = inputs(cfg.name)
+    idx, cnt = _routed(cfg.name, top_p=cfg.top_p, k_floor=cfg.k_floor)
+    qd, qo = _tiled(cfg, olay, blay, q)
+    kd, ko = _tiled(cfg, olay, blay, k)
+    vd, vo = _tiled(cfg, olay, blay, v)
+    return cfg, olay, blay, idx, cnt, (qd, kd, vd), (qo, ko, vo)
+
+
+def test_topp_720p_fp8_sampled(topp_case):
+    cfg, olay, blay, idx, cnt, (qd, kd, vd), (qo, ko, vo) = topp_case
+    announce(f"attn {cfg.name} fp8 routed top-p")
+    qc, qs = vsa.quant_fp8_tiles(blay, qd)
+    kc, ks = vsa.quant_fp8_tiles(blay, kd)
+    vc, vs = vsa.quant_fp8_tiles(blay, vd)
+    di, dc = lists_to_device(idx, cnt)
+    out, lse = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs),
+                                         want_lse=True)
+    torch.cuda.synchronize()
+    items = _items(olay, 24, 6, must=[(0, 0, olay.n_tiles - 1)])
+    lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    sigma = 1.0 / math.sqrt(cfg.head_dim)
+    O, _ = OA.attention(qo, ko, vo, olay, lists_fn, sigma, items=items)
+    og = out.float().cpu().numpy()
+    _compare(og, O, None, None, olay, items, rel_gate=REL_L2_FP8, abs_gate=np.inf)
+    # diagnostic only: against the oracle on the dequantised inputs
+    deq = [OF.dequantize_tiles(c.cpu().numpy(), s.cpu().numpy(), olay) for c, s in
+           ((qc, qs), (kc, ks), (vc, vs))]
+    Od, _ = OA.attention(*deq, olay, lists_fn, sigma, items=items[:8])
+    C = olay.tile_tokens
+    g = np.concatenate([og[b, h, t * C:(t + 1) * C] for b, h, t in items[:8]])
+    r = np.concatenate([Od[b, h, t * C:(t + 1) * C] for b, h, t in items[:8]])
+    print("fp8 vs dequantised oracle: max_abs=%.3e rel_l2=%.3e" % errors(g, r))
+
+
+def test_topp_720p_bf16_sampled(topp_case):
+    cfg, olay, blay, idx, cnt, (qd, kd, vd), (qo, ko, vo) = topp_case
+    announce(f"attn {cfg.name} bf16 routed top-p")
+    di, dc = lists_to_device(idx, cnt)
+    out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+    torch.cuda.synchronize()
+    items = _items(olay, 16, 7, must=[(0, olay.heads - 1, olay.n_tiles - 1)])
+    lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    O, L = OA.attention(qo, ko, vo, olay, lists_fn, 1.0 / math.sqrt(cfg.head_dim), items=items)
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
+
+
+def test_empty_lists_pad_rows_and_guard_band():
+    cfg = CONFIGS["window_480p"]
+    olay, blay = layouts(cfg, heads=2)
+    rng = np.random.default_rng(9)
+    from synth import round_to_bf16
+    q, k, v = (round_to_bf16(rng.standard_normal((1, olay.n_tokens, 2, 128)).astype(np.float32))
+               for _ in range(3))
+    lists = OM.window_lists(olay, 0, 1, 1)
+    lists = [[] if t % 7 == 3 else row for t, row in enumerate(lists)]   # some empty lists
+    idx, cnt = table_from_lists(lists, width=9)
+    announce("attn empty lists + guard band")
+    qd, qo = _tiled(cfg, olay, blay, q)
+    kd, ko = _tiled(cfg, olay, blay, k)
+    vd, vo = _tiled(cfg, olay, blay, v)
+    di, dc = lists_to_device(idx, cnt)
+    n = olay.n_padded * 2 * 128
+    guard = 4096
+    buf = torch.full((n + guard,), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[:n].view(1, 2, olay.n_padded, 128)
+    vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[n:] == 3.0).all())
+    O, _ = OA.attention(qo, ko, vo, olay, OA.shared_lists(lists), 1.0 / math.sqrt(128))
+    og = out.float().cpu().numpy()
+    C = olay.tile_tokens
+    for t in range(olay.n_tiles):
+        if t % 7 == 3:
+            assert np.all(og[0, :, t * C:(t + 1) * C] == 0)
+    order = OL.token_order(olay)
+    assert np.all(og[0, :, order < 0] == 0)
+    items = [(0, h, t) for h in range(2) for t in range(olay.n_tiles)]
+    _compare(og, O, None, None, olay, items)
+
+
+def test_list_modes_agree():
+    """A shared table and the same table repeated per head give identical output."""
+    cfg = CONFIGS["window_480p"]
+    olay, blay = layouts(cfg, heads=3)
+    rng = np.random.default_rng(10)
+    from synth import round_to_bf16
+    x = [round_to_bf16(rng.standard_normal((1, olay.n_tokens, 3, 128)).astype(np.float32))
+         for _ in range(3)]
+    lists = OM.window_lists(olay, 1, 1, 1)
+    idx, cnt = table_from_lists(lists)
+    announce("attn list modes")
+    t = [vsa.tile_permute(blay, to_device(a, "bf16")) for a in x]
+    di, dc = lists_to_device(idx, cnt)
+    o1, _ = vsa.block_sparse_attn_fwd(blay, *t, di, dc)
+    di4 = di[None, None].expand(1, 3, *di.shape).contiguous()
+    dc4 = dc[None, None].expand(1, 3, *dc.shape).contiguous()
+    o2, _ = vsa.block_sparse_attn_fwd(blay, *t, di4, dc4)
+    torch.cuda.synchronize()
+    mae, rl2 = errors(o1.float().cpu().numpy(), o2.float().cpu().numpy().astype(np.float64))
+    assert mae <= 1e-2 and rl2 <= 1e-3

@@ -96,3 +96,21 @@ def test_pad_query_tile_gets_empty_list():
     s = R.coarse_scores(qb, kb, 1.0)
     lists = R.select_lists(s, top_k=1)
     assert lists[0][0][1] == [] and lists[0][0][0] == [0]
+
+
+def test_vectorized_selection_matches_per_row():
+    rng = np.random.default_rng(8)
+    s = np.round(rng.standard_normal((2, 3, 40, 40)) * 2, 1)      # ties on purpose
+    s[0, 1, :, 7] = -np.inf                                          # a key tile without tokens
+    s[1, 2, 5, :] = np.nan                                           # a query tile without tokens
+    s[1, 2, 5, 3] = -np.inf
+    for kw in ({"top_k": 5}, {"top_k": 60}, {"top_p": 0.9, "k_floor": 16},
+               {"top_p": 0.5, "k_floor": 0}, {"top_p": 0.999, "k_floor": 3}):
+        slow = R.select_lists(s, **kw)
+        idx, cnt = R.select_lists_vectorized(s, **kw)
+        for b in range(2):
+            for h in range(3):
+                for i in range(40):
+                    c = int(cnt[b, h, i])
+                    assert idx[b, h, i, :c].tolist() == slow[b][h][i]
+                    assert np.all(idx[b, h, i, c:] == -1)
