@@ -9,7 +9,7 @@ import block_sparse_attention_token_amd as vsa
 from oracle import layout as OL
 from oracle import masks as OM
 from oracle.layout import Layout as OLayout
-from synth import CONFIGS
+from synth import CONFIGS, round_to_bf16
 from tests.conftest import read_golden
 from tests.gpu_util import (announce, host_bits, inputs, layouts, ref_bits, table_from_lists,
                             to_device)
@@ -52,14 +52,13 @@ def test_permute_small_grids_bitexact(grid, tile, kind, stride):
     x = rng.standard_normal((2, T * H * W, 3, 8)).astype(np.float32)
     announce(f"permute small {grid} {tile} {kind}")
     for dt in ("f32", "bf16"):
-        xd = to_device(x, dt)
+        xr = round_to_bf16(x) if dt == "bf16" else x
+        xd = to_device(xr, dt)
         # canary-filled output proves the pad rows are written as zeros
         info = vsa.layout_info(blay)
         out = torch.full((2, 3, info.n_padded, 8), 7.0, dtype=xd.dtype, device="cuda")
         vsa.tile_permute(blay, xd, out=out)
         torch.cuda.synchronize()
-        from synth import round_to_bf16
-        xr = round_to_bf16(x) if dt == "bf16" else x
         assert np.array_equal(host_bits(out), ref_bits(OL.permute(xr, olay), dt))
         back = vsa.tile_permute(blay, out, inverse=True)
         torch.cuda.synchronize()

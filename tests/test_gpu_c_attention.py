@@ -1,8 +1,14 @@
 """GPU parity: block-sparse attention forward against the fp64 oracle.
 
 Both sides get identical key-tile lists: the oracle's lists are uploaded to
-the GPU. Gates: bf16 max-abs 2e-2 and relative L2 1e-2; fp8 relative L2
-5e-2 against the oracle on the unquantised bf16 inputs.
+the GPU. Gates: bf16 max-abs 2e-2 and relative L2 1e-2. fp8: relative L2
+5e-2 against the oracle of the fp8 method (oracle e4m3 quantiser, then fp64
+attention on the dequantised tensors); against the oracle on the unquantised
+bf16 inputs the kernel may add at most 10% (+5e-3) to the error the
+quantisation itself causes there.
+LSE: 2e-3 absolute for bf16 inputs; for fp32 inputs, which the kernel rounds
+to bf16, up to 2.5e-2 (bound: sigma * 2 * 2^-9 * sum_e |q_e k_e|, about 0.024
+at d = 64 with unit-variance inputs).
 """
 import math
 
@@ -37,7 +43,8 @@ def _items(olay, n, seed, must=()):
     return sorted(picks)
 
 
-def _compare(out_gpu, O_ref, lse_gpu, L_ref, olay, items, rel_gate=REL_L2, abs_gate=MAX_ABS):
+def _compare(out_gpu, O_ref, lse_gpu, L_ref, olay, items, rel_gate=REL_L2, abs_gate=MAX_ABS,
+             lse_gate=2e-3):
     C = olay.tile_tokens
     g, r, gl, rl = [], [], [], []
     for b, h, t in items:
@@ -54,7 +61,8 @@ def _compare(out_gpu, O_ref, lse_gpu, L_ref, olay, items, rel_gate=REL_L2, abs_g
         gl, rl = np.concatenate(gl), np.concatenate(rl)
         fin = np.isfinite(rl)
         assert np.array_equal(np.isfinite(gl), fin)
-        assert np.abs(gl[fin] - rl[fin]).max() <= 2e-3
+        assert np.abs(gl[fin] - rl[fin]).max() <= lse_gate
+    return mae, rl2
 
 
 def _run_shared(name, radius, n_items, dense=False, seed=0, full=False):
@@ -79,7 +87,8 @@ def _run_shared(name, radius, n_items, dense=False, seed=0, full=False):
     O, L = OA.attention(qo, ko, vo, olay, OA.shared_lists(lists), sigma, items=items)
     if items is None:
         items = [(0, h, t) for h in range(olay.heads) for t in range(olay.n_tiles)]
-    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items,
+             lse_gate=2.5e-2 if cfg.dtype == "f32" else 2e-3)
     return out
 
 
@@ -153,23 +162,32 @@ def test_topp_720p_fp8_sampled(topp_case):
     kc, ks = vsa.quant_fp8_tiles(blay, kd)
     vc, vs = vsa.quant_fp8_tiles(blay, vd)
     di, dc = lists_to_device(idx, cnt)
-    out, lse = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs),
-                                         want_lse=True)
+    out, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs))
     torch.cuda.synchronize()
-    items = _items(olay, 24, 6, must=[(0, 0, olay.n_tiles - 1)])
-    lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
-    sigma = 1.0 / math.sqrt(cfg.head_dim)
-    O, _ = OA.attention(qo, ko, vo, olay, lists_fn, sigma, items=items)
     og = out.float().cpu().numpy()
-    _compare(og, O, None, None, olay, items, rel_gate=REL_L2_FP8, abs_gate=np.inf)
-    # diagnostic only: against the oracle on the dequantised inputs
-    deq = [OF.dequantize_tiles(c.cpu().numpy(), s.cpu().numpy(), olay) for c, s in
-           ((qc, qs), (kc, ks), (vc, vs))]
-    Od, _ = OA.attention(*deq, olay, lists_fn, sigma, items=items[:8])
+    # oracle side on 4 heads (quantisation is independent per head)
+    rng = np.random.default_rng(6)
+    heads = sorted(rng.choice(cfg.heads, 4, replace=False).tolist())
+    sub = OL.Layout(T=cfg.T, H=cfg.H, W=cfg.W, heads=4, head_dim=cfg.head_dim, tile=cfg.tile)
+    xs = [x[:, heads].astype(np.float32) for x in (qo, ko, vo)]
+    deq = [OF.dequantize_tiles(*OF.quantize_tiles(x, sub), sub) for x in xs]
+    items = [(0, j, int(t)) for j in range(4) for t in rng.integers(0, olay.n_tiles, 5)]
+    items.append((0, 3, olay.n_tiles - 1))
+    lists_fn = lambda b, j, t: idx[b, heads[j], t, :cnt[b, heads[j], t]].tolist()
+    sigma = 1.0 / math.sqrt(cfg.head_dim)
+    Od, _ = OA.attention(*deq, sub, lists_fn, sigma, items=items)
+    Ou, _ = OA.attention(*(x.astype(np.float64) for x in xs), sub, lists_fn, sigma, items=items)
     C = olay.tile_tokens
-    g = np.concatenate([og[b, h, t * C:(t + 1) * C] for b, h, t in items[:8]])
-    r = np.concatenate([Od[b, h, t * C:(t + 1) * C] for b, h, t in items[:8]])
-    print("fp8 vs dequantised oracle: max_abs=%.3e rel_l2=%.3e" % errors(g, r))
+    g = np.concatenate([og[0, heads[j], t * C:(t + 1) * C] for _, j, t in items])
+    rd = np.concatenate([Od[0, j, t * C:(t + 1) * C] for _, j, t in items])
+    ru = np.concatenate([Ou[0, j, t * C:(t + 1) * C] for _, j, t in items])
+    mae_d, rl2_d = errors(g, rd)
+    mae_u, rl2_u = errors(g, ru)
+    _, rl2_q = errors(rd, ru)
+    print(f"fp8 vs oracle(dequantised): max_abs={mae_d:.3e} rel_l2={rl2_d:.3e}; "
+          f"vs oracle(bf16): rel_l2={rl2_u:.3e}; quantisation alone: rel_l2={rl2_q:.3e}")
+    assert rl2_d <= REL_L2_FP8
+    assert rl2_u <= 1.1 * rl2_q + 5e-3
 
 
 def test_topp_720p_bf16_sampled(topp_case):
