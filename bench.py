@@ -1,0 +1,379 @@
+"""Benchmark: block-sparse video attention forward on one MI355X.
+
+Default workload: the Wan-14B 768p Skiparse-2D hybrid (21x48x80 latent grid,
+40 heads, d = 128, bf16): one step is one 4-layer cycle (three Skiparse-2D
+sparse layers and one dense layer). Every layer runs the whole hot path:
+tile permute of Q, K and V, attention over the cached fixed lists (built
+once per shape, as a Skiparse pattern is head- and data-invariant), and the
+inverse permute of O. The other four workloads are measured after it and
+reported under "per_workload" (one layer per step each).
+
+Printed: ONE JSON line. value = executed TFLOP/s of the attention over the
+whole timed step (permutes included in the time); roofline = the attention
+kernel's executed FLOP per launch / its average launch time (HIP events on
+the launch stream) against the 2.5 PFLOP/s dense bf16 peak; cpu_baseline =
+the fp64 oracle timed on this host on a seeded sample of (head, query tile)
+items of the sparse layer.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+                       [--only-headline] [--no-cpu-baseline] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse video-attn fwd: ms/layer, executed TFLOP/s and % of MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def exec_flops(pairs: int, d: int, tile: int) -> float:
+    """Executed FLOP of attention: 4 * d * tile^2 per (query tile, key tile) pair."""
+    return 4.0 * d * tile * tile * pairs
+
+
+class Timer:
+    """Accumulates HIP-event durations of launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = {}
+        self.total = {}
+        self.count = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn()
+        e1.record()
+        self.pending.setdefault(name, []).append((e0, e1))
+        return r
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, evs in self.pending.items():
+            for e0, e1 in evs:
+                self.total[name] = self.total.get(name, 0.0) + e0.elapsed_time(e1)
+                self.count[name] = self.count.get(name, 0) + 1
+        self.pending.clear()
+
+    def reset(self):
+        self.pending.clear()
+        self.total.clear()
+        self.count.clear()
+
+
+def to_dev(x, dtype, torch, np):
+    from synth import bf16_bits
+    if dtype == "bf16":
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def build_workload(name, torch, np, vsa):
+    """Inputs on the GPU plus a step function for one workload."""
+    from synth import CONFIGS, make_qkv
+    cfg = CONFIGS[name]
+    t0 = time.time()
+    q, k, v = make_qkv(cfg)
+    lay = vsa.Layout(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, head_dim=cfg.head_dim,
+                     kind=cfg.kind, tile=cfg.tile, stride=cfg.stride)
+    info = vsa.layout_info(lay)
+    nat = [to_dev(x, cfg.dtype, torch, np) for x in (q, k, v)]
+    del q, k, v
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s")
+    C, d, n = info.tile_tokens, cfg.head_dim, info.n_tiles
+    state = {"cfg": cfg, "lay": lay, "info": info}
+
+    if cfg.mask in ("window", "skiparse"):
+        radius = cfg.window if cfg.mask == "window" else (0, 0, 0)
+        kv_idx, kv_cnt = vsa.build_mask_window(lay, radius)      # cached: built once per shape
+        torch.cuda.synchronize()
+        pairs_sparse = int(kv_cnt.sum().item()) * cfg.heads
+
+    def layer(timer, dense=False):
+        tq, tk, tv = (timer.run("permute", lambda x=x: vsa.tile_permute(lay, x)) for x in nat)
+        if cfg.mask in ("window", "skiparse"):
+            if dense:
+                out, _ = timer.run("attn_dense", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv))
+            else:
+                out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv,
+                                                                              kv_idx, kv_cnt))
+        elif cfg.mask == "topk":
+            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(lay, tq, tk, top_k=cfg.top_k))
+            state["cnt"] = cnt
+            out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv, idx, cnt))
+        else:   # top-p routing on bf16, then fp8 attention
+            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(
+                lay, tq, tk, top_p=cfg.top_p, k_floor=cfg.k_floor))
+            state["cnt"] = cnt
+            (qc, qs), (kc, ks), (vc, vs) = (timer.run("quant", lambda x=x: vsa.quant_fp8_tiles(lay, x))
+                                           for x in (tq, tk, tv))
+            out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(
+                lay, qc, kc, vc, idx, cnt, scales=(qs, ks, vs)))
+        timer.run("unpermute", lambda: vsa.tile_permute(lay, out, inverse=True))
+
+    def step(timer):
+        if cfg.dense_every:
+            for i in range(cfg.dense_every):
+                layer(timer, dense=(i == cfg.dense_every - 1))
+        else:
+            layer(timer)
+
+    def flops():
+        """(executed attention FLOP per step, per attention launch kind)."""
+        if cfg.mask in ("window", "skiparse"):
+            sparse = exec_flops(pairs_sparse, d, C)
+            if cfg.dense_every:
+                dense = exec_flops(n * n * cfg.heads, d, C)
+                return sparse * (cfg.dense_every - 1) + dense, {"attn": sparse, "attn_dense": dense}
+            return sparse, {"attn": sparse}
+        pairs = int(state["cnt"].sum().item())
+        f = exec_flops(pairs, d, C)
+        return f, {"attn": f}
+
+    def dense_equiv():
+        per_layer = 4.0 * d * float(info.n_tokens) ** 2 * cfg.heads
+        return per_layer * (cfg.dense_every or 1)
+
+    state.update(step=step, flops=flops, dense_equiv=dense_equiv, nat=nat)
+    return state
+
+
+def measure(state, torch, steps, warmup):
+    timer = Timer(torch)
+    for _ in range(warmup):
+        state["step"](timer)
+    timer.collect()
+    timer.reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.time()
+    e0.record()
+    for _ in range(steps):
+        state["step"](timer)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t_wall
+    ms_step = e0.elapsed_time(e1) / steps
+    timer.collect()
+    return ms_step, wall, timer
+
+
+def cpu_baseline(name, np, seconds=12.0):
+    """Time the fp64 oracle on a seeded sample of sparse-layer (head, query tile) items."""
+    from oracle import attention as OA
+    from oracle import layout as OL
+    from oracle import masks as OM
+    from synth import CONFIGS, make_qkv
+    cfg = CONFIGS[name]
+    heads = [0, cfg.heads // 2]
+    q, k, v = make_qkv(cfg)
+    lay = OL.Layout(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), head_dim=cfg.head_dim,
+                    kind=cfg.kind, tile=cfg.tile, stride=cfg.stride)
+    xs = [OL.permute(np.ascontiguousarray(x[:, :, heads]), lay).astype(np.float64)
+          for x in (q, k, v)]
+    del q, k, v
+    if cfg.mask == "skiparse":
+        lists = OM.skiparse_lists(lay)
+    elif cfg.mask == "window":
+        lists = OM.window_lists(lay, *cfg.window)
+    else:
+        lists = OM.dense_lists(lay)
+    rng = np.random.default_rng(1234)
+    sigma = 1.0 / math.sqrt(cfg.head_dim)
+    done_pairs = 0
+    n_items = 0
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        h = int(rng.integers(0, len(heads)))
+        t = int(rng.integers(0, lay.n_tiles))
+        OA.attention(*xs, lay, OA.shared_lists(lists), sigma, items=[(0, h, t)])
+        done_pairs += len(lists[t])
+        n_items += 1
+    el = time.time() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {
+        "value": exec_flops(done_pairs, cfg.head_dim, lay.tile_tokens) / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n_items} seeded (head, query-tile) items of the {name} sparse layer, "
+                  f"fp64 numpy, {el:.1f}s wall",
+    }
+
+
+def traffic_from_profiles(kernel_src_hash):
+    """HBM bytes per attention launch from the committed counter summary.
+
+    The summary records the sha256 of the attention source it was measured
+    on; if the kernel has changed since, the figure is stale and None is
+    returned.
+    """
+    path = os.path.join(ROOT, "profiles", "attn_skiparse_768p_pmc.md")
+    rec = {}
+    try:
+        with open(path) as f:
+            for line in f:
+                if ":" in line and line.split(":", 1)[0] in ("attn_source_sha256", "bytes_per_launch"):
+                    k, v = line.split(":", 1)
+                    rec[k] = v.strip()
+    except OSError:
+        return None
+    if rec.get("attn_source_sha256") != kernel_src_hash or "bytes_per_launch" not in rec:
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="skiparse_768p")
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also launch one plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the block-sparse attention path has no multi-GPU "
+              "mode in this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_token_amd as vsa
+    torch.cuda.init()
+
+    if args.calib_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1 GiB read + 1 GiB written")
+
+    head = build_workload(args.workload, torch, np, vsa)
+    cfg = head["cfg"]
+    ms_step, wall, timer = measure(head, torch, args.steps, args.warmup)
+    step_flops, per_launch = head["flops"]()
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    layers = cfg.dense_every or 1
+    # roofline: the attention kernel over every attention launch of the timed steps
+    attn_ms = sum(timer.total.get(k, 0.0) for k in ("attn", "attn_dense"))
+    attn_n = sum(timer.count.get(k, 0) for k in ("attn", "attn_dense"))
+    attn_flops = sum(per_launch[k] * timer.count.get(k, 0) for k in per_launch)
+    peak = FP8_PEAK_TFLOPS if cfg.fp8 else BF16_PEAK_TFLOPS
+    achieved = (attn_flops / attn_n) / (attn_ms / attn_n * 1e-3) / 1e12
+    with open(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn.hip"), "rb") as f:
+        src_hash = hashlib.sha256(f.read()).hexdigest()
+    kernels = {k: {"ms_avg": timer.total[k] / timer.count[k], "launches_per_step": timer.count[k] // args.steps}
+               for k in timer.total}
+    for k, f in per_launch.items():
+        if k in kernels:
+            kernels[k]["tflops"] = f / (kernels[k]["ms_avg"] * 1e-3) / 1e12
+            kernels[k]["frac_of_peak"] = kernels[k]["tflops"] / peak
+    info = head["info"]
+    perm_bytes = 2 * info.n_tokens * cfg.heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    if "permute" in kernels:
+        kernels["permute"]["gbs"] = perm_bytes / (kernels["permute"]["ms_avg"] * 1e-3) / 1e9
+        kernels["permute"]["frac_of_hbm_peak"] = kernels["permute"]["gbs"] / HBM_PEAK_GBS
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if cfg.fp8 else cfg.dtype,
+        "data": "synthetic (seeded Q/K/V of the workload's shape and distribution)",
+        "config": {
+            "workload": cfg.name,
+            "grid_thw": [cfg.T, cfg.H, cfg.W],
+            "heads": cfg.heads,
+            "head_dim": cfg.head_dim,
+            "tile": list(cfg.tile),
+            "mask": cfg.mask,
+            "dense_every": cfg.dense_every,
+            "layers_per_step": layers,
+            "ms_per_layer": round(ms_step / layers, 3),
+            "exec_tflop_per_step": round(step_flops / 1e12, 3),
+            "frac_of_mfma_peak": round(value / peak, 4),
+            "dense_equiv_tflops": round(head["dense_equiv"]() / (ms_step * 1e-3) / 1e12, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_from_profiles(src_hash),
+        },
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 2),
+    }
+    del head
+    torch.cuda.empty_cache()
+
+    if not args.only_headline:
+        from synth import CONFIGS
+        per = {}
+        for name in CONFIGS:
+            if name == args.workload:
+                continue
+            st = build_workload(name, torch, np, vsa)
+            ms, _, tm = measure(st, torch, 3, 1)
+            f, pl = st["flops"]()
+            pk = FP8_PEAK_TFLOPS if st["cfg"].fp8 else BF16_PEAK_TFLOPS
+            a_ms = tm.total["attn"] / tm.count["attn"]
+            per[name] = {
+                "ms_per_layer": round(ms / (st["cfg"].dense_every or 1), 4),
+                "exec_tflops_step": round(f / (ms * 1e-3) / 1e12, 2),
+                "attn_ms": round(a_ms, 4),
+                "attn_tflops": round(pl["attn"] / (a_ms * 1e-3) / 1e12, 2),
+                "attn_frac_of_peak": round(pl["attn"] / (a_ms * 1e-3) / 1e12 / pk, 4),
+                "peak_tflops": pk,
+                "kernels_ms": {k: round(tm.total[k] / tm.count[k], 4) for k in tm.total},
+            }
+            log(f"{name}: {per[name]}")
+            del st
+            torch.cuda.empty_cache()
+        out["per_workload"] = per
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on host cores")
+        out["cpu_baseline"] = cpu_baseline(args.workload, np)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
