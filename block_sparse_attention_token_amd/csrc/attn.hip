@@ -4,7 +4,7 @@
 // Type row; FVAttn summary): each query tile visits only the key/value tiles
 // of its list, with an online softmax.
 //
-// One wavefront owns one query tile (32 or 64 rows, in 32-row groups) and
+// A wavefront owns 32 query rows (bf16) or one 64-row query tile (fp8) and
 // computes the transposed products
 //   S^T  = K . Q^T     A = K rows (LDS), B = Q^T (registers)
 //   O^T += V^T . P^T   A = V^T rows (LDS), B = P^T (registers)
@@ -15,15 +15,14 @@
 // accumulator holds them and V^T is written to LDS in that same order, so P
 // never moves between lanes.
 //
-// Work shapes:
-//   WAVES == 1: one wave per query tile, walking its own list (routed
-//               masks, where neighbouring tiles share few key tiles);
-//   WAVES == 4: four waves = four consecutive query tiles that walk the
-//               ascending union of their lists once, each K/V tile loaded
-//               into LDS once for all four (dense, Skiparse-2D and window
-//               lists); a wave whose list lacks a tile skips its math. The
-//               LDS tiles are double-buffered: tile s+1 is fetched while
-//               tile s is computed, with one barrier per tile.
+// Work shapes (QPW = query tiles per workgroup):
+//   QPW == 1: one query tile per workgroup, walking its own list (routed
+//             masks, where neighbouring tiles share few key tiles);
+//   QPW == 4: four consecutive query tiles walk the ascending union of their
+//             lists once, each K/V tile loaded into LDS once for all of them
+//             (dense, Skiparse-2D and window lists); waves whose list lacks
+//             a tile skip its math. The LDS tiles are double-buffered: tile
+//             s+1 is fetched while tile s is computed, one barrier per tile.
 // The softmax subtracts a lazily raised running maximum: it only moves when
 // a score exceeds it by more than 2^kLazy (exp2 units), so O^T is rarely
 // rescaled. Pad keys are masked from one ballot per padded tile.
@@ -71,20 +70,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 struct WaveWork {
   long long head_row0;     // first row of this (b, head) in the tiled tensors
   int bh;                  // b * heads + head
-  int qt;                  // this wave's query tile
+  int slot;                // which of the workgroup's query tiles this wave works on
+  int qt;                  // that query tile
   bool active;             // qt < n_tiles
   const int32_t* list;     // null: dense
   int cnt;
 };
 
-template <int WAVES>
+// QPW query tiles per workgroup, WPQ waves per query tile.
+template <int QPW, int WPQ>
 __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs& a, int n_work,
                                               int wave) {
   WaveWork w;
   const int item = xcd_remap(blockIdx.x, n_work);
-  const int wg_per_bh = (L.n_tiles + WAVES - 1) / WAVES;
+  const int wg_per_bh = (L.n_tiles + QPW - 1) / QPW;
   w.bh = item / wg_per_bh;
-  w.qt = (item - w.bh * wg_per_bh) * WAVES + wave;
+  w.slot = wave / WPQ;
+  w.qt = (item - w.bh * wg_per_bh) * QPW + w.slot;
   w.active = w.qt < L.n_tiles;
   w.head_row0 = (long long)w.bh * L.n_padded;
   w.list = nullptr;
@@ -101,19 +103,22 @@ __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs
   return w;
 }
 
-// WAVES > 1: write the ascending union of the waves' lists into sched[], each
-// entry = tile | (mask of waves listing it) << 24; returns its length.
-template <int WAVES>
+// QPW > 1: write the ascending union of the query tiles' lists into sched[],
+// each entry = tile | (mask of query-tile slots listing it) << 24; returns
+// its length.
+template <int QPW, int WPQ>
 __device__ int build_schedule(const DevLayout& L, const WaveWork& w, int* dyn, int* scan,
-                              int tid, int lane, int wave) {
-  constexpr int THREADS = 64 * WAVES;
+                              int tid, int lane) {
+  constexpr int THREADS = 64 * QPW * WPQ;
   int* marks = dyn;
   int* sched = dyn + L.n_tiles;
   for (int t = tid; t < L.n_tiles; t += THREADS) marks[t] = 0;
   __syncthreads();
-  for (int i = lane; i < w.cnt; i += 64) {
-    const int t = w.list ? min(max(w.list[i], 0), L.n_tiles - 1) : i;
-    atomicOr(&marks[t], 1 << wave);
+  if ((tid >> 6) % WPQ == 0) {
+    for (int i = lane; i < w.cnt; i += 64) {
+      const int t = w.list ? min(max(w.list[i], 0), L.n_tiles - 1) : i;
+      atomicOr(&marks[t], 1 << w.slot);
+    }
   }
   __syncthreads();
   const int per = (L.n_tiles + THREADS - 1) / THREADS;
@@ -136,14 +141,14 @@ __device__ int build_schedule(const DevLayout& L, const WaveWork& w, int* dyn, i
   return len;
 }
 
-template <int WAVES>
+template <int QPW>
 __device__ __forceinline__ int sched_tile(const int* sched, const WaveWork& w, int s, int n_tiles) {
-  if constexpr (WAVES > 1) return sched[s] & 0xFFFFFF;
+  if constexpr (QPW > 1) return sched[s] & 0xFFFFFF;
   else return w.list ? min(max(w.list[s], 0), n_tiles - 1) : s;
 }
-template <int WAVES>
-__device__ __forceinline__ bool sched_mine(const int* sched, int s, int wave) {
-  if constexpr (WAVES > 1) return (sched[s] >> (24 + wave)) & 1;
+template <int QPW>
+__device__ __forceinline__ bool sched_mine(const int* sched, int s, int slot) {
+  if constexpr (QPW > 1) return (sched[s] >> (24 + slot)) & 1;
   else return true;
 }
 
@@ -218,22 +223,26 @@ __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint
 __device__ __forceinline__ int vt_swizzle(int c, int cpr) { return (c ^ (c >> 3)) & (cpr - 1); }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel
-template <int TILE, int D, int WAVES, bool F32IN>
-__global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(DevLayout L, AttnArgs a,
-                                                                  int n_work) {
-  constexpr int QG = TILE / 32;          // 32-row query groups per wave
+// bf16 kernel: one wave = 32 query rows (a query tile of 64 rows takes two
+// waves, which share the K/V tiles in LDS). About 200 registers per wave let
+// two waves share each SIMD, so one wave's softmax runs while the other's
+// MFMAs do. QPW query tiles per workgroup: 4 for shared lists (union walk,
+// LDS double-buffered), 1 for routed lists.
+template <int TILE, int D, int QPW, bool F32IN>
+__global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
+  constexpr int WPQ = TILE / 32;         // waves per query tile
   constexpr int MB = TILE / 32;          // 32-token blocks of a kv tile
   constexpr int KS = D / 16;             // QK^T k-steps over the head dim
   constexpr int CB = D / 32;             // 32-channel blocks of O^T
   constexpr int PS = TILE / 16;          // PV k-steps over kv tokens
   constexpr int CPR_K = D / 8;           // 16-byte chunks per K row
   constexpr int CPR_V = TILE / 8;        // 16-byte chunks per V^T row
-  constexpr int THREADS = 64 * WAVES;
+  constexpr int THREADS = 64 * QPW * WPQ;
   constexpr int K_PER_T = TILE * CPR_K / THREADS;
   constexpr int V_PIECES = (TILE / 4) * (D / 8);         // 4 tokens x 8 channels
   constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
-  constexpr int NBUF = WAVES > 1 ? 2 : 1;
+  constexpr int NBUF = QPW > 1 ? 2 : 1;
   constexpr float kLazy = 8.0f;
   static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
   static_assert((TILE * CPR_K) % THREADS == 0, "K tile split");
@@ -241,42 +250,34 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(DevLayout L, A
   __shared__ uint4 k_lds[NBUF][TILE * CPR_K];
   __shared__ uint4 v_lds[NBUF][D * CPR_V];
   __shared__ int scan[THREADS];
-  extern __shared__ int dyn[];           // WAVES > 1: marks + schedule
+  extern __shared__ int dyn[];           // QPW > 1: marks + schedule
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  const int rg = wave % WPQ;             // which 32 rows of the query tile
 
-  const WaveWork ww = wave_work<WAVES>(L, a, n_work, wave);
+  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
   const int* sched = dyn + L.n_tiles;
   int len;
-  if constexpr (WAVES > 1) len = build_schedule<WAVES>(L, ww, dyn, scan, tid, lane, wave);
+  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
   else len = ww.cnt;
 
-  // Q^T fragments (B operand): query row 32*qg + l32, channels 16*ks + 8*half ..
+  // Q^T fragments (B operand): query row 32*rg + l32, channels 16*ks + 8*half ..
   const int qt_c = min(ww.qt, L.n_tiles - 1);
-  uint4 qf[QG][KS];
+  uint4 qf[KS];
+  {
+    const long long row = ww.head_row0 + (long long)qt_c * TILE + 32 * rg + l32;
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const long long row = ww.head_row0 + (long long)qt_c * TILE + 32 * qg + l32;
-      qf[qg][ks] = load8<F32IN>(a.q, row * D + ks * 16 + half * 8);
-    }
-
-  f32x16_t oacc[CB][QG];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) oacc[cb][qg] = f32x16_t{};
-  float m_run[QG], l_run[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    m_run[qg] = -INFINITY;
-    l_run[qg] = 0.0f;
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = load8<F32IN>(a.q, row * D + ks * 16 + half * 8);
   }
+
+  f32x16_t oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
 
   uint4 kreg[K_PER_T];
   uint4 vreg[V_PER_T][4];
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(DevLayout L, A
 
   const float sl2 = a.scale_log2;
   if (len > 0) {
-    const int t0 = sched_tile<WAVES>(sched, ww, 0, L.n_tiles);
+    const int t0 = sched_tile<QPW>(sched, ww, 0, L.n_tiles);
     load_k(t0);
     load_v(t0);
     store_k(0);
@@ -358,70 +359,65 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(DevLayout L, A
 
   for (int s = 0; s < len; ++s) {
     const int cur = NBUF == 2 ? (s & 1) : 0;
-    const int tile = sched_tile<WAVES>(sched, ww, s, L.n_tiles);
-    const bool mine = sched_mine<WAVES>(sched, s, wave);
+    const int tile = sched_tile<QPW>(sched, ww, s, L.n_tiles);
+    const bool mine = sched_mine<QPW>(sched, s, ww.slot);
     const bool has_next = s + 1 < len;
-    const int next = has_next ? sched_tile<WAVES>(sched, ww, s + 1, L.n_tiles) : 0;
+    const int next = has_next ? sched_tile<QPW>(sched, ww, s + 1, L.n_tiles) : 0;
     if (has_next) {
       load_k(next);
       if constexpr (NBUF == 2) load_v(next);
     }
+    f32x16_t sacc[MB];
     if (mine) {
       // ---- S^T = K . Q^T
-      f32x16_t sacc[QG][MB];
 #pragma unroll
-      for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) sacc[qg][mb] = f32x16_t{};
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int r = 32 * mb + l32;
           const uint4 av = k_lds[cur][r * CPR_K + ((2 * ks + half) ^ (r % CPR_K))];
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg)
-            sacc[qg][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, qf[qg][ks]),
-                sacc[qg][mb], 0, 0, 0);
+          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, qf[ks]), sacc[mb],
+              0, 0, 0);
         }
-      if constexpr (NBUF == 1) {
-        __syncthreads();                          // done reading K(tile)
-        if (has_next) {
-          store_k(0);
-          load_v(next);
-        }
+    }
+    if constexpr (NBUF == 1) {
+      __syncthreads();                            // done reading K(tile)
+      if (has_next) {
+        store_k(0);
+        load_v(next);
       }
+    }
+    if (mine) {
       bool full;
       const uint32_t bits = kv_valid_bits<MB>(L, tile, lane, half, full);
-      // ---- softmax and O^T += V^T . P^T, one query group at a time
+      const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazy, m_run, l_run);
+      if (alpha != 1.0f) {
 #pragma unroll
-      for (int qg = 0; qg < QG; ++qg) {
-        const float alpha = softmax_step<MB>(sacc[qg], full, bits, sl2, kLazy, m_run[qg], l_run[qg]);
-        if (alpha != 1.0f) {
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[cb][qg] *= alpha;
-        }
-        uint4 pk[PS];
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-          const int mb = ps >> 1, r0 = 8 * (ps & 1);
-          pk[ps] = make_uint4(pack2(sacc[qg][mb][r0 + 0], sacc[qg][mb][r0 + 1]),
-                              pack2(sacc[qg][mb][r0 + 2], sacc[qg][mb][r0 + 3]),
-                              pack2(sacc[qg][mb][r0 + 4], sacc[qg][mb][r0 + 5]),
-                              pack2(sacc[qg][mb][r0 + 6], sacc[qg][mb][r0 + 7]));
-        }
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const int c = 32 * cb + l32;
-            const uint4 av = v_lds[cur][c * CPR_V + ((2 * ps + half) ^ vt_swizzle(c, CPR_V))];
-            oacc[cb][qg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, pk[ps]),
-                oacc[cb][qg], 0, 0, 0);
-          }
+        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
       }
+      uint4 pk[PS];
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps) {
+        const int mb = ps >> 1, r0 = 8 * (ps & 1);
+        pk[ps] = make_uint4(pack2(sacc[mb][r0 + 0], sacc[mb][r0 + 1]),
+                            pack2(sacc[mb][r0 + 2], sacc[mb][r0 + 3]),
+                            pack2(sacc[mb][r0 + 4], sacc[mb][r0 + 5]),
+                            pack2(sacc[mb][r0 + 6], sacc[mb][r0 + 7]));
+      }
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int c = 32 * cb + l32;
+          const uint4 av = v_lds[cur][c * CPR_V + ((2 * ps + half) ^ vt_swizzle(c, CPR_V))];
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, pk[ps]), oacc[cb],
+              0, 0, 0);
+        }
     }
     if constexpr (NBUF == 2) {
       if (has_next) {
@@ -441,32 +437,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bf16_kernel(DevLayout L, A
   // ---- epilogue: normalise and write O (and lse)
   if (!ww.active) return;
   const TileValid tq = tile_valid(L, ww.qt);
+  const int qrow = 32 * rg + l32;
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const bool real = row_is_real(L, tq, qrow);
+  const float inv = (real && lt > 0.0f) ? 1.0f / lt : 0.0f;
+  const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    const int qrow = 32 * qg + l32;
-    const float lt = l_run[qg] + __shfl_xor(l_run[qg], 32);
-    const bool real = row_is_real(L, tq, qrow);
-    const float inv = (real && lt > 0.0f) ? 1.0f / lt : 0.0f;
-    const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = 32 * cb + 8 * g + 4 * half;
-        const float o0 = oacc[cb][qg][4 * g + 0] * inv, o1 = oacc[cb][qg][4 * g + 1] * inv;
-        const float o2 = oacc[cb][qg][4 * g + 2] * inv, o3 = oacc[cb][qg][4 * g + 3] * inv;
-        if constexpr (F32IN) {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * D + c0) =
-              make_float4(o0, o1, o2, o3);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
-              make_uint2(pack2(o0, o1), pack2(o2, o3));
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * cb + 8 * g + 4 * half;
+      const float o0 = oacc[cb][4 * g + 0] * inv, o1 = oacc[cb][4 * g + 1] * inv;
+      const float o2 = oacc[cb][4 * g + 2] * inv, o3 = oacc[cb][4 * g + 3] * inv;
+      if constexpr (F32IN) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * D + c0) =
+            make_float4(o0, o1, o2, o3);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
+            make_uint2(pack2(o0, o1), pack2(o2, o3));
       }
-    if (a.lse && half == 0) {
-      a.lse[orow] = (real && lt > 0.0f) ? (m_run[qg] + __log2f(lt)) * 0.69314718055994531f
-                                        : -INFINITY;
     }
+  if (a.lse && half == 0) {
+    a.lse[orow] = (real && lt > 0.0f) ? (m_run + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -495,8 +487,8 @@ __device__ __forceinline__ i32x8_t cat8(uint4 x, uint4 y) {
 }
 
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void attn_fp8_kernel(DevLayout L, AttnArgs a,
-                                                                 int n_work) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int TILE = 64, D = 128, QG = 2, MB = 2, CB = 4, KS = 2;
   constexpr int THREADS = 64 * WAVES;
   constexpr int K_PER_T = TILE * D / 16 / THREADS;   // 512 chunks of 16 codes
@@ -515,10 +507,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fp8_kernel(DevLayout L, At
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const WaveWork ww = wave_work<WAVES>(L, a, n_work, wave);
+  const WaveWork ww = wave_work<WAVES, 1>(L, a, n_work, wave);
   const int* sched = dyn + L.n_tiles;
   int len;
-  if constexpr (WAVES > 1) len = build_schedule<WAVES>(L, ww, dyn, scan, tid, lane, wave);
+  if constexpr (WAVES > 1) len = build_schedule<WAVES, 1>(L, ww, dyn, scan, tid, lane);
   else len = ww.cnt;
 
   const uint8_t* Q = static_cast<const uint8_t*>(a.q);
@@ -637,7 +629,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fp8_kernel(DevLayout L, At
   for (int s = 0; s < len; ++s) {
     const int cur = s & 1;
     const int tile = sched_tile<WAVES>(sched, ww, s, L.n_tiles);
-    const bool mine = sched_mine<WAVES>(sched, s, wave);
+    const bool mine = sched_mine<WAVES>(sched, s, ww.slot);
     const bool has_next = s + 1 < len;
     if (has_next) {
       const int next = sched_tile<WAVES>(sched, ww, s + 1, L.n_tiles);
@@ -730,12 +722,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fp8_kernel(DevLayout L, At
 }
 
 // ---------------------------------------------------------------------------
-template <int TILE, int D, int WAVES, bool F32IN>
+template <int TILE, int D, int QPW, bool F32IN>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
-  const int n_work = L.B * L.heads * ((L.n_tiles + WAVES - 1) / WAVES);
-  const size_t dyn = WAVES > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_bf16_kernel<TILE, D, WAVES, F32IN>), dim3(n_work), dim3(64 * WAVES),
-                     dyn, s, L, a, n_work);
+  const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
+  const size_t dyn = QPW > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
+  hipLaunchKernelGGL((attn_bf16_kernel<TILE, D, QPW, F32IN>), dim3(n_work),
+                     dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
