@@ -4,8 +4,7 @@
 // Type row; FVAttn summary): each query tile visits only the key/value tiles
 // of its list, with an online softmax.
 //
-// A wavefront owns 32 query rows (bf16) or one 64-row query tile (fp8) and
-// computes the transposed products
+// A wavefront owns 32 query rows and computes the transposed products
 //   S^T  = K . Q^T     A = K rows (LDS), B = Q^T (registers)
 //   O^T += V^T . P^T   A = V^T rows (LDS), B = P^T (registers)
 // so every lane holds one query row (lane % 32) of S^T, P^T and O^T: the
@@ -44,18 +43,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 8 consecutive elements at element offset `off` as 8 bf16 in a uint4.
-template <bool F32IN>
-__device__ __forceinline__ uint4 load8(const void* base, long long off) {
-  if constexpr (F32IN) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 x = p[0], y = p[1];
-    return make_uint4(pack2(x.x, x.y), pack2(x.z, x.w), pack2(y.x, y.y), pack2(y.z, y.w));
-  } else {
-    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-  }
-}
-
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {   // lo16(a) | lo16(b) << 16
   return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
@@ -64,6 +51,34 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {   // hi16(
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer-resource loads: the base of one (b, head) slice of a tensor sits in
+// SGPRs and each load takes a 32-bit byte offset (VGPR part + SGPR part), so
+// tile loads need no 64-bit address registers; offsets past num_records read
+// as zero instead of faulting.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFFll ? bytes : 0x7FFFFFFFll),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// 8 consecutive elements at byte offset voff + soff as 8 bf16 (f32 input: 32 bytes, rounded)
+template <bool F32IN>
+__device__ __forceinline__ uint4 bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (F32IN) {
+    const uint4 x = bload(r, voff, soff), y = bload(r, voff + 16, soff);
+    return make_uint4(pack2(__uint_as_float(x.x), __uint_as_float(x.y)),
+                      pack2(__uint_as_float(x.z), __uint_as_float(x.w)),
+                      pack2(__uint_as_float(y.x), __uint_as_float(y.y)),
+                      pack2(__uint_as_float(y.z), __uint_as_float(y.w)));
+  } else {
+    return bload(r, voff, soff);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Work assignment and the per-workgroup schedule (shared by both kernels).
@@ -153,14 +168,17 @@ __device__ __forceinline__ bool sched_mine(const int* sched, int s, int slot) {
 }
 
 // Bit (16*mb + r) set iff the kv token this lane holds in register r of S^T
-// block mb is a real token. Wave-uniform `full` short-cuts the common case.
+// block mb (token tok0 + 32*mb + 8*(r/4) + 4*half + r%4 of the tile) is a
+// real token. Wave-uniform `full` short-cuts the common case.
 template <int MB>
-__device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, int lane, int half,
-                                                  bool& full) {
+__device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, int tok0, int lane,
+                                                  int half, bool& full) {
   const TileValid tv = tile_valid(L, tile);
-  full = tv.full;
-  if (full) return 0xFFFFFFFFu;
-  const bool v = lane < 32 * MB && row_is_real(L, tv, lane);
+  bool f = tv.full;
+  if (!f && L.kind == 1) f = tok0 + 32 * MB <= tv.vlen;   // Skiparse: pads only at the tail
+  full = f;
+  if (f) return 0xFFFFFFFFu;
+  const bool v = lane < 32 * MB && row_is_real(L, tv, tok0 + lane);
   const unsigned long long vm = __ballot(v);
   uint32_t m = 0;
 #pragma unroll
@@ -173,32 +191,26 @@ __device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, 
 
 // Online-softmax step on one 32-row query group: scores s (raw dot products,
 // MB blocks of 16 per lane) become p = exp2(s * sl2 - m_run), in place.
+// sl2 >= 0 (a negative softmax scale is folded into Q by the caller).
 // Returns the factor O must be multiplied by (1 when m_run did not move).
 template <int MB>
 __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint32_t bits,
                                               float sl2, float lazy, float& m_run, float& l_run) {
-  float hi = -INFINITY, lo = INFINITY;
+  float hi = -INFINITY;
   if (full) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        hi = fmaxf(hi, s[mb][r]);
-        lo = fminf(lo, s[mb][r]);
-      }
+      for (int r = 0; r < 16; ++r) hi = fmaxf(hi, s[mb][r]);
   } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = (bits >> (16 * mb + r)) & 1u;
-        hi = fmaxf(hi, ok ? s[mb][r] : -INFINITY);
-        lo = fminf(lo, ok ? s[mb][r] : INFINITY);
-      }
+      for (int r = 0; r < 16; ++r)
+        hi = fmaxf(hi, ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY);
   }
   hi = fmaxf(hi, __shfl_xor(hi, 32));
-  lo = fminf(lo, __shfl_xor(lo, 32));
-  const float mx = sl2 >= 0.0f ? hi * sl2 : lo * sl2;    // max over the tile of s * sl2
+  const float mx = hi * sl2;                             // max over the tile of s * sl2
   float alpha = 1.0f;
   if (mx > m_run + lazy) {
     alpha = fast_exp2(m_run - mx);                       // 0 on the first tile
@@ -223,219 +235,151 @@ __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint
 __device__ __forceinline__ int vt_swizzle(int c, int cpr) { return (c ^ (c >> 3)) & (cpr - 1); }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: one wave = 32 query rows (a query tile of 64 rows takes two
-// waves, which share the K/V tiles in LDS). About 200 registers per wave let
-// two waves share each SIMD, so one wave's softmax runs while the other's
-// MFMAs do. QPW query tiles per workgroup: 4 for shared lists (union walk,
-// LDS double-buffered), 1 for routed lists.
-template <int TILE, int D, int QPW, bool F32IN>
-__global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
-  constexpr int WPQ = TILE / 32;         // waves per query tile
-  constexpr int MB = TILE / 32;          // 32-token blocks of a kv tile
-  constexpr int KS = D / 16;             // QK^T k-steps over the head dim
-  constexpr int CB = D / 32;             // 32-channel blocks of O^T
-  constexpr int PS = TILE / 16;          // PV k-steps over kv tokens
-  constexpr int CPR_K = D / 8;           // 16-byte chunks per K row
-  constexpr int CPR_V = TILE / 8;        // 16-byte chunks per V^T row
-  constexpr int THREADS = 64 * QPW * WPQ;
-  constexpr int K_PER_T = TILE * CPR_K / THREADS;
-  constexpr int V_PIECES = (TILE / 4) * (D / 8);         // 4 tokens x 8 channels
-  constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
-  constexpr int NBUF = QPW > 1 ? 2 : 1;
-  constexpr float kLazy = 8.0f;
-  static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
-  static_assert((TILE * CPR_K) % THREADS == 0, "K tile split");
+// bf16 kernels. One wave owns 32 query rows (a 64-row query tile takes two
+// waves) and about 200 registers, so two waves share each SIMD and one
+// wave's softmax can run while the other's MFMAs do.
 
-  __shared__ uint4 k_lds[NBUF][TILE * CPR_K];
-  __shared__ uint4 v_lds[NBUF][D * CPR_V];
-  __shared__ int scan[THREADS];
-  extern __shared__ int dyn[];           // QPW > 1: marks + schedule
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const int rg = wave % WPQ;             // which 32 rows of the query tile
-
-  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
-  const int* sched = dyn + L.n_tiles;
-  int len;
-  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
-  else len = ww.cnt;
-
-  // Q^T fragments (B operand): query row 32*rg + l32, channels 16*ks + 8*half ..
-  const int qt_c = min(ww.qt, L.n_tiles - 1);
-  uint4 qf[KS];
-  {
-    const long long row = ww.head_row0 + (long long)qt_c * TILE + 32 * rg + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = load8<F32IN>(a.q, row * D + ks * 16 + half * 8);
-  }
-
-  f32x16_t oacc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
-
+// Register staging of one kv block (KVH tokens x D channels) and its store
+// into LDS: K row-major with 16-byte chunks XOR-swizzled by row; V
+// transposed to V^T rows (one per channel) in the token order of the S^T
+// accumulator (register r of block mb in half-wave h holds token
+// 32*mb + 8*(r/4) + 4*h + r%4), built from 4-token x 8-channel pieces.
+template <int KVH, int D, int THREADS, bool F32IN>
+struct BfTile {
+  static constexpr int ES = F32IN ? 4 : 2;
+  static constexpr int CPR_K = D / 8;               // 16-byte chunks per K row
+  static constexpr int CPR_V = KVH / 8;             // 16-byte chunks per V^T row
+  static constexpr int K_CHUNKS = KVH * CPR_K;
+  static constexpr int K_PER_T = (K_CHUNKS + THREADS - 1) / THREADS;
+  static constexpr int V_PIECES = (KVH / 4) * (D / 8);
+  static constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
+  static constexpr int K_LDS = KVH * CPR_K;         // uint4 per K buffer
+  static constexpr int V_LDS = D * CPR_V;           // uint4 per V^T buffer
   uint4 kreg[K_PER_T];
   uint4 vreg[V_PER_T][4];
-  auto load_k = [&](int tile) {
-    const long long base = (ww.head_row0 + (long long)tile * TILE) * D;
+
+  // block_off: byte offset of the kv block inside this (b, head) slice
+  __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rv, uint32_t block_off, int tid) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * THREADS;
-      kreg[i] = load8<F32IN>(a.k, base + (long long)(c / CPR_K) * D + (c % CPR_K) * 8);
+      const int c = tid + i * THREADS;            // chunk c = 8 elements at element 8*c
+      if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS)
+        kreg[i] = bload8<F32IN>(rk, tid * 8 * ES, block_off + i * THREADS * 8 * ES);
     }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * THREADS;
-      const int r = c / CPR_K, ch = c % CPR_K;
-      k_lds[buf][r * CPR_K + (ch ^ (r % CPR_K))] = kreg[i];
-    }
-  };
-  // V piece u = 4 consecutive kv tokens x 8 channels (channel chunk cc,
-  // quarter q4); its tokens go to V^T positions 4*q4 .. 4*q4+3, which is the
-  // token order of the S^T accumulator: register r of block mb in half-wave
-  // h holds token 32*mb + 8*(r/4) + 4*h + r%4.
-  auto load_v = [&](int tile) {
-    const long long base = (ww.head_row0 + (long long)tile * TILE) * D;
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
-      if (u < V_PIECES) {
+      if (V_PIECES % THREADS == 0 || u < V_PIECES) {
         const int cc = u % (D / 8), q4 = u / (D / 8);
         const int pc = q4 >> 1;
         const int tok0 = 16 * (pc >> 1) + 4 * (pc & 1) + 8 * (q4 & 1);
+        const uint32_t voff = (uint32_t)((tok0 * D + cc * 8) * ES);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[i][j] = load8<F32IN>(a.v, base + (long long)(tok0 + j) * D + cc * 8);
+        for (int j = 0; j < 4; ++j) vreg[i][j] = bload8<F32IN>(rv, voff + j * D * ES, block_off);
       }
     }
-  };
-  auto store_v = [&](int buf) {
+  }
+  __device__ __forceinline__ void store(uint4* k_lds, uint4* v_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int c = tid + i * THREADS;
+      if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS) {
+        const int r = c / CPR_K, ch = c % CPR_K;
+        k_lds[r * CPR_K + (ch ^ (r % CPR_K))] = kreg[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
-      if (u < V_PIECES) {
+      if (V_PIECES % THREADS == 0 || u < V_PIECES) {
         const int cc = u % (D / 8), q4 = u / (D / 8);
         const int pc = q4 >> 1;
-        const uint32_t in[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
-                                   {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w},
-                                   {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w},
-                                   {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w}};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = cc * 8 + e;
           const int dw = e >> 1;
           uint2 o;
           if (e & 1) {
-            o.x = perm_hi(in[0][dw], in[1][dw]);
-            o.y = perm_hi(in[2][dw], in[3][dw]);
+            o.x = perm_hi(vreg[i][0][dw], vreg[i][1][dw]);
+            o.y = perm_hi(vreg[i][2][dw], vreg[i][3][dw]);
           } else {
-            o.x = perm_lo(in[0][dw], in[1][dw]);
-            o.y = perm_lo(in[2][dw], in[3][dw]);
+            o.x = perm_lo(vreg[i][0][dw], vreg[i][1][dw]);
+            o.y = perm_lo(vreg[i][2][dw], vreg[i][3][dw]);
           }
-          uint2* dst =
-              reinterpret_cast<uint2*>(&v_lds[buf][c * CPR_V + (pc ^ vt_swizzle(c, CPR_V))]);
+          uint2* dst = reinterpret_cast<uint2*>(&v_lds[c * CPR_V + (pc ^ vt_swizzle(c, CPR_V))]);
           dst[q4 & 1] = o;
         }
       }
     }
-  };
-
-  const float sl2 = a.scale_log2;
-  if (len > 0) {
-    const int t0 = sched_tile<QPW>(sched, ww, 0, L.n_tiles);
-    load_k(t0);
-    load_v(t0);
-    store_k(0);
-    store_v(0);
-    __syncthreads();
   }
+};
 
-  for (int s = 0; s < len; ++s) {
-    const int cur = NBUF == 2 ? (s & 1) : 0;
-    const int tile = sched_tile<QPW>(sched, ww, s, L.n_tiles);
-    const bool mine = sched_mine<QPW>(sched, s, ww.slot);
-    const bool has_next = s + 1 < len;
-    const int next = has_next ? sched_tile<QPW>(sched, ww, s + 1, L.n_tiles) : 0;
-    if (has_next) {
-      load_k(next);
-      if constexpr (NBUF == 2) load_v(next);
+// S^T (KVH kv tokens x 32 query rows) = K . Q^T from one K buffer
+template <int KVH, int D>
+__device__ __forceinline__ void bf_scores(const uint4* k_lds, const uint4 (&qf)[D / 16],
+                                          f32x16_t (&sacc)[KVH / 32], int l32, int half) {
+  constexpr int CPR_K = D / 8;
+#pragma unroll
+  for (int mb = 0; mb < KVH / 32; ++mb) sacc[mb] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < KVH / 32; ++mb) {
+      const int r = 32 * mb + l32;
+      const uint4 av = k_lds[r * CPR_K + ((2 * ks + half) ^ (r % CPR_K))];
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, qf[ks]),
+                                                         sacc[mb], 0, 0, 0);
     }
-    f32x16_t sacc[MB];
-    if (mine) {
-      // ---- S^T = K . Q^T
+}
+
+// P^T (bf16, B operands of the PV product) from the probabilities in sacc
+template <int KVH>
+__device__ __forceinline__ void bf_pack_p(const f32x16_t (&p)[KVH / 32], uint4 (&pk)[KVH / 16]) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = 32 * mb + l32;
-          const uint4 av = k_lds[cur][r * CPR_K + ((2 * ks + half) ^ (r % CPR_K))];
-          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, qf[ks]), sacc[mb],
-              0, 0, 0);
-        }
-    }
-    if constexpr (NBUF == 1) {
-      __syncthreads();                            // done reading K(tile)
-      if (has_next) {
-        store_k(0);
-        load_v(next);
-      }
-    }
-    if (mine) {
-      bool full;
-      const uint32_t bits = kv_valid_bits<MB>(L, tile, lane, half, full);
-      const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazy, m_run, l_run);
-      if (alpha != 1.0f) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
-      }
-      uint4 pk[PS];
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        const int mb = ps >> 1, r0 = 8 * (ps & 1);
-        pk[ps] = make_uint4(pack2(sacc[mb][r0 + 0], sacc[mb][r0 + 1]),
-                            pack2(sacc[mb][r0 + 2], sacc[mb][r0 + 3]),
-                            pack2(sacc[mb][r0 + 4], sacc[mb][r0 + 5]),
-                            pack2(sacc[mb][r0 + 6], sacc[mb][r0 + 7]));
-      }
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int c = 32 * cb + l32;
-          const uint4 av = v_lds[cur][c * CPR_V + ((2 * ps + half) ^ vt_swizzle(c, CPR_V))];
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, pk[ps]), oacc[cb],
-              0, 0, 0);
-        }
-    }
-    if constexpr (NBUF == 2) {
-      if (has_next) {
-        store_k(cur ^ 1);
-        store_v(cur ^ 1);
-      }
-      __syncthreads();
-    } else {
-      __syncthreads();                            // done reading V^T(tile)
-      if (has_next) {
-        store_v(0);
-        __syncthreads();
-      }
-    }
+  for (int ps = 0; ps < KVH / 16; ++ps) {
+    const int mb = ps >> 1, r0 = 8 * (ps & 1);
+    pk[ps] = make_uint4(pack2(p[mb][r0 + 0], p[mb][r0 + 1]), pack2(p[mb][r0 + 2], p[mb][r0 + 3]),
+                        pack2(p[mb][r0 + 4], p[mb][r0 + 5]), pack2(p[mb][r0 + 6], p[mb][r0 + 7]));
   }
+}
 
-  // ---- epilogue: normalise and write O (and lse)
-  if (!ww.active) return;
+// O^T += V^T . P^T from one V^T buffer
+template <int KVH, int D>
+__device__ __forceinline__ void bf_pv(const uint4* v_lds, const uint4 (&pk)[KVH / 16],
+                                      f32x16_t (&oacc)[D / 32], int l32, int half) {
+  constexpr int CPR_V = KVH / 8;
+#pragma unroll
+  for (int ps = 0; ps < KVH / 16; ++ps)
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int c = 32 * cb + l32;
+      const uint4 av = v_lds[c * CPR_V + ((2 * ps + half) ^ vt_swizzle(c, CPR_V))];
+      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, pk[ps]),
+                                                         oacc[cb], 0, 0, 0);
+    }
+}
+
+// Q^T fragments for query row 32*rg + l32 of tile qt; a negative softmax
+// scale is folded into Q (sign flip) so the softmax only needs a maximum.
+template <int TILE, int D, bool F32IN>
+__device__ __forceinline__ void bf_load_q(rsrc_t rq, int qt, int rg, int l32, int half,
+                                          uint32_t qsign, uint4 (&qf)[D / 16]) {
+  constexpr int ES = F32IN ? 4 : 2;
+  const uint32_t row_off = (uint32_t)((qt * TILE + 32 * rg + l32) * D * ES);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint4 x = bload8<F32IN>(rq, row_off + (ks * 16 + half * 8) * ES, 0);
+    qf[ks] = make_uint4(x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign);
+  }
+}
+
+// Normalise and write this wave's 32 output rows (and lse)
+template <int TILE, int D, bool F32IN>
+__device__ __forceinline__ void bf_epilogue(const DevLayout& L, const AttnArgs& a, const WaveWork& ww,
+                                            int rg, int l32, int half, const f32x16_t (&oacc)[D / 32],
+                                            float m_run, float l_run) {
   const TileValid tq = tile_valid(L, ww.qt);
   const int qrow = 32 * rg + l32;
   const float lt = l_run + __shfl_xor(l_run, 32);
@@ -443,7 +387,7 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   const float inv = (real && lt > 0.0f) ? 1.0f / lt : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+  for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int c0 = 32 * cb + 8 * g + 4 * half;
@@ -462,18 +406,216 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   }
 }
 
+constexpr float kLazyBf16 = 8.0f;
+
+// Generic kernel: routed lists (QPW = 1) and 32-token tiles. Each list entry
+// is walked as TILE/KVH kv blocks of KVH tokens, double-buffered in LDS.
+// KVH = 32 for 64-token tiles with routed lists keeps two buffers within
+// 32 KB, so four workgroups (eight waves) fit a CU.
+template <int TILE, int KVH, int D, int QPW, bool F32IN>
+__global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
+  constexpr int WPQ = TILE / 32;         // waves per query tile
+  constexpr int SUB = TILE / KVH;        // kv blocks per tile
+  constexpr int MB = KVH / 32;
+  constexpr int THREADS = 64 * QPW * WPQ;
+  using IO = BfTile<KVH, D, THREADS, F32IN>;
+  static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
+
+  __shared__ uint4 k_lds[2][IO::K_LDS];
+  __shared__ uint4 v_lds[2][IO::V_LDS];
+  __shared__ int scan[THREADS];
+  extern __shared__ int dyn[];           // QPW > 1: marks + schedule
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = wave % WPQ;
+
+  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
+  const int* sched = dyn + L.n_tiles;
+  int len;
+  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
+  else len = ww.cnt;
+
+  const long long head_bytes = L.n_padded * D * IO::ES;
+  const char* qb = static_cast<const char*>(a.q) + ww.head_row0 * D * IO::ES;
+  const rsrc_t rq = make_rsrc(qb, head_bytes);
+  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + ww.head_row0 * D * IO::ES, head_bytes);
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + ww.head_row0 * D * IO::ES, head_bytes);
+
+  const float sl2 = fabsf(a.scale_log2);
+  uint4 qf[D / 16];
+  bf_load_q<TILE, D, F32IN>(rq, min(ww.qt, L.n_tiles - 1), rg, l32, half,
+                            a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  IO io;
+  auto block_off = [&](int step) -> uint32_t {
+    const int tile = sched_tile<QPW>(sched, ww, step / SUB, L.n_tiles);
+    return (uint32_t)((tile * TILE + (step % SUB) * KVH) * D * IO::ES);
+  };
+  const int steps = len * SUB;
+  if (steps > 0) {
+    io.load(rk, rv, block_off(0), tid);
+    io.store(k_lds[0], v_lds[0], tid);
+    __syncthreads();
+  }
+  for (int s = 0; s < steps; ++s) {
+    const int cur = s & 1;
+    const int entry = s / SUB;
+    const int tile = sched_tile<QPW>(sched, ww, entry, L.n_tiles);
+    const bool mine = sched_mine<QPW>(sched, entry, ww.slot);
+    const bool has_next = s + 1 < steps;
+    if (has_next) io.load(rk, rv, block_off(s + 1), tid);
+    if (mine) {
+      f32x16_t sacc[MB];
+      bf_scores<KVH, D>(k_lds[cur], qf, sacc, l32, half);
+      bool full;
+      const uint32_t bits = kv_valid_bits<MB>(L, tile, (s % SUB) * KVH, lane, half, full);
+      const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazyBf16, m_run, l_run);
+      if (alpha != 1.0f) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
+      }
+      uint4 pk[KVH / 16];
+      bf_pack_p<KVH>(sacc, pk);
+      bf_pv<KVH, D>(v_lds[cur], pk, oacc, l32, half);
+    }
+    if (has_next) io.store(k_lds[cur ^ 1], v_lds[cur ^ 1], tid);
+    __syncthreads();
+  }
+  if (!ww.active) return;
+  bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
+}
+
+// Ping-pong kernel for shared or dense lists with 64-token tiles: four query
+// tiles (eight waves) walk the union of their lists. The two waves on each
+// SIMD run one phase apart; each kv tile t becomes
+//   an MFMA block  [O += P(t-1) V(t-1);  S(t) = K(t) Q^T]   and
+//   a VALU block   [softmax of S(t) -> P(t)],
+// so in every phase (one barrier each) one wave of each SIMD issues MFMAs
+// while the other runs its softmax. Tile t is used from phase 2t (its K) to
+// phase 2t+3 (its V, by the later group), so three LDS buffers rotate: the
+// loads for tile t+3 are issued in phase 2t+4 and stored in phase 2t+5.
+template <int D, bool F32IN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_pp_kernel(DevLayout L, AttnArgs a, int n_work) {
+  constexpr int TILE = 64, QPW = 4, WPQ = 2, MB = 2, THREADS = 512, NB = 3;
+  using IO = BfTile<TILE, D, THREADS, F32IN>;
+
+  __shared__ uint4 k_lds[NB][IO::K_LDS];
+  __shared__ uint4 v_lds[NB][IO::V_LDS];
+  __shared__ int scan[THREADS];
+  extern __shared__ int dyn[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int rg = wave % WPQ;
+  // The two waves that share a SIMD run one phase apart: read each wave's
+  // SIMD from the hardware id register; the first wave on a SIMD is group 0.
+  __shared__ int simd_of[8];
+  if (lane == 0) simd_of[wave] = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;
+  __syncthreads();
+  int rank = 0;
+  for (int w = 0; w < wave; ++w) rank += simd_of[w] == simd_of[wave];
+  const int group = rank & 1;
+
+  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
+  const int* sched = dyn + L.n_tiles;
+  const int len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
+
+  const long long head_bytes = L.n_padded * D * IO::ES;
+  const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + ww.head_row0 * D * IO::ES, head_bytes);
+  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + ww.head_row0 * D * IO::ES, head_bytes);
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + ww.head_row0 * D * IO::ES, head_bytes);
+
+  const float sl2 = fabsf(a.scale_log2);
+  uint4 qf[D / 16];
+  bf_load_q<TILE, D, F32IN>(rq, min(ww.qt, L.n_tiles - 1), rg, l32, half,
+                            a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  IO io;
+  auto tile_off = [&](int t) -> uint32_t {
+    return (uint32_t)(sched_tile<QPW>(sched, ww, t, L.n_tiles) * TILE * D * IO::ES);
+  };
+  // prologue: tiles 0..2 into buffers 0..2
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    if (t < len) {
+      io.load(rk, rv, tile_off(t), tid);
+      io.store(k_lds[t], v_lds[t], tid);
+    }
+  }
+  __syncthreads();
+
+  f32x16_t sacc[MB];
+  uint4 pk[TILE / 16];
+  const int nphase = 2 * len + 2;
+  for (int p = 0; p < nphase; ++p) {
+    // prefetch of tile p/2 + 1 into the buffer tile p/2 - 2 has released
+    if (p >= 4) {
+      const int t = (p >> 1) + 1;
+      if (t < len) {
+        if ((p & 1) == 0) io.load(rk, rv, tile_off(t), tid);
+        else io.store(k_lds[t % NB], v_lds[t % NB], tid);
+      }
+    }
+    const int b = p - group;             // this wave's block
+    if (b >= 0 && b <= 2 * len) {
+      const int t = b >> 1;
+      if ((b & 1) == 0) {
+        // MFMA block: PV of tile t-1, scores of tile t
+        if (t >= 1 && sched_mine<QPW>(sched, t - 1, ww.slot))
+          bf_pv<TILE, D>(v_lds[(t - 1) % NB], pk, oacc, l32, half);
+        if (t < len && sched_mine<QPW>(sched, t, ww.slot))
+          bf_scores<TILE, D>(k_lds[t % NB], qf, sacc, l32, half);
+      } else if (t < len && sched_mine<QPW>(sched, t, ww.slot)) {
+        // VALU block: softmax of tile t
+        const int tile = sched_tile<QPW>(sched, ww, t, L.n_tiles);
+        bool full;
+        const uint32_t bits = kv_valid_bits<MB>(L, tile, 0, lane, half, full);
+        const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazyBf16, m_run, l_run);
+        if (alpha != 1.0f) {
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
+        }
+        bf_pack_p<TILE>(sacc, pk);
+      }
+    }
+    __syncthreads();
+  }
+  if (!ww.active) return;
+  bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
+}
+
 // ---------------------------------------------------------------------------
 // fp8 e4m3 variant (FPSAttention, Approach: FP8 on the same tiles as the
-// sparsity). Q/K/V are e4m3 codes with one fp32 scale per (b, head, tile).
-//   S^T = Kc . Qc^T   v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales),
+// sparsity). Q/K/V are e4m3 codes with one fp32 scale per (b, head, tile);
+// tiles are 64 tokens, d = 128, and one wave owns 32 query rows (two waves
+// per query tile, two waves per SIMD), as in the bf16 kernel.
+//   S^T = Kc . Qc^T   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales,
 //                     times q_scale * k_scale(tile) * sigma * log2(e);
-//   O^T += Vc^T . P8^T with P8 = e4m3(p * 112 * v_scale(tile) / max_t v_scale)
+//   O^T += Vc^T . P8^T with P8 = e4m3(p * 112 * v_scale(tile) / max_t v_scale).
 // The lazy-rescale threshold is 2 (p <= 4), so p * 112 * (<= 1) stays within
 // e4m3's 448. Folding v_scale(tile) / max v_scale into P keeps one O
-// accumulator scale for the whole walk; O = acc * max v_scale / 112 / l.
-// The two half-waves each hold 32 of a tile's 64 kv tokens, so one K=64 MFMA
-// covers the whole tile in the PV product. Tiles are 64 tokens, d = 128; LDS
-// holds two K/V tile buffers in both work shapes.
+// accumulator scale for the whole walk: O = acc * max v_scale / 112 / l.
+// The two half-waves each hold 32 of a tile's 64 kv tokens (element e of a
+// lane in half-wave h is token 32*(e/16) + 8*((e%16)/4) + 4*h + e%4), so one
+// K=64 MFMA covers the whole tile in the PV product. LDS keeps two K/V tile
+// buffers (16 KB each) in both work shapes.
 constexpr float kP8Scale = 112.0f;          // 448 / 2^2
 
 __device__ __forceinline__ int k8_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
@@ -486,11 +628,11 @@ __device__ __forceinline__ i32x8_t cat8(uint4 x, uint4 y) {
   return r;
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int QPW>
+__global__ __launch_bounds__(128 * QPW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
-  constexpr int TILE = 64, D = 128, QG = 2, MB = 2, CB = 4, KS = 2;
-  constexpr int THREADS = 64 * WAVES;
+  constexpr int TILE = 64, D = 128, WPQ = 2, MB = 2, CB = 4, KS = 2;
+  constexpr int THREADS = 64 * QPW * WPQ;
   constexpr int K_PER_T = TILE * D / 16 / THREADS;   // 512 chunks of 16 codes
   constexpr int V_PIECES = (TILE / 4) * (D / 16);    // 4 tokens x 16 channels
   constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
@@ -506,16 +648,18 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  const int rg = wave % WPQ;
 
-  const WaveWork ww = wave_work<WAVES, 1>(L, a, n_work, wave);
+  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
   const int* sched = dyn + L.n_tiles;
   int len;
-  if constexpr (WAVES > 1) len = build_schedule<WAVES, 1>(L, ww, dyn, scan, tid, lane);
+  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
   else len = ww.cnt;
 
-  const uint8_t* Q = static_cast<const uint8_t*>(a.q);
-  const uint8_t* K = static_cast<const uint8_t*>(a.k);
-  const uint8_t* V = static_cast<const uint8_t*>(a.v);
+  const long long head_bytes = L.n_padded * D;
+  const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(a.q) + ww.head_row0 * D, head_bytes);
+  const rsrc_t rk = make_rsrc(static_cast<const uint8_t*>(a.k) + ww.head_row0 * D, head_bytes);
+  const rsrc_t rv = make_rsrc(static_cast<const uint8_t*>(a.v) + ww.head_row0 * D, head_bytes);
   const float* ksc = a.k_scale + (long long)ww.bh * L.n_tiles;
   const float* vsc = a.v_scale + (long long)ww.bh * L.n_tiles;
 
@@ -526,38 +670,35 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   for (int off = 32; off > 0; off >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, off));
   const float inv_wmax = wmax > 0.0f ? 1.0f / wmax : 0.0f;
   const int qt_c = min(ww.qt, L.n_tiles - 1);
-  const float qk_base = a.q_scale[(long long)ww.bh * L.n_tiles + qt_c] * a.scale_log2;
+  // a negative softmax scale is folded into Q (sign bit of every code)
+  const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80808080u : 0u;
+  const float qk_base = a.q_scale[(long long)ww.bh * L.n_tiles + qt_c] * fabsf(a.scale_log2);
 
-  // Q codes as B operands: query row 32*qg + l32, bytes 64*ks + 32*half .. +31
-  i32x8_t qf[QG][KS];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg)
+  // Q codes as B operands: query row 32*rg + l32, bytes 64*ks + 32*half .. +31
+  i32x8_t qf[KS];
+  {
+    const uint32_t row_off = (uint32_t)((qt_c * TILE + 32 * rg + l32) * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4* p = reinterpret_cast<const uint4*>(
-          Q + (ww.head_row0 + (long long)qt_c * TILE + 32 * qg + l32) * D + 64 * ks + 32 * half);
-      qf[qg][ks] = cat8(p[0], p[1]);
+      uint4 x = bload(rq, row_off + 64 * ks + 32 * half, 0);
+      uint4 y = bload(rq, row_off + 64 * ks + 32 * half + 16, 0);
+      x = make_uint4(x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign);
+      y = make_uint4(y.x ^ qsign, y.y ^ qsign, y.z ^ qsign, y.w ^ qsign);
+      qf[ks] = cat8(x, y);
     }
-
-  f32x16_t oacc[CB][QG];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) oacc[cb][qg] = f32x16_t{};
-  float m_run[QG], l_run[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    m_run[qg] = -INFINITY;
-    l_run[qg] = 0.0f;
   }
+
+  f32x16_t oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
 
   uint4 kreg[K_PER_T];
   uint4 vreg[V_PER_T][4];
   auto load_k = [&](int tile) {
-    const uint4* base =
-        reinterpret_cast<const uint4*>(K + (ww.head_row0 + (long long)tile * TILE) * D);
+    const uint32_t tile_off = (uint32_t)(tile * TILE * D);
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) kreg[i] = base[tid + i * THREADS];
+    for (int i = 0; i < K_PER_T; ++i) kreg[i] = bload(rk, tid * 16, tile_off + i * THREADS * 16);
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -569,21 +710,19 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
   // V piece u: tokens tok0 .. tok0+3 (tok0 = 4 * (u / 8)) x channels 16 * (u % 8) ..
   auto load_v = [&](int tile) {
-    const uint4* base =
-        reinterpret_cast<const uint4*>(V + (ww.head_row0 + (long long)tile * TILE) * D);
+    const uint32_t tile_off = (uint32_t)(tile * TILE * D);
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (u < V_PIECES) {
-        const int cg = u & 7, tok0 = 4 * (u >> 3);
+        const uint32_t voff = (uint32_t)(4 * (u >> 3) * D + 16 * (u & 7));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vreg[i][j] = base[(tok0 + j) * 8 + cg];
+        for (int j = 0; j < 4; ++j) vreg[i][j] = bload(rv, voff + j * D, tile_off);
       }
     }
   };
-  // kv token of element e (0..31) of a lane in half-wave h: 32*(e/16) +
-  // 8*((e%16)/4) + 4*h + e%4; tokens tok0..tok0+3 therefore sit at V^T byte
-  // positions p0..p0+3 with p0 = 32*h + 16*(tok0/32) + 4*((tok0/8)%4).
+  // tokens tok0..tok0+3 sit at V^T byte positions p0..p0+3 with
+  // p0 = 32*h + 16*(tok0/32) + 4*((tok0/8)%4), h = (tok0/4)%2
   auto store_v = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
@@ -618,7 +757,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
 
   if (len > 0) {
-    const int t0 = sched_tile<WAVES>(sched, ww, 0, L.n_tiles);
+    const int t0 = sched_tile<QPW>(sched, ww, 0, L.n_tiles);
     load_k(t0);
     load_v(t0);
     store_k(0);
@@ -628,20 +767,18 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 
   for (int s = 0; s < len; ++s) {
     const int cur = s & 1;
-    const int tile = sched_tile<WAVES>(sched, ww, s, L.n_tiles);
-    const bool mine = sched_mine<WAVES>(sched, s, ww.slot);
+    const int tile = sched_tile<QPW>(sched, ww, s, L.n_tiles);
+    const bool mine = sched_mine<QPW>(sched, s, ww.slot);
     const bool has_next = s + 1 < len;
     if (has_next) {
-      const int next = sched_tile<WAVES>(sched, ww, s + 1, L.n_tiles);
+      const int next = sched_tile<QPW>(sched, ww, s + 1, L.n_tiles);
       load_k(next);
       load_v(next);
     }
     if (mine) {
-      f32x16_t sacc[QG][MB];
+      f32x16_t sacc[MB];
 #pragma unroll
-      for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) sacc[qg][mb] = f32x16_t{};
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -650,32 +787,27 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
           const int sw = k8_swizzle(r);
           const i32x8_t av = cat8(k_lds[cur][r * 8 + ((4 * ks + 2 * half) ^ sw)],
                                   k_lds[cur][r * 8 + ((4 * ks + 2 * half + 1) ^ sw)]);
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg)
-            sacc[qg][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, qf[qg][ks], sacc[qg][mb], 0, 0, 0, 127, 0, 127);
+          sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[ks], sacc[mb], 0, 0,
+                                                                     0, 127, 0, 127);
         }
       bool full;
-      const uint32_t bits = kv_valid_bits<MB>(L, tile, lane, half, full);
+      const uint32_t bits = kv_valid_bits<MB>(L, tile, 0, lane, half, full);
       const float cs = qk_base * ksc[tile];
       const float pscale = kP8Scale * vsc[tile] * inv_wmax;
-      i32x8_t pk[QG];
+      const float alpha = softmax_step<MB>(sacc, full, bits, cs, kLazy, m_run, l_run);
+      if (alpha != 1.0f) {
 #pragma unroll
-      for (int qg = 0; qg < QG; ++qg) {
-        const float alpha = softmax_step<MB>(sacc[qg], full, bits, cs, kLazy, m_run[qg], l_run[qg]);
-        if (alpha != 1.0f) {
+        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+      }
+      i32x8_t pk;
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[cb][qg] *= alpha;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int mb = i >> 2, r0 = 4 * (i & 3);
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[qg][mb][r0] * pscale,
-                                                   sacc[qg][mb][r0 + 1] * pscale, 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[qg][mb][r0 + 2] * pscale,
-                                               sacc[qg][mb][r0 + 3] * pscale, wv, true);
-          pk[qg][i] = wv;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int mb = i >> 2, r0 = 4 * (i & 3);
+        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[mb][r0] * pscale, sacc[mb][r0 + 1] * pscale,
+                                                 0, false);
+        wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[mb][r0 + 2] * pscale,
+                                             sacc[mb][r0 + 3] * pscale, wv, true);
+        pk[i] = wv;
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
@@ -683,10 +815,8 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
         const int sw = v8_swizzle(c);
         const i32x8_t av = cat8(v_lds[cur][c * 4 + ((2 * half) ^ sw)],
                                 v_lds[cur][c * 4 + ((2 * half + 1) ^ sw)]);
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg)
-          oacc[cb][qg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              av, pk[qg], oacc[cb][qg], 0, 0, 0, 127, 0, 127);
+        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pk, oacc[cb], 0, 0, 0, 127,
+                                                                   0, 127);
       }
     }
     if (has_next) {
@@ -698,51 +828,58 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 
   if (!ww.active) return;
   const TileValid tq = tile_valid(L, ww.qt);
+  const int qrow = 32 * rg + l32;
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const bool real = row_is_real(L, tq, qrow);
+  const float inv = (real && lt > 0.0f) ? wmax / (kP8Scale * lt) : 0.0f;
+  const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    const int qrow = 32 * qg + l32;
-    const float lt = l_run[qg] + __shfl_xor(l_run[qg], 32);
-    const bool real = row_is_real(L, tq, qrow);
-    const float inv = (real && lt > 0.0f) ? wmax / (kP8Scale * lt) : 0.0f;
-    const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = 32 * cb + 8 * g + 4 * half;
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
-            make_uint2(pack2(oacc[cb][qg][4 * g] * inv, oacc[cb][qg][4 * g + 1] * inv),
-                       pack2(oacc[cb][qg][4 * g + 2] * inv, oacc[cb][qg][4 * g + 3] * inv));
-      }
-    if (a.lse && half == 0) {
-      a.lse[orow] = (real && lt > 0.0f) ? (m_run[qg] + __log2f(lt)) * 0.69314718055994531f
-                                        : -INFINITY;
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * cb + 8 * g + 4 * half;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
+          make_uint2(pack2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv),
+                     pack2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv));
     }
+  if (a.lse && half == 0) {
+    a.lse[orow] = (real && lt > 0.0f) ? (m_run + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int TILE, int D, int QPW, bool F32IN>
+template <int TILE, int KVH, int D, int QPW, bool F32IN>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_bf16_kernel<TILE, D, QPW, F32IN>), dim3(n_work),
+  hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN>), dim3(n_work),
                      dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
-template <int WAVES>
+template <int D, bool F32IN>
+hipError_t launch_bf16_pp(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
+  const int n_work = L.B * L.heads * ((L.n_tiles + 3) / 4);
+  const size_t dyn = (size_t)2 * L.n_tiles * sizeof(int);
+  hipLaunchKernelGGL((attn_bf16_pp_kernel<D, F32IN>), dim3(n_work), dim3(512), dyn, s, L, a, n_work);
+  return hipGetLastError();
+}
+
+template <int QPW>
 hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
-  const int n_work = L.B * L.heads * ((L.n_tiles + WAVES - 1) / WAVES);
-  const size_t dyn = WAVES > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_fp8_kernel<WAVES>), dim3(n_work), dim3(64 * WAVES), dyn, s, L, a,
-                     n_work);
+  const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
+  const size_t dyn = QPW > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
+  hipLaunchKernelGGL((attn_fp8_kernel<QPW>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
 template <int TILE, int D, bool F32IN>
 hipError_t launch_bf16_shape(const DevLayout& L, const AttnArgs& a, bool grouped, hipStream_t s) {
-  return grouped ? launch_bf16<TILE, D, 4, F32IN>(L, a, s) : launch_bf16<TILE, D, 1, F32IN>(L, a, s);
+  if constexpr (TILE == 64) {
+    return grouped ? launch_bf16_pp<D, F32IN>(L, a, s) : launch_bf16<64, 32, D, 1, F32IN>(L, a, s);
+  } else {
+    return grouped ? launch_bf16<32, 32, D, 4, F32IN>(L, a, s) : launch_bf16<32, 32, D, 1, F32IN>(L, a, s);
+  }
 }
 
 }  // namespace
