@@ -52,6 +52,19 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {   // hi16(
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Scheduling hint for a block of N LDS operand reads feeding N MFMAs: keep
+// PRE reads in flight ahead of the MFMA that consumes them, then alternate.
+template <int N, int PRE>
+__device__ __forceinline__ void reads_ahead_of_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);          // DS reads
+#pragma unroll
+  for (int i = 0; i < N - PRE; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+}
+
 // Buffer-resource loads: the base of one (b, head) slice of a tensor sits in
 // SGPRs and each load takes a 32-bit byte offset (VGPR part + SGPR part), so
 // tile loads need no 64-bit address registers; offsets past num_records read
@@ -156,14 +169,16 @@ __device__ int build_schedule(const DevLayout& L, const WaveWork& w, int* dyn, i
   return len;
 }
 
+// Schedule entries are the same for every lane of a wave: readfirstlane
+// moves them to scalar registers so the branches on them are scalar.
 template <int QPW>
 __device__ __forceinline__ int sched_tile(const int* sched, const WaveWork& w, int s, int n_tiles) {
-  if constexpr (QPW > 1) return sched[s] & 0xFFFFFF;
-  else return w.list ? min(max(w.list[s], 0), n_tiles - 1) : s;
+  if constexpr (QPW > 1) return __builtin_amdgcn_readfirstlane(sched[s]) & 0xFFFFFF;
+  else return w.list ? min(max(__builtin_amdgcn_readfirstlane(w.list[s]), 0), n_tiles - 1) : s;
 }
 template <int QPW>
 __device__ __forceinline__ bool sched_mine(const int* sched, int s, int slot) {
-  if constexpr (QPW > 1) return (sched[s] >> (24 + slot)) & 1;
+  if constexpr (QPW > 1) return (__builtin_amdgcn_readfirstlane(sched[s]) >> (24 + slot)) & 1;
   else return true;
 }
 
@@ -192,23 +207,20 @@ __device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, 
 // Online-softmax step on one 32-row query group: scores s (raw dot products,
 // MB blocks of 16 per lane) become p = exp2(s * sl2 - m_run), in place.
 // sl2 >= 0 (a negative softmax scale is folded into Q by the caller).
-// Returns the factor O must be multiplied by (1 when m_run did not move).
-template <int MB>
-__device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint32_t bits,
-                                              float sl2, float lazy, float& m_run, float& l_run) {
+// MASKED: bit (16*mb + r) of `bits` says whether that key is real; masked
+// keys get p = 0. Returns the factor O must be multiplied by (1 when m_run
+// did not move).
+template <int MB, bool MASKED>
+__device__ __forceinline__ float softmax_core(f32x16_t (&s)[MB], uint32_t bits, float sl2,
+                                              float lazy, float& m_run, float& l_run) {
   float hi = -INFINITY;
-  if (full) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hi = fmaxf(hi, s[mb][r]);
-  } else {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        hi = fmaxf(hi, ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY);
-  }
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (MASKED) hi = fmaxf(hi, ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY);
+      else hi = fmaxf(hi, s[mb][r]);
+    }
   hi = fmaxf(hi, __shfl_xor(hi, 32));
   const float mx = hi * sl2;                             // max over the tile of s * sl2
   float alpha = 1.0f;
@@ -224,7 +236,7 @@ __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(fmaf(s[mb][r], sl2, nm));
-      if (!full) p = ((bits >> (16 * mb + r)) & 1u) ? p : 0.0f;
+      if constexpr (MASKED) p = ((bits >> (16 * mb + r)) & 1u) ? p : 0.0f;
       s[mb][r] = p;
       psum += p;
     }
@@ -232,7 +244,12 @@ __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint
   return alpha;
 }
 
-__device__ __forceinline__ int vt_swizzle(int c, int cpr) { return (c ^ (c >> 3)) & (cpr - 1); }
+template <int MB>
+__device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint32_t bits,
+                                              float sl2, float lazy, float& m_run, float& l_run) {
+  if (full) return softmax_core<MB, false>(s, bits, sl2, lazy, m_run, l_run);
+  return softmax_core<MB, true>(s, bits, sl2, lazy, m_run, l_run);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 kernels. One wave owns 32 query rows (a 64-row query tile takes two
@@ -240,21 +257,27 @@ __device__ __forceinline__ int vt_swizzle(int c, int cpr) { return (c ^ (c >> 3)
 // wave's softmax can run while the other's MFMAs do.
 
 // Register staging of one kv block (KVH tokens x D channels) and its store
-// into LDS: K row-major with 16-byte chunks XOR-swizzled by row; V
-// transposed to V^T rows (one per channel) in the token order of the S^T
-// accumulator (register r of block mb in half-wave h holds token
-// 32*mb + 8*(r/4) + 4*h + r%4), built from 4-token x 8-channel pieces.
+// into LDS: K row-major, V transposed to V^T rows (one per channel) in the
+// token order of the S^T accumulator (register r of block mb in half-wave h
+// holds token 32*mb + 8*(r/4) + 4*h + r%4), built from 4-token x 8-channel
+// pieces. Every LDS row is padded by 16 bytes: the 16 rows a half-wave
+// reads at one column then start 16 bytes apart, which spreads them over
+// all banks, and each fragment address is one base register plus an
+// immediate offset.
 template <int KVH, int D, int THREADS, bool F32IN>
 struct BfTile {
   static constexpr int ES = F32IN ? 4 : 2;
   static constexpr int CPR_K = D / 8;               // 16-byte chunks per K row
   static constexpr int CPR_V = KVH / 8;             // 16-byte chunks per V^T row
+  static constexpr int KS_ = CPR_K + 1;             // padded row strides, in uint4
+  static constexpr int VS_ = CPR_V + 1;
   static constexpr int K_CHUNKS = KVH * CPR_K;
   static constexpr int K_PER_T = (K_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int V_PIECES = (KVH / 4) * (D / 8);
+  static constexpr int QUARTERS = KVH / 4;
+  static constexpr int V_PIECES = QUARTERS * (D / 8);
   static constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
-  static constexpr int K_LDS = KVH * CPR_K;         // uint4 per K buffer
-  static constexpr int V_LDS = D * CPR_V;           // uint4 per V^T buffer
+  static constexpr int K_LDS = KVH * KS_;           // uint4 per K buffer
+  static constexpr int V_LDS = D * VS_;             // uint4 per V^T buffer
   uint4 kreg[K_PER_T];
   uint4 vreg[V_PER_T][4];
 
@@ -270,7 +293,7 @@ struct BfTile {
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (V_PIECES % THREADS == 0 || u < V_PIECES) {
-        const int cc = u % (D / 8), q4 = u / (D / 8);
+        const int q4 = u % QUARTERS, cc = u / QUARTERS;
         const int pc = q4 >> 1;
         const int tok0 = 16 * (pc >> 1) + 4 * (pc & 1) + 8 * (q4 & 1);
         const uint32_t voff = (uint32_t)((tok0 * D + cc * 8) * ES);
@@ -283,20 +306,17 @@ struct BfTile {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int c = tid + i * THREADS;
-      if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS) {
-        const int r = c / CPR_K, ch = c % CPR_K;
-        k_lds[r * CPR_K + (ch ^ (r % CPR_K))] = kreg[i];
-      }
+      if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS) k_lds[(c / CPR_K) * KS_ + c % CPR_K] = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (V_PIECES % THREADS == 0 || u < V_PIECES) {
-        const int cc = u % (D / 8), q4 = u / (D / 8);
-        const int pc = q4 >> 1;
+        const int q4 = u % QUARTERS, cc = u / QUARTERS;
+        // positions 4*q4 .. 4*q4+3 of channel rows cc*8 .. cc*8+7
+        uint2* dst = reinterpret_cast<uint2*>(v_lds + (cc * 8) * VS_) + q4;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int c = cc * 8 + e;
           const int dw = e >> 1;
           uint2 o;
           if (e & 1) {
@@ -306,31 +326,35 @@ struct BfTile {
             o.x = perm_lo(vreg[i][0][dw], vreg[i][1][dw]);
             o.y = perm_lo(vreg[i][2][dw], vreg[i][3][dw]);
           }
-          uint2* dst = reinterpret_cast<uint2*>(&v_lds[c * CPR_V + (pc ^ vt_swizzle(c, CPR_V))]);
-          dst[q4 & 1] = o;
+          dst[e * VS_ * 2] = o;
         }
       }
     }
   }
 };
 
-// S^T (KVH kv tokens x 32 query rows) = K . Q^T from one K buffer
+// S^T (KVH kv tokens x 32 query rows) = K . Q^T from one K buffer. All K
+// fragments are read before the MFMAs so their LDS latency overlaps.
 template <int KVH, int D>
 __device__ __forceinline__ void bf_scores(const uint4* k_lds, const uint4 (&qf)[D / 16],
                                           f32x16_t (&sacc)[KVH / 32], int l32, int half) {
-  constexpr int CPR_K = D / 8;
+  constexpr int KS_ = D / 8 + 1;
+  const uint4* base = k_lds + l32 * KS_ + half;
+  uint4 kf[D / 16][KVH / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < KVH / 32; ++mb) kf[ks][mb] = base[mb * 32 * KS_ + 2 * ks];
 #pragma unroll
   for (int mb = 0; mb < KVH / 32; ++mb) sacc[mb] = f32x16_t{};
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-    for (int mb = 0; mb < KVH / 32; ++mb) {
-      const int r = 32 * mb + l32;
-      const uint4 av = k_lds[r * CPR_K + ((2 * ks + half) ^ (r % CPR_K))];
-      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+    for (int mb = 0; mb < KVH / 32; ++mb)
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks][mb]),
                                                          __builtin_bit_cast(bf16x8_t, qf[ks]),
                                                          sacc[mb], 0, 0, 0);
-    }
+  reads_ahead_of_mfma<(D / 16) * (KVH / 32), 5>();
 }
 
 // P^T (bf16, B operands of the PV product) from the probabilities in sacc
@@ -344,21 +368,25 @@ __device__ __forceinline__ void bf_pack_p(const f32x16_t (&p)[KVH / 32], uint4 (
   }
 }
 
-// O^T += V^T . P^T from one V^T buffer
+// O^T += V^T . P^T from one V^T buffer (fragments read ahead of the MFMAs)
 template <int KVH, int D>
 __device__ __forceinline__ void bf_pv(const uint4* v_lds, const uint4 (&pk)[KVH / 16],
                                       f32x16_t (&oacc)[D / 32], int l32, int half) {
-  constexpr int CPR_V = KVH / 8;
+  constexpr int VS_ = KVH / 8 + 1;
+  const uint4* base = v_lds + l32 * VS_ + half;
+  uint4 vf[KVH / 16][D / 32];
 #pragma unroll
   for (int ps = 0; ps < KVH / 16; ++ps)
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
-      const int c = 32 * cb + l32;
-      const uint4 av = v_lds[c * CPR_V + ((2 * ps + half) ^ vt_swizzle(c, CPR_V))];
-      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+    for (int cb = 0; cb < D / 32; ++cb) vf[ps][cb] = base[cb * 32 * VS_ + 2 * ps];
+#pragma unroll
+  for (int ps = 0; ps < KVH / 16; ++ps)
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[ps][cb]),
                                                          __builtin_bit_cast(bf16x8_t, pk[ps]),
                                                          oacc[cb], 0, 0, 0);
-    }
+  reads_ahead_of_mfma<(KVH / 16) * (D / 32), 5>();
 }
 
 // Q^T fragments for query row 32*rg + l32 of tile qt; a negative softmax
@@ -428,7 +456,7 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   extern __shared__ int dyn[];           // QPW > 1: marks + schedule
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -494,113 +522,6 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
 }
 
-// Ping-pong kernel for shared or dense lists with 64-token tiles: four query
-// tiles (eight waves) walk the union of their lists. The two waves on each
-// SIMD run one phase apart; each kv tile t becomes
-//   an MFMA block  [O += P(t-1) V(t-1);  S(t) = K(t) Q^T]   and
-//   a VALU block   [softmax of S(t) -> P(t)],
-// so in every phase (one barrier each) one wave of each SIMD issues MFMAs
-// while the other runs its softmax. Tile t is used from phase 2t (its K) to
-// phase 2t+3 (its V, by the later group), so three LDS buffers rotate: the
-// loads for tile t+3 are issued in phase 2t+4 and stored in phase 2t+5.
-template <int D, bool F32IN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bf16_pp_kernel(DevLayout L, AttnArgs a, int n_work) {
-  constexpr int TILE = 64, QPW = 4, WPQ = 2, MB = 2, THREADS = 512, NB = 3;
-  using IO = BfTile<TILE, D, THREADS, F32IN>;
-
-  __shared__ uint4 k_lds[NB][IO::K_LDS];
-  __shared__ uint4 v_lds[NB][IO::V_LDS];
-  __shared__ int scan[THREADS];
-  extern __shared__ int dyn[];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const int rg = wave % WPQ;
-  // The two waves that share a SIMD run one phase apart: read each wave's
-  // SIMD from the hardware id register; the first wave on a SIMD is group 0.
-  __shared__ int simd_of[8];
-  if (lane == 0) simd_of[wave] = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;
-  __syncthreads();
-  int rank = 0;
-  for (int w = 0; w < wave; ++w) rank += simd_of[w] == simd_of[wave];
-  const int group = rank & 1;
-
-  const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
-  const int* sched = dyn + L.n_tiles;
-  const int len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
-
-  const long long head_bytes = L.n_padded * D * IO::ES;
-  const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + ww.head_row0 * D * IO::ES, head_bytes);
-  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + ww.head_row0 * D * IO::ES, head_bytes);
-  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + ww.head_row0 * D * IO::ES, head_bytes);
-
-  const float sl2 = fabsf(a.scale_log2);
-  uint4 qf[D / 16];
-  bf_load_q<TILE, D, F32IN>(rq, min(ww.qt, L.n_tiles - 1), rg, l32, half,
-                            a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  IO io;
-  auto tile_off = [&](int t) -> uint32_t {
-    return (uint32_t)(sched_tile<QPW>(sched, ww, t, L.n_tiles) * TILE * D * IO::ES);
-  };
-  // prologue: tiles 0..2 into buffers 0..2
-#pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    if (t < len) {
-      io.load(rk, rv, tile_off(t), tid);
-      io.store(k_lds[t], v_lds[t], tid);
-    }
-  }
-  __syncthreads();
-
-  f32x16_t sacc[MB];
-  uint4 pk[TILE / 16];
-  const int nphase = 2 * len + 2;
-  for (int p = 0; p < nphase; ++p) {
-    // prefetch of tile p/2 + 1 into the buffer tile p/2 - 2 has released
-    if (p >= 4) {
-      const int t = (p >> 1) + 1;
-      if (t < len) {
-        if ((p & 1) == 0) io.load(rk, rv, tile_off(t), tid);
-        else io.store(k_lds[t % NB], v_lds[t % NB], tid);
-      }
-    }
-    const int b = p - group;             // this wave's block
-    if (b >= 0 && b <= 2 * len) {
-      const int t = b >> 1;
-      if ((b & 1) == 0) {
-        // MFMA block: PV of tile t-1, scores of tile t
-        if (t >= 1 && sched_mine<QPW>(sched, t - 1, ww.slot))
-          bf_pv<TILE, D>(v_lds[(t - 1) % NB], pk, oacc, l32, half);
-        if (t < len && sched_mine<QPW>(sched, t, ww.slot))
-          bf_scores<TILE, D>(k_lds[t % NB], qf, sacc, l32, half);
-      } else if (t < len && sched_mine<QPW>(sched, t, ww.slot)) {
-        // VALU block: softmax of tile t
-        const int tile = sched_tile<QPW>(sched, ww, t, L.n_tiles);
-        bool full;
-        const uint32_t bits = kv_valid_bits<MB>(L, tile, 0, lane, half, full);
-        const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazyBf16, m_run, l_run);
-        if (alpha != 1.0f) {
-#pragma unroll
-          for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
-        }
-        bf_pack_p<TILE>(sacc, pk);
-      }
-    }
-    __syncthreads();
-  }
-  if (!ww.active) return;
-  bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
-}
-
 // ---------------------------------------------------------------------------
 // fp8 e4m3 variant (FPSAttention, Approach: FP8 on the same tiles as the
 // sparsity). Q/K/V are e4m3 codes with one fp32 scale per (b, head, tile);
@@ -615,11 +536,11 @@ void attn_bf16_pp_kernel(DevLayout L, AttnArgs a, int n_work) {
 // The two half-waves each hold 32 of a tile's 64 kv tokens (element e of a
 // lane in half-wave h is token 32*(e/16) + 8*((e%16)/4) + 4*h + e%4), so one
 // K=64 MFMA covers the whole tile in the PV product. LDS keeps two K/V tile
-// buffers (16 KB each) in both work shapes.
+// buffers in both work shapes, rows padded by 16 bytes as in the bf16 kernel.
 constexpr float kP8Scale = 112.0f;          // 448 / 2^2
 
-__device__ __forceinline__ int k8_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int v8_swizzle(int c) { return ((c >> 1) ^ (c >> 3)) & 3; }
+constexpr int kK8Stride = 9;                // K rows: 8 chunks of 16 codes + 16 B pad
+constexpr int kV8Stride = 5;                // V^T rows: 4 chunks + 16 B pad
 
 __device__ __forceinline__ i32x8_t cat8(uint4 x, uint4 y) {
   i32x8_t r;
@@ -638,13 +559,13 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
   constexpr float kLazy = 2.0f;
 
-  __shared__ uint4 k_lds[2][TILE * 8];               // 64 rows x 128 B
-  __shared__ uint4 v_lds[2][D * 4];                  // V^T: 128 rows x 64 B
+  __shared__ uint4 k_lds[2][TILE * kK8Stride];       // 64 rows x (128 + 16) B
+  __shared__ uint4 v_lds[2][D * kV8Stride];          // V^T: 128 rows x (64 + 16) B
   __shared__ int scan[THREADS];
   extern __shared__ int dyn[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -704,18 +625,17 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int c = tid + i * THREADS;
-      const int r = c >> 3, ch = c & 7;
-      k_lds[buf][r * 8 + (ch ^ k8_swizzle(r))] = kreg[i];
+      k_lds[buf][(c >> 3) * kK8Stride + (c & 7)] = kreg[i];
     }
   };
-  // V piece u: tokens tok0 .. tok0+3 (tok0 = 4 * (u / 8)) x channels 16 * (u % 8) ..
+  // V piece u: tokens tok0 .. tok0+3 (tok0 = 4 * (u % 16)) x channels 16 * (u / 16) ..
   auto load_v = [&](int tile) {
     const uint32_t tile_off = (uint32_t)(tile * TILE * D);
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (u < V_PIECES) {
-        const uint32_t voff = (uint32_t)(4 * (u >> 3) * D + 16 * (u & 7));
+        const uint32_t voff = (uint32_t)(4 * (u & 15) * D + 16 * (u >> 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j) vreg[i][j] = bload(rv, voff + j * D, tile_off);
       }
@@ -728,7 +648,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (u < V_PIECES) {
-        const int cg = u & 7, tok0 = 4 * (u >> 3);
+        const int cg = u >> 4, tok0 = 4 * (u & 15);
         const int hh = (tok0 >> 2) & 1, A = tok0 >> 5, B = (tok0 >> 3) & 3;
         const int p0 = 32 * hh + 16 * A + 4 * B;
         const uint32_t in[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
@@ -748,8 +668,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             const int c = 16 * cg + 4 * dw + bb;
-            uint32_t* row = reinterpret_cast<uint32_t*>(&v_lds[buf][c * 4]);
-            row[((p0 >> 4) ^ v8_swizzle(c)) * 4 + ((p0 & 15) >> 2)] = o[bb];
+            reinterpret_cast<uint32_t*>(&v_lds[buf][c * kV8Stride])[p0 >> 2] = o[bb];
           }
         }
       }
@@ -777,19 +696,21 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     }
     if (mine) {
       f32x16_t sacc[MB];
+      i32x8_t kf[KS][MB];
+      const uint4* kb = k_lds[cur] + l32 * kK8Stride + 2 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          kf[ks][mb] = cat8(kb[mb * 32 * kK8Stride + 4 * ks], kb[mb * 32 * kK8Stride + 4 * ks + 1]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = 32 * mb + l32;
-          const int sw = k8_swizzle(r);
-          const i32x8_t av = cat8(k_lds[cur][r * 8 + ((4 * ks + 2 * half) ^ sw)],
-                                  k_lds[cur][r * 8 + ((4 * ks + 2 * half + 1) ^ sw)]);
-          sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[ks], sacc[mb], 0, 0,
-                                                                     0, 127, 0, 127);
-        }
+        for (int mb = 0; mb < MB; ++mb)
+          sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[ks][mb], qf[ks], sacc[mb], 0,
+                                                                     0, 0, 127, 0, 127);
       bool full;
       const uint32_t bits = kv_valid_bits<MB>(L, tile, 0, lane, half, full);
       const float cs = qk_base * ksc[tile];
@@ -809,15 +730,15 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
                                              sacc[mb][r0 + 3] * pscale, wv, true);
         pk[i] = wv;
       }
+      i32x8_t vf[CB];
+      const uint4* vb = v_lds[cur] + l32 * kV8Stride + 2 * half;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = 32 * cb + l32;
-        const int sw = v8_swizzle(c);
-        const i32x8_t av = cat8(v_lds[cur][c * 4 + ((2 * half) ^ sw)],
-                                v_lds[cur][c * 4 + ((2 * half + 1) ^ sw)]);
-        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pk, oacc[cb], 0, 0, 0, 127,
-                                                                   0, 127);
-      }
+      for (int cb = 0; cb < CB; ++cb)
+        vf[cb] = cat8(vb[cb * 32 * kV8Stride], vb[cb * 32 * kV8Stride + 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[cb], pk, oacc[cb], 0, 0, 0,
+                                                                   127, 0, 127);
     }
     if (has_next) {
       store_k(cur ^ 1);
@@ -857,14 +778,6 @@ hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool F32IN>
-hipError_t launch_bf16_pp(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
-  const int n_work = L.B * L.heads * ((L.n_tiles + 3) / 4);
-  const size_t dyn = (size_t)2 * L.n_tiles * sizeof(int);
-  hipLaunchKernelGGL((attn_bf16_pp_kernel<D, F32IN>), dim3(n_work), dim3(512), dyn, s, L, a, n_work);
-  return hipGetLastError();
-}
-
 template <int QPW>
 hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
@@ -876,7 +789,7 @@ hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
 template <int TILE, int D, bool F32IN>
 hipError_t launch_bf16_shape(const DevLayout& L, const AttnArgs& a, bool grouped, hipStream_t s) {
   if constexpr (TILE == 64) {
-    return grouped ? launch_bf16_pp<D, F32IN>(L, a, s) : launch_bf16<64, 32, D, 1, F32IN>(L, a, s);
+    return grouped ? launch_bf16<64, 64, D, 4, F32IN>(L, a, s) : launch_bf16<64, 32, D, 1, F32IN>(L, a, s);
   } else {
     return grouped ? launch_bf16<32, 32, D, 4, F32IN>(L, a, s) : launch_bf16<32, 32, D, 1, F32IN>(L, a, s);
   }
