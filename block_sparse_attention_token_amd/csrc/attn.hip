@@ -27,6 +27,8 @@
 // rescaled. Pad keys are masked from one ballot per padded tile.
 #include <float.h>
 
+#include <type_traits>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -133,26 +135,30 @@ __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs
 
 // QPW > 1: write the ascending union of the query tiles' lists into sched[],
 // each entry = tile | (mask of query-tile slots listing it) << 24; returns
-// its length.
+// its length. `shared` is set when every entry lists every active slot (the
+// query tiles share one list), so every wave owns every step of the walk.
+// `marks` (one byte per tile) and `scan` (one int per thread) are scratch
+// that the caller may alias onto LDS it only uses afterwards.
 template <int QPW, int WPQ>
-__device__ int build_schedule(const DevLayout& L, const WaveWork& w, int* dyn, int* scan,
-                              int tid, int lane) {
+__device__ int build_schedule(const DevLayout& L, const WaveWork& w, uint32_t* marks, int* scan,
+                              int* sched, int tid, int lane, bool& shared) {
+  static_assert(QPW <= 8, "slot masks are one byte");
   constexpr int THREADS = 64 * QPW * WPQ;
-  int* marks = dyn;
-  int* sched = dyn + L.n_tiles;
-  for (int t = tid; t < L.n_tiles; t += THREADS) marks[t] = 0;
+  const int words = (L.n_tiles + 3) >> 2;
+  for (int t = tid; t < words; t += THREADS) marks[t] = 0;
   __syncthreads();
   if ((tid >> 6) % WPQ == 0) {
     for (int i = lane; i < w.cnt; i += 64) {
       const int t = w.list ? min(max(w.list[i], 0), L.n_tiles - 1) : i;
-      atomicOr(&marks[t], 1 << w.slot);
+      atomicOr(&marks[t >> 2], 1u << (8 * (t & 3) + w.slot));
     }
   }
   __syncthreads();
+  auto mark = [&](int t) -> int { return (marks[t >> 2] >> (8 * (t & 3))) & 0xFF; };
   const int per = (L.n_tiles + THREADS - 1) / THREADS;
   const int lo = tid * per, hi = min(lo + per, L.n_tiles);
   int mine = 0;
-  for (int t = lo; t < hi; ++t) mine += marks[t] != 0;
+  for (int t = lo; t < hi; ++t) mine += mark(t) != 0;
   scan[tid] = mine;
   __syncthreads();
   for (int off = 1; off < THREADS; off <<= 1) {
@@ -163,9 +169,15 @@ __device__ int build_schedule(const DevLayout& L, const WaveWork& w, int* dyn, i
   }
   int pos = scan[tid] - mine;
   const int len = scan[THREADS - 1];
-  for (int t = lo; t < hi; ++t)
-    if (marks[t]) sched[pos++] = t | (marks[t] << 24);
-  __syncthreads();
+  const int qt0 = w.qt - w.slot;
+  const int active = (1 << min(max(L.n_tiles - qt0, 0), QPW)) - 1;
+  bool same = true;
+  for (int t = lo; t < hi; ++t) {
+    const int m = mark(t);
+    if (m) sched[pos++] = t | (m << 24);
+    same = same && (m == 0 || m == active);
+  }
+  shared = __syncthreads_and(same) != 0;
   return len;
 }
 
@@ -203,6 +215,70 @@ __device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, 
       m |= (uint32_t)((vm >> (32 * mb + 8 * g + 4 * half)) & 0xFull) << (16 * mb + 4 * g);
   return m;
 }
+
+// Bit (16*mb + r) set iff the kv token this lane holds in register r of S^T
+// block mb (token tok0 + 32*mb + 8*(r/4) + 4*half + r%4 of the tile) is a
+// real token, for a block known to hold padding.
+template <int MB>
+__device__ __forceinline__ uint32_t kv_pad_bits(const DevLayout& L, int tile, int tok0, int lane,
+                                                int half) {
+  const TileValid tv = tile_valid(L, tile);
+  const bool v = lane < 32 * MB && row_is_real(L, tv, tok0 + lane);
+  const unsigned long long vm = __ballot(v);
+  uint32_t m = 0;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      m |= (uint32_t)((vm >> (32 * mb + 8 * g + 4 * half)) & 0xFull) << (16 * mb + 4 * g);
+  return m;
+}
+
+// A window of 64 schedule entries held in two registers: lane i holds entry
+// base + i, its key tile and flags (bit j: kv block j of the tile holds
+// padding; bits 8..15: the query-tile slots that list it). Each step reads
+// its entry with v_readlane instead of a memory round trip; the window is
+// refilled once per 64 entries.
+template <int QPW, int SUB, int KVH>
+struct SchedWindow {
+  int base = 0, tile_v = 0, flags_v = 0;
+
+  __device__ __forceinline__ void fill(const DevLayout& L, const WaveWork& w, const int* sched,
+                                       int len, int b, int lane) {
+    base = b;
+    const int e = b + lane;
+    int tile = 0, flags = 0;
+    if (e < len) {
+      if constexpr (QPW > 1) {
+        const int ent = sched[e];
+        tile = ent & 0xFFFFFF;
+        flags = (ent >> 24) << 8;
+      } else {
+        tile = w.list ? min(max(w.list[e], 0), L.n_tiles - 1) : e;
+        flags = 1 << 8;
+      }
+      const TileValid tv = tile_valid(L, tile);
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        const bool full = tv.full || (L.kind == 1 && (j + 1) * KVH <= tv.vlen);  // Skiparse: pads at the tail
+        flags |= full ? 0 : 1 << j;
+      }
+    }
+    tile_v = tile;
+    flags_v = flags;
+  }
+  // entries lo .. hi must lie in the window (hi - lo < 64)
+  __device__ __forceinline__ void cover(const DevLayout& L, const WaveWork& w, const int* sched,
+                                        int len, int lo, int hi, int lane) {
+    if (hi - base >= 64) fill(L, w, sched, len, lo, lane);
+  }
+  __device__ __forceinline__ int tile(int e) const {
+    return __builtin_amdgcn_readlane(tile_v, e - base);
+  }
+  __device__ __forceinline__ int flags(int e) const {
+    return __builtin_amdgcn_readlane(flags_v, e - base);
+  }
+};
 
 // Online-softmax step on one 32-row query group: scores s (raw dot products,
 // MB blocks of 16 per lane) become p = exp2(s * sl2 - m_run), in place.
@@ -253,17 +329,27 @@ __device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint
 
 // ---------------------------------------------------------------------------
 // bf16 kernels. One wave owns 32 query rows (a 64-row query tile takes two
-// waves) and about 200 registers, so two waves share each SIMD and one
-// wave's softmax can run while the other's MFMAs do.
+// waves) and at most 256 registers, so two waves share each SIMD.
+//
+// The walk over kv blocks is software-pipelined inside each wave, because
+// gfx950 only overlaps MFMA and VALU work that is interleaved in the
+// instruction stream. Step s runs two scheduling regions:
+//   A: the 16 score MFMAs of block s+1, interleaved with the row maximum,
+//      the running-max update and the first half of exp2/pack of block s;
+//   B: the PV MFMAs of block s, interleaved with the second half of its
+//      exp2/pack (each 16-key group of P feeds its MFMAs as soon as it is
+//      packed).
+// K blocks are staged two steps ahead and V blocks one step ahead, each
+// double-buffered in LDS, with one barrier per step.
 
-// Register staging of one kv block (KVH tokens x D channels) and its store
-// into LDS: K row-major, V transposed to V^T rows (one per channel) in the
-// token order of the S^T accumulator (register r of block mb in half-wave h
-// holds token 32*mb + 8*(r/4) + 4*h + r%4), built from 4-token x 8-channel
-// pieces. Every LDS row is padded by 16 bytes: the 16 rows a half-wave
-// reads at one column then start 16 bytes apart, which spreads them over
-// all banks, and each fragment address is one base register plus an
-// immediate offset.
+// Register staging of K and V blocks (KVH tokens x D channels) and their
+// stores into LDS: K row-major, V transposed to V^T rows (one per channel)
+// in the token order of the S^T accumulator (register r of block mb in
+// half-wave h holds token 32*mb + 8*(r/4) + 4*h + r%4), built from 2-token x
+// 8-channel pieces (two consecutive tokens land on two adjacent positions).
+// Every LDS row is padded by 16 bytes: the 16 rows a half-wave reads at one
+// column then start 16 bytes apart, which spreads them over all banks, and
+// each fragment address is one base register plus an immediate offset.
 template <int KVH, int D, int THREADS, bool F32IN>
 struct BfTile {
   static constexpr int ES = F32IN ? 4 : 2;
@@ -273,120 +359,224 @@ struct BfTile {
   static constexpr int VS_ = CPR_V + 1;
   static constexpr int K_CHUNKS = KVH * CPR_K;
   static constexpr int K_PER_T = (K_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int QUARTERS = KVH / 4;
-  static constexpr int V_PIECES = QUARTERS * (D / 8);
+  static constexpr int PAIRS = KVH / 2;
+  static constexpr int V_PIECES = PAIRS * (D / 8);
   static constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
   static constexpr int K_LDS = KVH * KS_;           // uint4 per K buffer
   static constexpr int V_LDS = D * VS_;             // uint4 per V^T buffer
   uint4 kreg[K_PER_T];
-  uint4 vreg[V_PER_T][4];
+  uint4 vreg[V_PER_T][2];
+
+  // first token of V^T position pair q2 (positions 2*q2, 2*q2 + 1 hold
+  // tokens t0, t0 + 1): position 16*ps + 8*h + i of key group ps holds token
+  // 16*ps + 8*(i / 4) + 4*h + i % 4
+  static __device__ __forceinline__ int v_pair_token(int q2) {
+    const int pos = 2 * q2;
+    return 16 * (pos >> 4) + 8 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 1) + (pos & 3);
+  }
 
   // block_off: byte offset of the kv block inside this (b, head) slice
-  __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rv, uint32_t block_off, int tid) {
+  __device__ __forceinline__ void load_k(rsrc_t rk, uint32_t block_off, int tid) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int c = tid + i * THREADS;            // chunk c = 8 elements at element 8*c
       if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS)
         kreg[i] = bload8<F32IN>(rk, tid * 8 * ES, block_off + i * THREADS * 8 * ES);
     }
+  }
+  __device__ __forceinline__ void load_v(rsrc_t rv, uint32_t block_off, int tid) {
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (V_PIECES % THREADS == 0 || u < V_PIECES) {
-        const int q4 = u % QUARTERS, cc = u / QUARTERS;
-        const int pc = q4 >> 1;
-        const int tok0 = 16 * (pc >> 1) + 4 * (pc & 1) + 8 * (q4 & 1);
-        const uint32_t voff = (uint32_t)((tok0 * D + cc * 8) * ES);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vreg[i][j] = bload8<F32IN>(rv, voff + j * D * ES, block_off);
+        const int q2 = u % PAIRS, cc = u / PAIRS;
+        const uint32_t voff = (uint32_t)((v_pair_token(q2) * D + cc * 8) * ES);
+        vreg[i][0] = bload8<F32IN>(rv, voff, block_off);
+        vreg[i][1] = bload8<F32IN>(rv, voff, block_off + D * ES);
       }
     }
   }
-  __device__ __forceinline__ void store(uint4* k_lds, uint4* v_lds, int tid) const {
+  __device__ __forceinline__ void store_k(uint4* k_lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int c = tid + i * THREADS;
       if (K_CHUNKS % THREADS == 0 || c < K_CHUNKS) k_lds[(c / CPR_K) * KS_ + c % CPR_K] = kreg[i];
     }
+  }
+  __device__ __forceinline__ void store_v(uint4* v_lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
       if (V_PIECES % THREADS == 0 || u < V_PIECES) {
-        const int q4 = u % QUARTERS, cc = u / QUARTERS;
-        // positions 4*q4 .. 4*q4+3 of channel rows cc*8 .. cc*8+7
-        uint2* dst = reinterpret_cast<uint2*>(v_lds + (cc * 8) * VS_) + q4;
+        const int q2 = u % PAIRS, cc = u / PAIRS;
+        // positions 2*q2, 2*q2 + 1 of channel rows cc*8 .. cc*8+7
+        uint32_t* dst = reinterpret_cast<uint32_t*>(v_lds + (cc * 8) * VS_) + q2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int dw = e >> 1;
-          uint2 o;
-          if (e & 1) {
-            o.x = perm_hi(vreg[i][0][dw], vreg[i][1][dw]);
-            o.y = perm_hi(vreg[i][2][dw], vreg[i][3][dw]);
-          } else {
-            o.x = perm_lo(vreg[i][0][dw], vreg[i][1][dw]);
-            o.y = perm_lo(vreg[i][2][dw], vreg[i][3][dw]);
-          }
-          dst[e * VS_ * 2] = o;
+          dst[e * VS_ * 4] = (e & 1) ? perm_hi(vreg[i][0][dw], vreg[i][1][dw])
+                                     : perm_lo(vreg[i][0][dw], vreg[i][1][dw]);
         }
       }
     }
   }
 };
 
-// S^T (KVH kv tokens x 32 query rows) = K . Q^T from one K buffer. All K
-// fragments are read before the MFMAs so their LDS latency overlaps.
-template <int KVH, int D>
-__device__ __forceinline__ void bf_scores(const uint4* k_lds, const uint4 (&qf)[D / 16],
-                                          f32x16_t (&sacc)[KVH / 32], int l32, int half) {
-  constexpr int KS_ = D / 8 + 1;
-  const uint4* base = k_lds + l32 * KS_ + half;
-  uint4 kf[D / 16][KVH / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int mb = 0; mb < KVH / 32; ++mb) kf[ks][mb] = base[mb * 32 * KS_ + 2 * ks];
-#pragma unroll
-  for (int mb = 0; mb < KVH / 32; ++mb) sacc[mb] = f32x16_t{};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int mb = 0; mb < KVH / 32; ++mb)
-      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks][mb]),
-                                                         __builtin_bit_cast(bf16x8_t, qf[ks]),
-                                                         sacc[mb], 0, 0, 0);
-  reads_ahead_of_mfma<(D / 16) * (KVH / 32), 5>();
+// max / sum of a value over the two half-waves (lanes l and l ^ 32)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// P^T (bf16, B operands of the PV product) from the probabilities in sacc
-template <int KVH>
-__device__ __forceinline__ void bf_pack_p(const f32x16_t (&p)[KVH / 32], uint4 (&pk)[KVH / 16]) {
+// S^T block (KVH kv tokens x 32 query rows) = K . Q^T; kb = K buffer + lane base
+template <int KVH, int D>
+__device__ __forceinline__ void bf_scores(const uint4* kb, const uint4 (&qf)[D / 16],
+                                          f32x16_t (&sacc)[KVH / 32]) {
+  constexpr int KS_ = D / 8 + 1;
 #pragma unroll
-  for (int ps = 0; ps < KVH / 16; ++ps) {
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < KVH / 32; ++mb) {
+      const uint4 kf = kb[mb * 32 * KS_ + 2 * ks];
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                         __builtin_bit_cast(bf16x8_t, qf[ks]),
+                                                         ks == 0 ? f32x16_t{} : sacc[mb], 0, 0, 0);
+    }
+}
+
+// Padded keys of a block (bit (16*mb + r) of `bits` clear) get score -inf,
+// so the softmax below needs no mask: they add nothing to the maximum and
+// exp2 turns them into p = 0. The running maximum starts at -FLT_MAX rather
+// than -inf, so even a block whose keys are all padding yields p = 0, not NaN.
+template <int MB>
+__device__ __forceinline__ void mask_scores(f32x16_t (&s)[MB], uint32_t bits) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mb][r] = ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY;
+}
+
+// Row maximum of the raw scores (this lane's query row, both half-waves)
+template <int MB>
+__device__ __forceinline__ float bf_row_max(const f32x16_t (&s)[MB]) {
+  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[mb][r]);
+  return halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+}
+
+// Lazy running-max update from the block's row maximum `hi` (raw score
+// units, sl2 >= 0): m_run only moves when the block's scaled maximum exceeds
+// it by more than `lazy`. Returns the factor O must be multiplied by.
+__device__ __forceinline__ float bf_update_max(float hi, float sl2, float lazy, float& m_run,
+                                               float& l_run) {
+  const float mx = hi * sl2;
+  float alpha = 1.0f;
+  if (mx > m_run + lazy) {
+    alpha = fast_exp2(m_run - mx);                       // 0 on the first block
+    m_run = mx;
+    l_run *= alpha;
+  }
+  return alpha;
+}
+
+// p = exp2(s * sl2 - m_run) for the 16-key groups PS0 .. PS1-1 of the block,
+// packed to bf16 P^T operands; the packed (rounded) values are summed into
+// l_run, so numerator and denominator use the same weights.
+template <int MB, int PS0, int PS1>
+__device__ __forceinline__ void bf_exp_pack(const f32x16_t (&s)[MB], float sl2, float m_run,
+                                            float& l_run, uint4 (&pk)[2 * MB]) {
+  const float nm = -m_run;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int ps = PS0; ps < PS1; ++ps) {
     const int mb = ps >> 1, r0 = 8 * (ps & 1);
-    pk[ps] = make_uint4(pack2(p[mb][r0 + 0], p[mb][r0 + 1]), pack2(p[mb][r0 + 2], p[mb][r0 + 3]),
-                        pack2(p[mb][r0 + 4], p[mb][r0 + 5]), pack2(p[mb][r0 + 6], p[mb][r0 + 7]));
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[mb][r0 + i], sl2, nm));
+    pk[ps] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[ps].x), ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[ps].y), ones, acc1, false);
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[ps].z), ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[ps].w), ones, acc1, false);
+  }
+  l_run += acc0 + acc1;
+}
+
+// O^T += V^T . P^T for the 16-key groups PS0 .. PS1-1; vb = V^T buffer + lane base
+template <int KVH, int D, int PS0, int PS1>
+__device__ __forceinline__ void bf_pv(const uint4* vb, const uint4 (&pk)[KVH / 16],
+                                      f32x16_t (&oacc)[D / 32]) {
+  constexpr int VS_ = KVH / 8 + 1;
+#pragma unroll
+  for (int ps = PS0; ps < PS1; ++ps)
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const uint4 vf = vb[cb * 32 * VS_ + 2 * ps];
+      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                         __builtin_bit_cast(bf16x8_t, pk[ps]),
+                                                         oacc[cb], 0, 0, 0);
+    }
+}
+
+// Scheduling hint for a region of NM MFMAs, each fed by one LDS read issued
+// PRE MFMAs ahead, with up to NV VALU instructions placed after each MFMA.
+template <int NM, int PRE, int NV>
+__device__ __forceinline__ void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);          // DS reads
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+    if (i < NM - PRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);         // VALU
   }
 }
 
-// O^T += V^T . P^T from one V^T buffer (fragments read ahead of the MFMAs)
+// Row max of the current block and the lazy running-max update; returns
+// the factor O must be multiplied by before this block's PV products.
+template <int KVH>
+__device__ __forceinline__ float bf_block_max(const f32x16_t (&scur)[KVH / 32], float sl2,
+                                              float lazy, float& m_run, float& l_run) {
+  return bf_update_max(bf_row_max<KVH / 32>(scur), sl2, lazy, m_run, l_run);
+}
+
+// exp2/pack and PV products of the current block, each 16-key group of P
+// feeding its MFMAs as soon as it is packed
 template <int KVH, int D>
-__device__ __forceinline__ void bf_pv(const uint4* v_lds, const uint4 (&pk)[KVH / 16],
-                                      f32x16_t (&oacc)[D / 32], int l32, int half) {
-  constexpr int VS_ = KVH / 8 + 1;
-  const uint4* base = v_lds + l32 * VS_ + half;
-  uint4 vf[KVH / 16][D / 32];
-#pragma unroll
-  for (int ps = 0; ps < KVH / 16; ++ps)
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) vf[ps][cb] = base[cb * 32 * VS_ + 2 * ps];
-#pragma unroll
-  for (int ps = 0; ps < KVH / 16; ++ps)
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[ps][cb]),
-                                                         __builtin_bit_cast(bf16x8_t, pk[ps]),
-                                                         oacc[cb], 0, 0, 0);
-  reads_ahead_of_mfma<(KVH / 16) * (D / 32), 5>();
+__device__ __forceinline__ void bf_block_pv(const uint4* vb, const f32x16_t (&scur)[KVH / 32],
+                                            float sl2, float m_run, float& l_run,
+                                            f32x16_t (&oacc)[D / 32]) {
+  constexpr int MB = KVH / 32, NPS = KVH / 16;
+  uint4 pk[NPS];
+  bf_exp_pack<MB, 0, NPS / 2>(scur, sl2, m_run, l_run, pk);
+  bf_pv<KVH, D, 0, NPS / 2>(vb, pk, oacc);
+  bf_exp_pack<MB, NPS / 2, NPS>(scur, sl2, m_run, l_run, pk);
+  bf_pv<KVH, D, NPS / 2, NPS>(vb, pk, oacc);
+}
+
+// One pipelined step: the score MFMAs of the next block and the PV MFMAs of
+// the current one, with the current block's exp2/pack work and the next
+// block's row maximum (taken without its pad mask) interleaved between them.
+// Returns that row maximum.
+template <int KVH, int D>
+__device__ __forceinline__ float bf_step_mfma(const uint4* kb, const uint4* vb,
+                                              const uint4 (&qf)[D / 16],
+                                              f32x16_t (&snext)[KVH / 32],
+                                              const f32x16_t (&scur)[KVH / 32], float sl2,
+                                              float m_run, float& l_run,
+                                              f32x16_t (&oacc)[D / 32]) {
+  bf_scores<KVH, D>(kb, qf, snext);
+  bf_block_pv<KVH, D>(vb, scur, sl2, m_run, l_run, oacc);
+  const float hi = bf_row_max<KVH / 32>(snext);
+  interleave_hint<(D / 16) * (KVH / 32) + (KVH / 16) * (D / 32), 3, 4>();
+  return hi;
 }
 
 // Q^T fragments for query row 32*rg + l32 of tile qt; a negative softmax
@@ -410,7 +600,7 @@ __device__ __forceinline__ void bf_epilogue(const DevLayout& L, const AttnArgs& 
                                             float m_run, float l_run) {
   const TileValid tq = tile_valid(L, ww.qt);
   const int qrow = 32 * rg + l32;
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = halves_sum(l_run);
   const bool real = row_is_real(L, tq, qrow);
   const float inv = (real && lt > 0.0f) ? 1.0f / lt : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
@@ -436,24 +626,30 @@ __device__ __forceinline__ void bf_epilogue(const DevLayout& L, const AttnArgs& 
 
 constexpr float kLazyBf16 = 8.0f;
 
-// Generic kernel: routed lists (QPW = 1) and 32-token tiles. Each list entry
-// is walked as TILE/KVH kv blocks of KVH tokens, double-buffered in LDS.
-// KVH = 32 for 64-token tiles with routed lists keeps two buffers within
-// 32 KB, so four workgroups (eight waves) fit a CU.
+// One kernel for every bf16 / f32-input shape. Each schedule entry (a key
+// tile) is walked as TILE/KVH kv blocks of KVH tokens. KVH = 32 for routed
+// lists over 64-token tiles keeps the LDS buffers within 36 KB, so four
+// workgroups (eight waves) fit a CU.
+//
+// Two walks: the pipelined one when every wave owns every block (routed
+// lists, dense lists, query tiles sharing one list), and a plain
+// double-buffered one for unions whose blocks some waves skip.
 template <int TILE, int KVH, int D, int QPW, bool F32IN>
 __global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int WPQ = TILE / 32;         // waves per query tile
   constexpr int SUB = TILE / KVH;        // kv blocks per tile
   constexpr int MB = KVH / 32;
+  constexpr int NPS = KVH / 16;
   constexpr int THREADS = 64 * QPW * WPQ;
   using IO = BfTile<KVH, D, THREADS, F32IN>;
   static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
 
   __shared__ uint4 k_lds[2][IO::K_LDS];
   __shared__ uint4 v_lds[2][IO::V_LDS];
-  __shared__ int scan[THREADS];
-  extern __shared__ int dyn[];           // QPW > 1: marks + schedule
+  extern __shared__ int sched[];         // QPW > 1: the schedule (n_tiles entries)
+  static_assert(THREADS * 4 <= IO::K_LDS * 16, "scan scratch fits one K buffer");
+  static_assert(4096 <= IO::V_LDS * 16, "marks of 4096 tiles fit one V buffer");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -463,9 +659,14 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   const int rg = wave % WPQ;
 
   const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
-  const int* sched = dyn + L.n_tiles;
+  // the marks (n_tiles bytes, n_tiles <= 4096 on this path) and the scan
+  // borrow the second K/V buffers, which the walk first writes after the
+  // schedule's closing barrier
   int len;
-  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
+  bool shared = true;
+  if constexpr (QPW > 1)
+    len = build_schedule<QPW, WPQ>(L, ww, reinterpret_cast<uint32_t*>(v_lds[1]),
+                                   reinterpret_cast<int*>(k_lds[1]), sched, tid, lane, shared);
   else len = ww.cnt;
 
   const long long head_bytes = L.n_padded * D * IO::ES;
@@ -481,42 +682,120 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -FLT_MAX, l_run = 0.0f;
 
-  IO io;
-  auto block_off = [&](int step) -> uint32_t {
-    const int tile = sched_tile<QPW>(sched, ww, step / SUB, L.n_tiles);
-    return (uint32_t)((tile * TILE + (step % SUB) * KVH) * D * IO::ES);
-  };
   const int steps = len * SUB;
-  if (steps > 0) {
-    io.load(rk, rv, block_off(0), tid);
-    io.store(k_lds[0], v_lds[0], tid);
-    __syncthreads();
-  }
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    const int entry = s / SUB;
-    const int tile = sched_tile<QPW>(sched, ww, entry, L.n_tiles);
-    const bool mine = sched_mine<QPW>(sched, entry, ww.slot);
-    const bool has_next = s + 1 < steps;
-    if (has_next) io.load(rk, rv, block_off(s + 1), tid);
-    if (mine) {
-      f32x16_t sacc[MB];
-      bf_scores<KVH, D>(k_lds[cur], qf, sacc, l32, half);
-      bool full;
-      const uint32_t bits = kv_valid_bits<MB>(L, tile, (s % SUB) * KVH, lane, half, full);
-      const float alpha = softmax_step<MB>(sacc, full, bits, sl2, kLazyBf16, m_run, l_run);
-      if (alpha != 1.0f) {
+  IO io;
+  SchedWindow<QPW, SUB, KVH> win;
+  win.fill(L, ww, sched, len, 0, lane);
+  // the window must hold the entries of steps s .. s+2 before step s
+  auto cover = [&](int s) {
+    win.cover(L, ww, sched, len, s / SUB, min(s + 2, max(steps - 1, 0)) / SUB, lane);
+  };
+  // byte offset of kv block `step`; steps past the end reload the last
+  // block into a buffer nobody reads again
+  auto block_off = [&](int step) -> uint32_t {
+    step = min(step, steps - 1);
+    return (uint32_t)((win.tile(step / SUB) * TILE + (step % SUB) * KVH) * D * IO::ES);
+  };
+  const int k_lane = l32 * IO::KS_ + half;
+  const int v_lane = l32 * IO::VS_ + half;
+  // pad mask of block s: bit (16*mb + r) set for real keys, `full` when all are
+  auto block_bits = [&](int s, bool& full) -> uint32_t {
+    full = ((win.flags(s / SUB) >> (s % SUB)) & 1) == 0;
+    if (full) return 0xFFFFFFFFu;
+    return kv_pad_bits<MB>(L, win.tile(s / SUB), (s % SUB) * KVH, lane, half);
+  };
+  // running-max update from a block's row maximum and the (rare) rescale of O
+  auto update_max = [&](float hi) __attribute__((always_inline)) {
+    const float alpha = bf_update_max(hi, sl2, kLazyBf16, m_run, l_run);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {   // lanes whose max did not move multiply by 1
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
-      }
-      uint4 pk[KVH / 16];
-      bf_pack_p<KVH>(sacc, pk);
-      bf_pv<KVH, D>(v_lds[cur], pk, oacc, l32, half);
+      for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
     }
-    if (has_next) io.store(k_lds[cur ^ 1], v_lds[cur ^ 1], tid);
-    __syncthreads();
+  };
+
+  if (shared) {
+    // Pipelined walk. Step s (buffer parity P = s & 1): V(s) sits in V buffer
+    // P, K(s+1) in K buffer P^1; K(s+2) is staged into K buffer P and V(s+1)
+    // into V buffer P^1, both last read before the previous barrier. The row
+    // maximum of block s+1 is taken during step s. At the last step the
+    // scores of a clamped block are computed and never used.
+    f32x16_t s_a[MB], s_b[MB];
+    float hi = 0.0f;
+    if (steps > 0) {
+      io.load_k(rk, block_off(0), tid);
+      io.load_v(rv, block_off(0), tid);
+      io.store_k(k_lds[0], tid);
+      io.store_v(v_lds[0], tid);
+      io.load_k(rk, block_off(1), tid);
+      io.store_k(k_lds[1], tid);
+      __syncthreads();
+      bf_scores<KVH, D>(k_lds[0] + k_lane, qf, s_a);
+      hi = bf_row_max<MB>(s_a);
+      __syncthreads();                   // K buffer 0 is refilled during step 0
+    }
+    // `hi` is block s's row maximum taken without its pad mask; a padded
+    // block (rare) is masked and its maximum retaken at the step's start
+    auto step = [&](auto parity, int s, f32x16_t (&scur)[MB],
+                    f32x16_t (&snext)[MB]) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      cover(s);
+      io.load_k(rk, block_off(s + 2), tid);
+      io.load_v(rv, block_off(s + 1), tid);
+      bool full;
+      const uint32_t bits = block_bits(s, full);
+      if (!full) {
+        mask_scores<MB>(scur, bits);
+        hi = bf_row_max<MB>(scur);
+      }
+      update_max(hi);
+      hi = bf_step_mfma<KVH, D>(k_lds[P ^ 1] + k_lane, v_lds[P] + v_lane, qf, snext, scur, sl2,
+                                m_run, l_run, oacc);
+      __builtin_amdgcn_sched_barrier(0);  // the staging stores wait for their loads here
+      io.store_k(k_lds[P], tid);
+      io.store_v(v_lds[P ^ 1], tid);
+      __syncthreads();
+    };
+    for (int s = 0; s < steps; s += 2) {
+      step(std::integral_constant<int, 0>{}, s, s_a, s_b);
+      if (s + 1 >= steps) break;
+      step(std::integral_constant<int, 1>{}, s + 1, s_b, s_a);
+    }
+  } else {
+    // Plain double-buffered walk over a union: block s+1 is staged while
+    // block s is computed by the waves whose list holds it.
+    if (steps > 0) {
+      io.load_k(rk, block_off(0), tid);
+      io.load_v(rv, block_off(0), tid);
+      io.store_k(k_lds[0], tid);
+      io.store_v(v_lds[0], tid);
+      __syncthreads();
+    }
+    for (int s = 0; s < steps; ++s) {
+      const int P = s & 1;
+      const bool has_next = s + 1 < steps;
+      cover(s);
+      if (has_next) {
+        io.load_k(rk, block_off(s + 1), tid);
+        io.load_v(rv, block_off(s + 1), tid);
+      }
+      if ((win.flags(s / SUB) >> (8 + ww.slot)) & 1) {
+        f32x16_t sc[MB];
+        bf_scores<KVH, D>(k_lds[P] + k_lane, qf, sc);
+        bool full;
+        const uint32_t bits = block_bits(s, full);
+        if (!full) mask_scores<MB>(sc, bits);
+        update_max(bf_row_max<MB>(sc));
+        bf_block_pv<KVH, D>(v_lds[P] + v_lane, sc, sl2, m_run, l_run, oacc);
+        interleave_hint<(KVH / 16) * (D / 32), 3, 4>();
+      }
+      if (has_next) {
+        io.store_k(k_lds[P ^ 1], tid);
+        io.store_v(v_lds[P ^ 1], tid);
+      }
+      __syncthreads();
+    }
   }
   if (!ww.active) return;
   bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
@@ -561,8 +840,9 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 
   __shared__ uint4 k_lds[2][TILE * kK8Stride];       // 64 rows x (128 + 16) B
   __shared__ uint4 v_lds[2][D * kV8Stride];          // V^T: 128 rows x (64 + 16) B
-  __shared__ int scan[THREADS];
-  extern __shared__ int dyn[];
+  extern __shared__ int sched[];
+  static_assert(THREADS * 4 <= TILE * kK8Stride * 16, "scan scratch fits one K buffer");
+  static_assert(4096 <= D * kV8Stride * 16, "marks of 4096 tiles fit one V buffer");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -572,10 +852,13 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   const int rg = wave % WPQ;
 
   const WaveWork ww = wave_work<QPW, WPQ>(L, a, n_work, wave);
-  const int* sched = dyn + L.n_tiles;
   int len;
-  if constexpr (QPW > 1) len = build_schedule<QPW, WPQ>(L, ww, dyn, scan, tid, lane);
+  bool shared = true;
+  if constexpr (QPW > 1)
+    len = build_schedule<QPW, WPQ>(L, ww, reinterpret_cast<uint32_t*>(v_lds[1]),
+                                   reinterpret_cast<int*>(k_lds[1]), sched, tid, lane, shared);
   else len = ww.cnt;
+  (void)shared;
 
   const long long head_bytes = L.n_padded * D;
   const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(a.q) + ww.head_row0 * D, head_bytes);
@@ -772,7 +1055,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 template <int TILE, int KVH, int D, int QPW, bool F32IN>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
-  const size_t dyn = QPW > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
+  const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
   hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN>), dim3(n_work),
                      dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
@@ -781,7 +1064,7 @@ hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
 template <int QPW>
 hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
-  const size_t dyn = QPW > 1 ? (size_t)2 * L.n_tiles * sizeof(int) : 0;
+  const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
   hipLaunchKernelGGL((attn_fp8_kernel<QPW>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
