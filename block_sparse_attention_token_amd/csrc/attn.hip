@@ -675,7 +675,8 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + ww.head_row0 * D * IO::ES, head_bytes);
   const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + ww.head_row0 * D * IO::ES, head_bytes);
 
-  const float sl2 = fabsf(a.scale_log2);
+  // kept > 0 (a zero scale gives uniform weights) so a masked -inf stays -inf
+  const float sl2 = fmaxf(fabsf(a.scale_log2), FLT_MIN);
   uint4 qf[D / 16];
   bf_load_q<TILE, D, F32IN>(rq, min(ww.qt, L.n_tiles - 1), rg, l32, half,
                             a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
@@ -806,17 +807,23 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
 // sparsity). Q/K/V are e4m3 codes with one fp32 scale per (b, head, tile);
 // tiles are 64 tokens, d = 128, and one wave owns 32 query rows (two waves
 // per query tile, two waves per SIMD), as in the bf16 kernel.
-//   S^T = Kc . Qc^T   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales,
-//                     times q_scale * k_scale(tile) * sigma * log2(e);
-//   O^T += Vc^T . P8^T with P8 = e4m3(p * 112 * v_scale(tile) / max_t v_scale).
-// The lazy-rescale threshold is 2 (p <= 4), so p * 112 * (<= 1) stays within
-// e4m3's 448. Folding v_scale(tile) / max v_scale into P keeps one O
-// accumulator scale for the whole walk: O = acc * max v_scale / 112 / l.
+//   S^T = Kc . Qc^T   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+//                     scales; the exponent of p is S * cs(tile) with
+//                     cs = q_scale * k_scale(tile) * sigma * log2(e);
+//   O^T += Vc^T . P8^T, P8 = e4m3(p * ps(tile)), ps = 112 * v_scale(tile) /
+//                     max_t v_scale (112 for an all-zero V tile, whose codes
+//                     are all zero).
+// ps is folded into the exponent (p * ps = exp2(S * cs - m + log2 ps)) and
+// the running sum adds the tile's sum of p * ps times 1/ps. The lazy-rescale
+// threshold is 2 (p <= 4), so p * ps <= 448 fits e4m3, and one O accumulator
+// scale serves the whole walk: O = acc * max v_scale / 112 / l.
 // The two half-waves each hold 32 of a tile's 64 kv tokens (element e of a
 // lane in half-wave h is token 32*(e/16) + 8*((e%16)/4) + 4*h + e%4), so one
-// K=64 MFMA covers the whole tile in the PV product. LDS keeps two K/V tile
-// buffers in both work shapes, rows padded by 16 bytes as in the bf16 kernel.
+// K=64 MFMA covers the whole tile in the PV product. The walks are those of
+// the bf16 kernel: pipelined when every wave owns every tile, a plain
+// double-buffered union walk otherwise; LDS rows are padded by 16 bytes.
 constexpr float kP8Scale = 112.0f;          // 448 / 2^2
+constexpr float kLazyFp8 = 2.0f;
 
 constexpr int kK8Stride = 9;                // K rows: 8 chunks of 16 codes + 16 B pad
 constexpr int kV8Stride = 5;                // V^T rows: 4 chunks + 16 B pad
@@ -828,21 +835,123 @@ __device__ __forceinline__ i32x8_t cat8(uint4 x, uint4 y) {
   return r;
 }
 
+// Register staging of an fp8 K/V tile and its stores into LDS (K row-major,
+// V transposed to V^T rows in the token order above, from 4-token x
+// 16-channel pieces).
+template <int THREADS>
+struct F8Tile {
+  static constexpr int TILE = 64, D = 128;
+  static constexpr int K_PER_T = TILE * D / 16 / THREADS;   // 16-code chunks per thread
+  static constexpr int V_PIECES = (TILE / 4) * (D / 16);
+  static constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
+  static constexpr int K_LDS = TILE * kK8Stride;            // uint4 per K buffer
+  static constexpr int V_LDS = D * kV8Stride;               // uint4 per V^T buffer
+  uint4 kreg[K_PER_T];
+  uint4 vreg[V_PER_T][4];
+
+  __device__ __forceinline__ void load_k(rsrc_t rk, uint32_t tile_off, int tid) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) kreg[i] = bload(rk, tid * 16, tile_off + i * THREADS * 16);
+  }
+  __device__ __forceinline__ void store_k(uint4* k_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int c = tid + i * THREADS;
+      k_lds[(c >> 3) * kK8Stride + (c & 7)] = kreg[i];
+    }
+  }
+  // piece u: tokens 4*(u % 16) .. +3 x channels 16*(u / 16) .. +15
+  __device__ __forceinline__ void load_v(rsrc_t rv, uint32_t tile_off, int tid) {
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * THREADS;
+      if (V_PIECES % THREADS == 0 || u < V_PIECES) {
+        const uint32_t voff = (uint32_t)(4 * (u & 15) * D + 16 * (u >> 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vreg[i][j] = bload(rv, voff, tile_off + j * D);
+      }
+    }
+  }
+  // tokens t0..t0+3 sit at V^T byte positions p0..p0+3 with
+  // p0 = 32*h + 16*(t0/32) + 4*((t0/8)%4), h = (t0/4)%2
+  __device__ __forceinline__ void store_v(uint4* v_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * THREADS;
+      if (V_PIECES % THREADS == 0 || u < V_PIECES) {
+        const int cg = u >> 4, tok0 = 4 * (u & 15);
+        const int hh = (tok0 >> 2) & 1, A = tok0 >> 5, B = (tok0 >> 3) & 3;
+        const int p0 = 32 * hh + 16 * A + 4 * B;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(v_lds + (16 * cg) * kV8Stride) + (p0 >> 2);
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          const uint32_t x01l = __builtin_amdgcn_perm(vreg[i][1][dw], vreg[i][0][dw], 0x05010400u);
+          const uint32_t x01h = __builtin_amdgcn_perm(vreg[i][1][dw], vreg[i][0][dw], 0x07030602u);
+          const uint32_t x23l = __builtin_amdgcn_perm(vreg[i][3][dw], vreg[i][2][dw], 0x05010400u);
+          const uint32_t x23h = __builtin_amdgcn_perm(vreg[i][3][dw], vreg[i][2][dw], 0x07030602u);
+          dst[(4 * dw + 0) * kV8Stride * 4] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+          dst[(4 * dw + 1) * kV8Stride * 4] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+          dst[(4 * dw + 2) * kV8Stride * 4] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+          dst[(4 * dw + 3) * kV8Stride * 4] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+        }
+      }
+    }
+  }
+};
+
+// S^T (64 kv tokens x 32 query rows, raw code products) from one K buffer
+// (kb = buffer + lane base)
+__device__ __forceinline__ void f8_scores(const uint4* kb, const i32x8_t (&qf)[2], f32x16_t (&sacc)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const i32x8_t kf = cat8(kb[mb * 32 * kK8Stride + 4 * ks], kb[mb * 32 * kK8Stride + 4 * ks + 1]);
+      sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], ks == 0 ? f32x16_t{} : sacc[mb],
+                                                                 0, 0, 0, 127, 0, 127);
+    }
+}
+
+// P8^T = e4m3(exp2(S * cs + e0)) for the tile's 32 scores of this lane (e0 =
+// log2 ps - m_run); returns the sum of the unrounded p * ps
+__device__ __forceinline__ float f8_exp_pack(const f32x16_t (&s)[2], float cs, float e0, i32x8_t& pk) {
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int mb = i >> 2, r0 = 4 * (i & 3);
+    const float p0 = fast_exp2(fmaf(s[mb][r0 + 0], cs, e0));
+    const float p1 = fast_exp2(fmaf(s[mb][r0 + 1], cs, e0));
+    const float p2 = fast_exp2(fmaf(s[mb][r0 + 2], cs, e0));
+    const float p3 = fast_exp2(fmaf(s[mb][r0 + 3], cs, e0));
+    acc0 += p0 + p1;
+    acc1 += p2 + p3;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+    pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+  }
+  return acc0 + acc1;
+}
+
+// O^T += Vc^T . P8^T (vb = V^T buffer + lane base)
+__device__ __forceinline__ void f8_pv(const uint4* vb, const i32x8_t& pk, f32x16_t (&oacc)[4]) {
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const i32x8_t vf = cat8(vb[cb * 32 * kV8Stride], vb[cb * 32 * kV8Stride + 1]);
+    oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, oacc[cb], 0, 0, 0, 127, 0, 127);
+  }
+}
+
 template <int QPW>
 __global__ __launch_bounds__(128 * QPW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
-  constexpr int TILE = 64, D = 128, WPQ = 2, MB = 2, CB = 4, KS = 2;
+  constexpr int TILE = 64, D = 128, WPQ = 2, MB = 2, CB = 4, SUB = 1, KVH = 64;
   constexpr int THREADS = 64 * QPW * WPQ;
-  constexpr int K_PER_T = TILE * D / 16 / THREADS;   // 512 chunks of 16 codes
-  constexpr int V_PIECES = (TILE / 4) * (D / 16);    // 4 tokens x 16 channels
-  constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
-  constexpr float kLazy = 2.0f;
+  using IO = F8Tile<THREADS>;
 
-  __shared__ uint4 k_lds[2][TILE * kK8Stride];       // 64 rows x (128 + 16) B
-  __shared__ uint4 v_lds[2][D * kV8Stride];          // V^T: 128 rows x (64 + 16) B
+  __shared__ uint4 k_lds[2][IO::K_LDS];               // 64 rows x (128 + 16) B
+  __shared__ uint4 v_lds[2][IO::V_LDS];               // V^T: 128 rows x (64 + 16) B
   extern __shared__ int sched[];
-  static_assert(THREADS * 4 <= TILE * kK8Stride * 16, "scan scratch fits one K buffer");
-  static_assert(4096 <= D * kV8Stride * 16, "marks of 4096 tiles fit one V buffer");
+  static_assert(THREADS * 4 <= IO::K_LDS * 16, "scan scratch fits one K buffer");
+  static_assert(4096 <= IO::V_LDS * 16, "marks of 4096 tiles fit one V buffer");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -858,7 +967,6 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     len = build_schedule<QPW, WPQ>(L, ww, reinterpret_cast<uint32_t*>(v_lds[1]),
                                    reinterpret_cast<int*>(k_lds[1]), sched, tid, lane, shared);
   else len = ww.cnt;
-  (void)shared;
 
   const long long head_bytes = L.n_padded * D;
   const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(a.q) + ww.head_row0 * D, head_bytes);
@@ -874,16 +982,17 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   for (int off = 32; off > 0; off >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, off));
   const float inv_wmax = wmax > 0.0f ? 1.0f / wmax : 0.0f;
   const int qt_c = min(ww.qt, L.n_tiles - 1);
-  // a negative softmax scale is folded into Q (sign bit of every code)
+  // a negative softmax scale is folded into Q (sign bit of every code); the
+  // exponent scale is kept positive so that -inf stays -inf
   const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80808080u : 0u;
   const float qk_base = a.q_scale[(long long)ww.bh * L.n_tiles + qt_c] * fabsf(a.scale_log2);
 
   // Q codes as B operands: query row 32*rg + l32, bytes 64*ks + 32*half .. +31
-  i32x8_t qf[KS];
+  i32x8_t qf[2];
   {
     const uint32_t row_off = (uint32_t)((qt_c * TILE + 32 * rg + l32) * D);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       uint4 x = bload(rq, row_off + 64 * ks + 32 * half, 0);
       uint4 y = bload(rq, row_off + 64 * ks + 32 * half + 16, 0);
       x = make_uint4(x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign);
@@ -895,145 +1004,138 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   f32x16_t oacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -FLT_MAX, l_run = 0.0f;
 
-  uint4 kreg[K_PER_T];
-  uint4 vreg[V_PER_T][4];
-  auto load_k = [&](int tile) {
-    const uint32_t tile_off = (uint32_t)(tile * TILE * D);
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) kreg[i] = bload(rk, tid * 16, tile_off + i * THREADS * 16);
+  const int steps = len;
+  IO io;
+  SchedWindow<QPW, SUB, KVH> win;
+  // per-tile exponent scale, log2 ps and 1/ps of the window's tiles (lane i: entry base + i)
+  float cs_v = 0.0f, lps_v = 0.0f, ips_v = 1.0f;
+  auto fill = [&](int base) {
+    win.fill(L, ww, sched, len, base, lane);
+    const int t = win.tile_v;
+    const float vs = vsc[t];
+    float ps = vs > 0.0f ? fmaxf(kP8Scale * vs * inv_wmax, 0x1p-60f) : kP8Scale;
+    cs_v = fmaxf(qk_base * ksc[t], FLT_MIN);         // > 0, so a masked -inf stays -inf
+    lps_v = __log2f(ps);
+    ips_v = 1.0f / ps;
   };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * THREADS;
-      k_lds[buf][(c >> 3) * kK8Stride + (c & 7)] = kreg[i];
-    }
+  fill(0);
+  auto cover = [&](int s) {
+    if (min(s + 2, max(steps - 1, 0)) - win.base >= 64) fill(s);
   };
-  // V piece u: tokens tok0 .. tok0+3 (tok0 = 4 * (u % 16)) x channels 16 * (u / 16) ..
-  auto load_v = [&](int tile) {
-    const uint32_t tile_off = (uint32_t)(tile * TILE * D);
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * THREADS;
-      if (u < V_PIECES) {
-        const uint32_t voff = (uint32_t)(4 * (u & 15) * D + 16 * (u >> 4));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vreg[i][j] = bload(rv, voff + j * D, tile_off);
-      }
-    }
+  auto rd = [&](float v, int s) { return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), s - win.base)); };
+  auto tile_off = [&](int step) -> uint32_t {
+    step = min(step, steps - 1);
+    return (uint32_t)(win.tile(step) * TILE * D);
   };
-  // tokens tok0..tok0+3 sit at V^T byte positions p0..p0+3 with
-  // p0 = 32*h + 16*(tok0/32) + 4*((tok0/8)%4), h = (tok0/4)%2
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * THREADS;
-      if (u < V_PIECES) {
-        const int cg = u >> 4, tok0 = 4 * (u & 15);
-        const int hh = (tok0 >> 2) & 1, A = tok0 >> 5, B = (tok0 >> 3) & 3;
-        const int p0 = 32 * hh + 16 * A + 4 * B;
-        const uint32_t in[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
-                                   {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w},
-                                   {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w},
-                                   {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w}};
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          const uint32_t x01l = __builtin_amdgcn_perm(in[1][dw], in[0][dw], 0x05010400u);
-          const uint32_t x01h = __builtin_amdgcn_perm(in[1][dw], in[0][dw], 0x07030602u);
-          const uint32_t x23l = __builtin_amdgcn_perm(in[3][dw], in[2][dw], 0x05010400u);
-          const uint32_t x23h = __builtin_amdgcn_perm(in[3][dw], in[2][dw], 0x07030602u);
-          const uint32_t o[4] = {__builtin_amdgcn_perm(x23l, x01l, 0x05040100u),
-                                 __builtin_amdgcn_perm(x23l, x01l, 0x07060302u),
-                                 __builtin_amdgcn_perm(x23h, x01h, 0x05040100u),
-                                 __builtin_amdgcn_perm(x23h, x01h, 0x07060302u)};
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int c = 16 * cg + 4 * dw + bb;
-            reinterpret_cast<uint32_t*>(&v_lds[buf][c * kV8Stride])[p0 >> 2] = o[bb];
-          }
-        }
-      }
+  const int k_lane = l32 * kK8Stride + 2 * half;
+  const int v_lane = l32 * kV8Stride + 2 * half;
+  // pad mask, running-max update (rare rescale of O) and exp2/pack of block
+  // s; returns the packed P8^T operand
+  auto softmax = [&](int s, f32x16_t (&sc)[MB], float hi) __attribute__((always_inline)) {
+    const float cs = rd(cs_v, s);
+    const float mx = hi * cs;
+    float alpha = 1.0f;
+    if (mx > m_run + kLazyFp8) {
+      alpha = fast_exp2(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
     }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {   // lanes whose max did not move multiply by 1
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+    }
+    i32x8_t pk;
+    const float psum = f8_exp_pack(sc, cs, rd(lps_v, s) - m_run, pk);
+    l_run = fmaf(psum, rd(ips_v, s), l_run);
+    return pk;
+  };
+  // pad mask of block s applied to its scores; returns their row maximum
+  auto mask_max = [&](int s, f32x16_t (&sc)[MB], float hi) __attribute__((always_inline)) {
+    if ((win.flags(s) & 1) != 0) {
+      mask_scores<MB>(sc, kv_pad_bits<MB>(L, win.tile(s), 0, lane, half));
+      hi = bf_row_max<MB>(sc);
+    }
+    return hi;
   };
 
-  if (len > 0) {
-    const int t0 = sched_tile<QPW>(sched, ww, 0, L.n_tiles);
-    load_k(t0);
-    load_v(t0);
-    store_k(0);
-    store_v(0);
-    __syncthreads();
-  }
-
-  for (int s = 0; s < len; ++s) {
-    const int cur = s & 1;
-    const int tile = sched_tile<QPW>(sched, ww, s, L.n_tiles);
-    const bool mine = sched_mine<QPW>(sched, s, ww.slot);
-    const bool has_next = s + 1 < len;
-    if (has_next) {
-      const int next = sched_tile<QPW>(sched, ww, s + 1, L.n_tiles);
-      load_k(next);
-      load_v(next);
+  if (shared) {
+    // Pipelined walk: step s computes the scores of tile s+1 and the PV
+    // products of tile s under the softmax of tile s (buffers as in the
+    // bf16 kernel: V(s) in V buffer P, K(s+1) in K buffer P^1; K(s+2) and
+    // V(s+1) are staged into K buffer P and V buffer P^1).
+    f32x16_t s_a[MB], s_b[MB];
+    float hi = 0.0f;
+    if (steps > 0) {
+      io.load_k(rk, tile_off(0), tid);
+      io.load_v(rv, tile_off(0), tid);
+      io.store_k(k_lds[0], tid);
+      io.store_v(v_lds[0], tid);
+      io.load_k(rk, tile_off(1), tid);
+      io.store_k(k_lds[1], tid);
+      __syncthreads();
+      f8_scores(k_lds[0] + k_lane, qf, s_a);
+      hi = bf_row_max<MB>(s_a);
+      __syncthreads();                   // K buffer 0 is refilled during step 0
     }
-    if (mine) {
-      f32x16_t sacc[MB];
-      i32x8_t kf[KS][MB];
-      const uint4* kb = k_lds[cur] + l32 * kK8Stride + 2 * half;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          kf[ks][mb] = cat8(kb[mb * 32 * kK8Stride + 4 * ks], kb[mb * 32 * kK8Stride + 4 * ks + 1]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[ks][mb], qf[ks], sacc[mb], 0,
-                                                                     0, 0, 127, 0, 127);
-      bool full;
-      const uint32_t bits = kv_valid_bits<MB>(L, tile, 0, lane, half, full);
-      const float cs = qk_base * ksc[tile];
-      const float pscale = kP8Scale * vsc[tile] * inv_wmax;
-      const float alpha = softmax_step<MB>(sacc, full, bits, cs, kLazy, m_run, l_run);
-      if (alpha != 1.0f) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+    auto step = [&](auto parity, int s, f32x16_t (&scur)[MB],
+                    f32x16_t (&snext)[MB]) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      cover(s);
+      io.load_k(rk, tile_off(s + 2), tid);
+      io.load_v(rv, tile_off(s + 1), tid);
+      hi = mask_max(s, scur, hi);
+      f8_scores(k_lds[P ^ 1] + k_lane, qf, snext);
+      const i32x8_t pk = softmax(s, scur, hi);
+      f8_pv(v_lds[P] + v_lane, pk, oacc);
+      hi = bf_row_max<MB>(snext);
+      interleave_hint<8, 2, 8>();
+      __builtin_amdgcn_sched_barrier(0);  // the staging stores wait for their loads here
+      io.store_k(k_lds[P], tid);
+      io.store_v(v_lds[P ^ 1], tid);
+      __syncthreads();
+    };
+    for (int s = 0; s < steps; s += 2) {
+      step(std::integral_constant<int, 0>{}, s, s_a, s_b);
+      if (s + 1 >= steps) break;
+      step(std::integral_constant<int, 1>{}, s + 1, s_b, s_a);
+    }
+  } else {
+    if (steps > 0) {
+      io.load_k(rk, tile_off(0), tid);
+      io.load_v(rv, tile_off(0), tid);
+      io.store_k(k_lds[0], tid);
+      io.store_v(v_lds[0], tid);
+      __syncthreads();
+    }
+    for (int s = 0; s < steps; ++s) {
+      const int P = s & 1;
+      const bool has_next = s + 1 < steps;
+      cover(s);
+      if (has_next) {
+        io.load_k(rk, tile_off(s + 1), tid);
+        io.load_v(rv, tile_off(s + 1), tid);
       }
-      i32x8_t pk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int mb = i >> 2, r0 = 4 * (i & 3);
-        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[mb][r0] * pscale, sacc[mb][r0 + 1] * pscale,
-                                                 0, false);
-        wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[mb][r0 + 2] * pscale,
-                                             sacc[mb][r0 + 3] * pscale, wv, true);
-        pk[i] = wv;
+      if ((win.flags(s) >> (8 + ww.slot)) & 1) {
+        f32x16_t sc[MB];
+        f8_scores(k_lds[P] + k_lane, qf, sc);
+        const float hi = mask_max(s, sc, bf_row_max<MB>(sc));
+        const i32x8_t pk = softmax(s, sc, hi);
+        f8_pv(v_lds[P] + v_lane, pk, oacc);
       }
-      i32x8_t vf[CB];
-      const uint4* vb = v_lds[cur] + l32 * kV8Stride + 2 * half;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        vf[cb] = cat8(vb[cb * 32 * kV8Stride], vb[cb * 32 * kV8Stride + 1]);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[cb], pk, oacc[cb], 0, 0, 0,
-                                                                   127, 0, 127);
+      if (has_next) {
+        io.store_k(k_lds[P ^ 1], tid);
+        io.store_v(v_lds[P ^ 1], tid);
+      }
+      __syncthreads();
     }
-    if (has_next) {
-      store_k(cur ^ 1);
-      store_v(cur ^ 1);
-    }
-    __syncthreads();
   }
 
   if (!ww.active) return;
   const TileValid tq = tile_valid(L, ww.qt);
   const int qrow = 32 * rg + l32;
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = halves_sum(l_run);
   const bool real = row_is_real(L, tq, qrow);
   const float inv = (real && lt > 0.0f) ? wmax / (kP8Scale * lt) : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
