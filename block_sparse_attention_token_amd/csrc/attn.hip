@@ -579,6 +579,28 @@ __device__ __forceinline__ float bf_step_mfma(const uint4* kb, const uint4* vb,
   return hi;
 }
 
+// One pipelined step with the PV product one block behind: the score MFMAs
+// of block s+1 and the PV MFMAs of block s-1 (whose P^T operands were packed
+// during the previous step) around the exp2/pack work of block s, so no
+// MFMA of the step waits on the step's own VALU work. Returns the row
+// maximum of block s+1 (taken without its pad mask).
+template <int KVH, int D>
+__device__ __forceinline__ float bf_step_lag(const uint4* kb, const uint4* vb,
+                                             const uint4 (&qf)[D / 16],
+                                             f32x16_t (&snext)[KVH / 32],
+                                             const f32x16_t (&scur)[KVH / 32], float sl2,
+                                             float m_run, float& l_run,
+                                             const uint4 (&pprev)[KVH / 16],
+                                             uint4 (&pcur)[KVH / 16], f32x16_t (&oacc)[D / 32]) {
+  constexpr int MB = KVH / 32, NPS = KVH / 16;
+  bf_scores<KVH, D>(kb, qf, snext);
+  bf_exp_pack<MB, 0, NPS>(scur, sl2, m_run, l_run, pcur);
+  bf_pv<KVH, D, 0, NPS>(vb, pprev, oacc);
+  const float hi = bf_row_max<MB>(snext);
+  interleave_hint<(D / 16) * MB + NPS * (D / 32), 3, 4>();
+  return hi;
+}
+
 // Q^T fragments for query row 32*rg + l32 of tile qt; a negative softmax
 // scale is folded into Q (sign flip) so the softmax only needs a maximum.
 template <int TILE, int D, bool F32IN>
@@ -717,51 +739,80 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
 
   if (shared) {
-    // Pipelined walk. Step s (buffer parity P = s & 1): V(s) sits in V buffer
-    // P, K(s+1) in K buffer P^1; K(s+2) is staged into K buffer P and V(s+1)
-    // into V buffer P^1, both last read before the previous barrier. The row
-    // maximum of block s+1 is taken during step s. At the last step the
-    // scores of a clamped block are computed and never used.
+    // Pipelined walk with the PV product one block behind. Step s (buffer
+    // parity P = s & 1): K(s+1) sits in K buffer P^1 and V(s-1) in V buffer
+    // P^1; K(s+2) is staged into K buffer P and V(s) into V buffer P, both
+    // last read before the previous barrier. The row maximum of block s+1 is
+    // taken during step s. At the last step the scores of a clamped block
+    // are computed and never used. Before the first step V buffer 1 and the P operands
+    // of "block -1" are zero, so the first step's PV product adds nothing.
     f32x16_t s_a[MB], s_b[MB];
+    uint4 pk_a[NPS], pk_b[NPS];
+#pragma unroll
+    for (int i = 0; i < NPS; ++i) pk_b[i] = make_uint4(0u, 0u, 0u, 0u);
     float hi = 0.0f;
     if (steps > 0) {
       io.load_k(rk, block_off(0), tid);
-      io.load_v(rv, block_off(0), tid);
       io.store_k(k_lds[0], tid);
-      io.store_v(v_lds[0], tid);
       io.load_k(rk, block_off(1), tid);
       io.store_k(k_lds[1], tid);
+      for (int i = tid; i < IO::V_LDS; i += THREADS) v_lds[1][i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
       bf_scores<KVH, D>(k_lds[0] + k_lane, qf, s_a);
       hi = bf_row_max<MB>(s_a);
       __syncthreads();                   // K buffer 0 is refilled during step 0
     }
     // `hi` is block s's row maximum taken without its pad mask; a padded
-    // block (rare) is masked and its maximum retaken at the step's start
-    auto step = [&](auto parity, int s, f32x16_t (&scur)[MB],
-                    f32x16_t (&snext)[MB]) __attribute__((always_inline)) {
+    // block (rare) is masked and its maximum retaken at the step's start.
+    // Entering step s, O holds the products of blocks up to s-2 on the scale
+    // of the running maximum before step s-1's update, and P(s-1) is on the
+    // scale after it; step s-1's rescale factor `alpha` is applied to O
+    // first, then the running maximum takes block s.
+    float alpha = 1.0f;
+    bool pending = false;
+    auto rescale_o = [&]() __attribute__((always_inline)) {
+      if (pending) {                     // lanes whose max did not move multiply by 1
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
+      }
+    };
+    auto step = [&](auto parity, int s, f32x16_t (&scur)[MB], f32x16_t (&snext)[MB],
+                    const uint4 (&pprev)[NPS], uint4 (&pcur)[NPS]) __attribute__((always_inline)) {
       constexpr int P = decltype(parity)::value;
       cover(s);
       io.load_k(rk, block_off(s + 2), tid);
-      io.load_v(rv, block_off(s + 1), tid);
+      io.load_v(rv, block_off(s), tid);
+      rescale_o();
       bool full;
       const uint32_t bits = block_bits(s, full);
       if (!full) {
         mask_scores<MB>(scur, bits);
         hi = bf_row_max<MB>(scur);
       }
-      update_max(hi);
-      hi = bf_step_mfma<KVH, D>(k_lds[P ^ 1] + k_lane, v_lds[P] + v_lane, qf, snext, scur, sl2,
-                                m_run, l_run, oacc);
+      alpha = bf_update_max(hi, sl2, kLazyBf16, m_run, l_run);
+      pending = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+      hi = bf_step_lag<KVH, D>(k_lds[P ^ 1] + k_lane, v_lds[P ^ 1] + v_lane, qf, snext, scur,
+                               sl2, m_run, l_run, pprev, pcur, oacc);
       __builtin_amdgcn_sched_barrier(0);  // the staging stores wait for their loads here
       io.store_k(k_lds[P], tid);
-      io.store_v(v_lds[P ^ 1], tid);
+      io.store_v(v_lds[P], tid);
       __syncthreads();
     };
+    // after the last step its rescale and its block's PV product remain;
+    // the last P operands are left in pk_b, the last V block in the buffer
+    // of the last step's parity
     for (int s = 0; s < steps; s += 2) {
-      step(std::integral_constant<int, 0>{}, s, s_a, s_b);
-      if (s + 1 >= steps) break;
-      step(std::integral_constant<int, 1>{}, s + 1, s_b, s_a);
+      step(std::integral_constant<int, 0>{}, s, s_a, s_b, pk_b, pk_a);
+      if (s + 1 >= steps) {
+#pragma unroll
+        for (int i = 0; i < NPS; ++i) pk_b[i] = pk_a[i];
+        break;
+      }
+      step(std::integral_constant<int, 1>{}, s + 1, s_b, s_a, pk_a, pk_b);
+    }
+    if (steps > 0) {
+      rescale_o();
+      bf_pv<KVH, D, 0, NPS>(v_lds[(steps - 1) & 1] + v_lane, pk_b, oacc);
     }
   } else {
     // Plain double-buffered walk over a union: block s+1 is staged while
