@@ -656,7 +656,7 @@ constexpr float kLazyBf16 = 8.0f;
 // Two walks: the pipelined one when every wave owns every block (routed
 // lists, dense lists, query tiles sharing one list), and a plain
 // double-buffered one for unions whose blocks some waves skip.
-template <int TILE, int KVH, int D, int QPW, bool F32IN>
+template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF>
 __global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int WPQ = TILE / 32;         // waves per query tile
@@ -667,8 +667,9 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   using IO = BfTile<KVH, D, THREADS, F32IN>;
   static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
 
-  __shared__ uint4 k_lds[2][IO::K_LDS];
-  __shared__ uint4 v_lds[2][IO::V_LDS];
+  static_assert(NBUF == 2 || NBUF == 4, "two or four K/V buffers");
+  __shared__ uint4 k_lds[NBUF][IO::K_LDS];
+  __shared__ uint4 v_lds[NBUF][IO::V_LDS];
   extern __shared__ int sched[];         // QPW > 1: the schedule (n_tiles entries)
   static_assert(THREADS * 4 <= IO::K_LDS * 16, "scan scratch fits one K buffer");
   static_assert(4096 <= IO::V_LDS * 16, "marks of 4096 tiles fit one V buffer");
@@ -739,28 +740,39 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
 
   if (shared) {
-    // Pipelined walk with the PV product one block behind. Step s (buffer
-    // parity P = s & 1): K(s+1) sits in K buffer P^1 and V(s-1) in V buffer
-    // P^1; K(s+2) is staged into K buffer P and V(s) into V buffer P, both
-    // last read before the previous barrier. The row maximum of block s+1 is
-    // taken during step s. At the last step the scores of a clamped block
-    // are computed and never used. Before the first step V buffer 1 and the P operands
-    // of "block -1" are zero, so the first step's PV product adds nothing.
+    // Pipelined walk with the PV product one block behind, over a ring of
+    // NBUF K and NBUF V buffers (block j in buffer j % NBUF). Step s takes
+    // K(s+1) and V(s-1) from their buffers, and stages K(s+LK) and V(s+LV),
+    // loaded at the step's start, at its end. With NBUF = 2 (LK = 2, LV = 0)
+    // every step ends in a barrier; with NBUF = 4 (LK = 3, LV = 1) only odd
+    // steps do, which still puts a barrier between each store and the first
+    // read of that block, and between the last read of a buffer and the
+    // store that refills it. The row maximum of block s+1 is taken during
+    // step s; at the last steps the scores of a clamped block are computed
+    // and never used. Before the first step the V buffer of "block -1" and
+    // its P operands are zero, so the first step's PV product adds nothing.
+    constexpr int LK = NBUF == 4 ? 3 : 2, LV = NBUF == 4 ? 1 : 0;
     f32x16_t s_a[MB], s_b[MB];
     uint4 pk_a[NPS], pk_b[NPS];
 #pragma unroll
     for (int i = 0; i < NPS; ++i) pk_b[i] = make_uint4(0u, 0u, 0u, 0u);
     float hi = 0.0f;
     if (steps > 0) {
-      io.load_k(rk, block_off(0), tid);
-      io.store_k(k_lds[0], tid);
-      io.load_k(rk, block_off(1), tid);
-      io.store_k(k_lds[1], tid);
-      for (int i = tid; i < IO::V_LDS; i += THREADS) v_lds[1][i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int j = 0; j < LK; ++j) {
+        io.load_k(rk, block_off(j), tid);
+        io.store_k(k_lds[j], tid);
+      }
+#pragma unroll
+      for (int j = 0; j < LV; ++j) {
+        io.load_v(rv, block_off(j), tid);
+        io.store_v(v_lds[j], tid);
+      }
+      for (int i = tid; i < IO::V_LDS; i += THREADS) v_lds[NBUF - 1][i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
       bf_scores<KVH, D>(k_lds[0] + k_lane, qf, s_a);
       hi = bf_row_max<MB>(s_a);
-      __syncthreads();                   // K buffer 0 is refilled during step 0
+      __syncthreads();                   // K buffer 0 is refilled before the next barrier
     }
     // `hi` is block s's row maximum taken without its pad mask; a padded
     // block (rare) is masked and its maximum retaken at the step's start.
@@ -776,12 +788,13 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
         for (int cb = 0; cb < D / 32; ++cb) oacc[cb] *= alpha;
       }
     };
-    auto step = [&](auto parity, int s, f32x16_t (&scur)[MB], f32x16_t (&snext)[MB],
+    // I = s % NBUF; even steps take (s_a, s_b, pk_b, pk_a), odd ones the reverse
+    auto step = [&](auto phase, int s, f32x16_t (&scur)[MB], f32x16_t (&snext)[MB],
                     const uint4 (&pprev)[NPS], uint4 (&pcur)[NPS]) __attribute__((always_inline)) {
-      constexpr int P = decltype(parity)::value;
-      cover(s);
-      io.load_k(rk, block_off(s + 2), tid);
-      io.load_v(rv, block_off(s), tid);
+      constexpr int I = decltype(phase)::value;
+      win.cover(L, ww, sched, len, s / SUB, min(s + LK, steps - 1) / SUB, lane);
+      io.load_k(rk, block_off(s + LK), tid);
+      io.load_v(rv, block_off(s + LV), tid);
       rescale_o();
       bool full;
       const uint32_t bits = block_bits(s, full);
@@ -791,28 +804,42 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
       }
       alpha = bf_update_max(hi, sl2, kLazyBf16, m_run, l_run);
       pending = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-      hi = bf_step_lag<KVH, D>(k_lds[P ^ 1] + k_lane, v_lds[P ^ 1] + v_lane, qf, snext, scur,
-                               sl2, m_run, l_run, pprev, pcur, oacc);
+      hi = bf_step_lag<KVH, D>(k_lds[(I + 1) % NBUF] + k_lane, v_lds[(I + NBUF - 1) % NBUF] + v_lane,
+                               qf, snext, scur, sl2, m_run, l_run, pprev, pcur, oacc);
       __builtin_amdgcn_sched_barrier(0);  // the staging stores wait for their loads here
-      io.store_k(k_lds[P], tid);
-      io.store_v(v_lds[P], tid);
-      __syncthreads();
+      io.store_k(k_lds[(I + LK) % NBUF], tid);
+      io.store_v(v_lds[(I + LV) % NBUF], tid);
+      if (NBUF == 2 || (I & 1)) __syncthreads();
     };
     // after the last step its rescale and its block's PV product remain;
-    // the last P operands are left in pk_b, the last V block in the buffer
-    // of the last step's parity
-    for (int s = 0; s < steps; s += 2) {
-      step(std::integral_constant<int, 0>{}, s, s_a, s_b, pk_b, pk_a);
+    // the last P operands are left in pk_b
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    for (int s = 0; s < steps; s += NBUF) {
+      step(C0{}, s, s_a, s_b, pk_b, pk_a);
       if (s + 1 >= steps) {
 #pragma unroll
         for (int i = 0; i < NPS; ++i) pk_b[i] = pk_a[i];
         break;
       }
-      step(std::integral_constant<int, 1>{}, s + 1, s_b, s_a, pk_a, pk_b);
+      step(C1{}, s + 1, s_b, s_a, pk_a, pk_b);
+      if constexpr (NBUF == 4) {
+        if (s + 2 >= steps) break;
+        step(C2{}, s + 2, s_a, s_b, pk_b, pk_a);
+        if (s + 3 >= steps) {
+#pragma unroll
+          for (int i = 0; i < NPS; ++i) pk_b[i] = pk_a[i];
+          break;
+        }
+        step(C3{}, s + 3, s_b, s_a, pk_a, pk_b);
+      }
     }
     if (steps > 0) {
+      __syncthreads();                   // the last V block is visible to every wave
       rescale_o();
-      bf_pv<KVH, D, 0, NPS>(v_lds[(steps - 1) & 1] + v_lane, pk_b, oacc);
+      bf_pv<KVH, D, 0, NPS>(v_lds[(steps - 1) % NBUF] + v_lane, pk_b, oacc);
     }
   } else {
     // Plain double-buffered walk over a union: block s+1 is staged while
@@ -1205,11 +1232,11 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 }
 
 // ---------------------------------------------------------------------------
-template <int TILE, int KVH, int D, int QPW, bool F32IN>
+template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF = 2>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN>), dim3(n_work),
+  hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF>), dim3(n_work),
                      dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
@@ -1225,7 +1252,8 @@ hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
 template <int TILE, int D, bool F32IN>
 hipError_t launch_bf16_shape(const DevLayout& L, const AttnArgs& a, bool grouped, hipStream_t s) {
   if constexpr (TILE == 64) {
-    return grouped ? launch_bf16<64, 64, D, 4, F32IN>(L, a, s) : launch_bf16<64, 32, D, 1, F32IN>(L, a, s);
+    return grouped ? launch_bf16<64, 64, D, 4, F32IN, 4>(L, a, s)
+                   : launch_bf16<64, 32, D, 1, F32IN>(L, a, s);
   } else {
     return grouped ? launch_bf16<32, 32, D, 4, F32IN>(L, a, s) : launch_bf16<32, 32, D, 1, F32IN>(L, a, s);
   }

@@ -260,3 +260,39 @@ def test_list_modes_agree():
     torch.cuda.synchronize()
     mae, rl2 = errors(o1.float().cpu().numpy(), o2.float().cpu().numpy().astype(np.float64))
     assert mae <= 1e-2 and rl2 <= 5e-3
+
+
+def test_shared_walk_list_lengths():
+    """Every list length from 1 to 9, and a few past the buffer ring, on the
+    walk taken when a workgroup's four query tiles share one list.
+
+    Groups of four consecutive query tiles get one list of random key tiles
+    (some of them padded at the grid's edge); the group's length cycles
+    through 1..9, 13..17, so the walk ends at every position of its unrolled
+    loop and at every phase of its buffer ring."""
+    cfg = CONFIGS["window_480p"]
+    olay, blay = layouts(cfg, heads=2)
+    rng = np.random.default_rng(12)
+    from synth import round_to_bf16
+    q, k, v = (round_to_bf16(rng.standard_normal((1, olay.n_tokens, 2, 128)).astype(np.float32))
+               for _ in range(3))
+    lengths = [1, 2, 3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17]
+    lists = []
+    for g in range((olay.n_tiles + 3) // 4):
+        n = lengths[g % len(lengths)]
+        row = sorted(rng.choice(olay.n_tiles, n, replace=False).tolist())
+        lists += [row] * 4
+    lists = lists[:olay.n_tiles]
+    idx, cnt = table_from_lists(lists)
+    announce("attn shared walk, list lengths 1..17")
+    qd, qo = _tiled(cfg, olay, blay, q)
+    kd, ko = _tiled(cfg, olay, blay, k)
+    vd, vo = _tiled(cfg, olay, blay, v)
+    di, dc = lists_to_device(idx, cnt)
+    out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+    torch.cuda.synchronize()
+    # one query tile of every group whose length is below 18, both heads
+    items = [(0, h, 4 * g + (g % 4)) for g in range(len(lengths) * 2) for h in range(2)]
+    items = [it for it in items if it[2] < olay.n_tiles]
+    O, L = OA.attention(qo, ko, vo, olay, OA.shared_lists(lists), 1.0 / math.sqrt(128), items=items)
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
