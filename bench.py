@@ -151,7 +151,34 @@ def build_workload(name, torch, np, vsa):
         per_layer = 4.0 * d * float(info.n_tokens) ** 2 * cfg.heads
         return per_layer * (cfg.dense_every or 1)
 
-    state.update(step=step, flops=flops, dense_equiv=dense_equiv, nat=nat)
+    def head_spread():
+        """Routed lists: max over heads of a head's visited pairs / the mean over heads."""
+        if "cnt" not in state:
+            return None
+        per_head = state["cnt"].reshape(-1, cfg.heads, n).sum(dim=(0, 2)).double()
+        return round(float(per_head.max() / per_head.mean()), 3)
+
+    def cold_attn(reps=3, scratch_mb=512):
+        """Sparse-layer attention with a scratch write of scratch_mb MB before each launch
+        (evicts the 256 MB MALL and the L2s); returns the mean launch time in ms."""
+        if cfg.mask not in ("window", "skiparse"):
+            return None
+        tq, tk, tv = (vsa.tile_permute(lay, x) for x in nat)
+        scratch = torch.empty(scratch_mb << 20, dtype=torch.uint8, device="cuda")
+        total = 0.0
+        for i in range(reps):
+            scratch.fill_(i + 1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vsa.block_sparse_attn_fwd(lay, tq, tk, tv, kv_idx, kv_cnt)
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        del scratch, tq, tk, tv
+        return total / reps
+
+    state.update(step=step, flops=flops, dense_equiv=dense_equiv, nat=nat, head_spread=head_spread,
+                 cold_attn=cold_attn)
     return state
 
 
@@ -252,6 +279,8 @@ def main():
     ap.add_argument("--workload", default="skiparse_768p")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mall-cold", action="store_true",
+                    help="skip the attention launches timed after a 512 MB scratch write")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -295,6 +324,12 @@ def main():
         if k in kernels:
             kernels[k]["tflops"] = f / (kernels[k]["ms_avg"] * 1e-3) / 1e12
             kernels[k]["frac_of_peak"] = kernels[k]["tflops"] / peak
+    cold_ms = None if args.no_mall_cold else head["cold_attn"]()
+    if cold_ms is not None:
+        kernels["attn_mall_cold"] = {
+            "ms_avg": cold_ms, "note": "sparse layer, 512 MB scratch write before each launch",
+            "tflops": per_launch["attn"] / (cold_ms * 1e-3) / 1e12,
+            "frac_of_peak": per_launch["attn"] / (cold_ms * 1e-3) / 1e12 / peak}
     info = head["info"]
     perm_bytes = 2 * info.n_tokens * cfg.heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     if "permute" in kernels:
@@ -362,6 +397,12 @@ def main():
                 "peak_tflops": pk,
                 "kernels_ms": {k: round(tm.total[k] / tm.count[k], 4) for k in tm.total},
             }
+            if st["cfg"].fp8:
+                per[name]["attn_frac_of_bf16_peak"] = round(
+                    pl["attn"] / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            spread = st["head_spread"]()
+            if spread is not None:
+                per[name]["head_pairs_max_over_mean"] = spread
             log(f"{name}: {per[name]}")
             del st
             torch.cuda.empty_cache()
