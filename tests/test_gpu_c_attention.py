@@ -296,3 +296,48 @@ def test_shared_walk_list_lengths():
     items = [it for it in items if it[2] < olay.n_tiles]
     O, L = OA.attention(qo, ko, vo, olay, OA.shared_lists(lists), 1.0 / math.sqrt(128), items=items)
     _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), L, olay, items)
+
+
+@pytest.mark.parametrize("tile,d,dtype", [((4, 4, 4), 64, "bf16"), ((2, 4, 4), 128, "bf16"),
+                                          ((2, 4, 4), 64, "bf16"), ((4, 4, 4), 128, "f32"),
+                                          ((4, 4, 4), 64, "f32"), ((2, 4, 4), 128, "f32")])
+@pytest.mark.parametrize("mode", ["shared", "routed"])
+def test_tile_and_head_dim_shapes(tile, d, dtype, mode):
+    """Every tile size / head size / input type the kernels take, on a ragged
+    grid, with shared window lists (query tiles walking one union) and with
+    routed per-head lists of random length (empty lists included)."""
+    T, H, W, heads = 7, 10, 13, 2
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=tile)
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=tile)
+    rng = np.random.default_rng(1200 + 100 * tile[0] + d + 7 * (dtype == "f32") + 3 * (mode == "routed"))
+    from synth import round_to_bf16
+    q, k, v = (rng.standard_normal((1, olay.n_tokens, heads, d)).astype(np.float32) for _ in range(3))
+    if dtype == "bf16":
+        q, k, v = (round_to_bf16(x) for x in (q, k, v))
+    announce(f"attn shapes tile={tile} d={d} {dtype} {mode}")
+    qd, qo = (vsa.tile_permute(blay, to_device(q, dtype)), OL.permute(q, olay).astype(np.float64))
+    kd, ko = (vsa.tile_permute(blay, to_device(k, dtype)), OL.permute(k, olay).astype(np.float64))
+    vd, vo = (vsa.tile_permute(blay, to_device(v, dtype)), OL.permute(v, olay).astype(np.float64))
+    n = olay.n_tiles
+    if mode == "shared":
+        lists = OM.window_lists(olay, 1, 1, 1)
+        idx, cnt = table_from_lists(lists)
+        lists_fn = OA.shared_lists(lists)
+    else:
+        width = max(1, n // 2)
+        idx = np.full((1, heads, n, width), -1, dtype=np.int32)
+        cnt = np.zeros((1, heads, n), dtype=np.int32)
+        for h in range(heads):
+            for t in range(n):
+                c = int(rng.integers(0, width + 1))
+                idx[0, h, t, :c] = np.sort(rng.choice(n, c, replace=False))
+                cnt[0, h, t] = c
+        lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    di, dc = lists_to_device(idx, cnt)
+    out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+    torch.cuda.synchronize()
+    O, Lr = OA.attention(qo, ko, vo, olay, lists_fn, 1.0 / math.sqrt(d))
+    items = [(0, h, t) for h in range(heads) for t in range(n)]
+    # fp32 inputs are rounded to bf16 for the products: the lse bound grows with d
+    _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), Lr, olay, items,
+             lse_gate=(2.5e-2 if d == 64 else 5e-2) if dtype == "f32" else 2e-3)
