@@ -341,3 +341,61 @@ def test_tile_and_head_dim_shapes(tile, d, dtype, mode):
     # fp32 inputs are rounded to bf16 for the products: the lse bound grows with d
     _compare(out.float().cpu().numpy(), O, lse.cpu().numpy(), Lr, olay, items,
              lse_gate=(2.5e-2 if d == 64 else 5e-2) if dtype == "f32" else 2e-3)
+
+
+@pytest.mark.parametrize("mode", ["window_union", "shared_lengths", "routed"])
+def test_fp8_walks(mode):
+    """fp8 attention on every walk: unions of window lists (plain walk), one
+    list per group of four query tiles with lengths 1..9 and 13..17
+    (pipelined walk ending at every position), and routed per-head lists with
+    empty ones; gated against the oracle of the fp8 method."""
+    T, H, W, heads, d = 9, 14, 22, 2, 128
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4))
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4))
+    rng = np.random.default_rng({"window_union": 1301, "shared_lengths": 1302, "routed": 1303}[mode])
+    from synth import round_to_bf16
+    x = [round_to_bf16(rng.standard_normal((1, olay.n_tokens, heads, d)).astype(np.float32))
+         for _ in range(3)]
+    announce(f"attn fp8 {mode}")
+    n = olay.n_tiles
+    if mode == "window_union":
+        lists = OM.window_lists(olay, 1, 1, 1)
+    elif mode == "shared_lengths":
+        lengths = [1, 2, 3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17]
+        lists = []
+        for g in range((n + 3) // 4):
+            row = sorted(rng.choice(n, min(lengths[g % len(lengths)], n), replace=False).tolist())
+            lists += [row] * 4
+        lists = lists[:n]
+    if mode == "routed":
+        width = n // 2
+        idx = np.full((1, heads, n, width), -1, dtype=np.int32)
+        cnt = np.zeros((1, heads, n), dtype=np.int32)
+        for h in range(heads):
+            for t in range(n):
+                c = int(rng.integers(0, width + 1))
+                idx[0, h, t, :c] = np.sort(rng.choice(n, c, replace=False))
+                cnt[0, h, t] = c
+        lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    else:
+        idx, cnt = table_from_lists(lists)
+        lists_fn = OA.shared_lists(lists)
+    tiled = [vsa.tile_permute(blay, to_device(a, "bf16")) for a in x]
+    (qc, qs), (kc, ks), (vc, vs) = (vsa.quant_fp8_tiles(blay, t) for t in tiled)
+    di, dc = lists_to_device(idx, cnt)
+    out, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs))
+    torch.cuda.synchronize()
+    xo = [OL.permute(a, olay).astype(np.float32) for a in x]
+    deq = [OF.dequantize_tiles(*OF.quantize_tiles(a, olay), olay) for a in xo]
+    O, _ = OA.attention(*deq, olay, lists_fn, 1.0 / math.sqrt(d))
+    og = out.float().cpu().numpy()
+    C = olay.tile_tokens
+    items = [(0, h, t) for h in range(heads) for t in range(n)]
+    g = np.concatenate([og[0, h, t * C:(t + 1) * C] for _, h, t in items])
+    r = np.concatenate([O[0, h, t * C:(t + 1) * C] for _, h, t in items])
+    mae, rl2 = errors(g, r)
+    print(f"fp8 {mode}: max_abs={mae:.3e} rel_l2={rl2:.3e}")
+    assert rl2 <= REL_L2_FP8
+    empty = [(h, t) for h in range(heads) for t in range(n) if not lists_fn(0, h, t)]
+    for h, t in empty:
+        assert np.all(og[0, h, t * C:(t + 1) * C] == 0)
