@@ -399,3 +399,54 @@ def test_fp8_walks(mode):
     empty = [(h, t) for h in range(heads) for t in range(n) if not lists_fn(0, h, t)]
     for h, t in empty:
         assert np.all(og[0, h, t * C:(t + 1) * C] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("mode", ["shared", "routed"])
+@pytest.mark.parametrize("scale", [0.17, -0.3, 0.0])
+def test_batch_and_softmax_scales(dtype, mode, scale):
+    """Batch of two, a softmax scale other than 1/sqrt(d), a negative one
+    (folded into Q) and zero (uniform weights over the key set)."""
+    T, H, W, heads, d, B = 5, 9, 10, 2, 128, 2
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4), batch=B)
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4), batch=B)
+    rng = np.random.default_rng(1400 + int(1000 * scale) + 10 * (mode == "routed") + (dtype == "fp8"))
+    from synth import round_to_bf16
+    x = [round_to_bf16(rng.standard_normal((B, olay.n_tokens, heads, d)).astype(np.float32))
+         for _ in range(3)]
+    announce(f"attn batch 2 scale {scale} {mode} {dtype}")
+    n = olay.n_tiles
+    if mode == "shared":
+        lists = OM.window_lists(olay, 1, 1, 1)
+        idx, cnt = table_from_lists(lists)
+        lists_fn = OA.shared_lists(lists)
+    else:
+        width = max(1, n // 2)
+        idx = np.full((B, heads, n, width), -1, dtype=np.int32)
+        cnt = np.zeros((B, heads, n), dtype=np.int32)
+        for b in range(B):
+            for h in range(heads):
+                for t in range(n):
+                    c = int(rng.integers(1, width + 1))
+                    idx[b, h, t, :c] = np.sort(rng.choice(n, c, replace=False))
+                    cnt[b, h, t] = c
+        lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    tiled = [vsa.tile_permute(blay, to_device(a, "bf16")) for a in x]
+    xo = [OL.permute(a, olay).astype(np.float64) for a in x]
+    di, dc = lists_to_device(idx, cnt)
+    if dtype == "fp8":
+        (qc, qs), (kc, ks), (vc, vs) = (vsa.quant_fp8_tiles(blay, t) for t in tiled)
+        out, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, softmax_scale=scale,
+                                           scales=(qs, ks, vs))
+        xo = [OF.dequantize_tiles(*OF.quantize_tiles(a.astype(np.float32), olay), olay) for a in xo]
+    else:
+        out, _ = vsa.block_sparse_attn_fwd(blay, *tiled, di, dc, softmax_scale=scale)
+    torch.cuda.synchronize()
+    O, _ = OA.attention(*xo, olay, lists_fn, scale)
+    og = out.float().cpu().numpy()
+    mae, rl2 = errors(og, np.nan_to_num(O))
+    print(f"scale {scale} {mode} {dtype}: max_abs={mae:.3e} rel_l2={rl2:.3e}")
+    if dtype == "fp8":
+        assert rl2 <= REL_L2_FP8
+    else:
+        assert mae <= MAX_ABS and rl2 <= REL_L2
