@@ -54,19 +54,6 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {   // hi16(
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Scheduling hint for a block of N LDS operand reads feeding N MFMAs: keep
-// PRE reads in flight ahead of the MFMA that consumes them, then alternate.
-template <int N, int PRE>
-__device__ __forceinline__ void reads_ahead_of_mfma() {
-  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);          // DS reads
-#pragma unroll
-  for (int i = 0; i < N - PRE; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one DS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
-}
-
 // Buffer-resource loads: the base of one (b, head) slice of a tensor sits in
 // SGPRs and each load takes a 32-bit byte offset (VGPR part + SGPR part), so
 // tile loads need no 64-bit address registers; offsets past num_records read
@@ -181,41 +168,6 @@ __device__ int build_schedule(const DevLayout& L, const WaveWork& w, uint32_t* m
   return len;
 }
 
-// Schedule entries are the same for every lane of a wave: readfirstlane
-// moves them to scalar registers so the branches on them are scalar.
-template <int QPW>
-__device__ __forceinline__ int sched_tile(const int* sched, const WaveWork& w, int s, int n_tiles) {
-  if constexpr (QPW > 1) return __builtin_amdgcn_readfirstlane(sched[s]) & 0xFFFFFF;
-  else return w.list ? min(max(__builtin_amdgcn_readfirstlane(w.list[s]), 0), n_tiles - 1) : s;
-}
-template <int QPW>
-__device__ __forceinline__ bool sched_mine(const int* sched, int s, int slot) {
-  if constexpr (QPW > 1) return (__builtin_amdgcn_readfirstlane(sched[s]) >> (24 + slot)) & 1;
-  else return true;
-}
-
-// Bit (16*mb + r) set iff the kv token this lane holds in register r of S^T
-// block mb (token tok0 + 32*mb + 8*(r/4) + 4*half + r%4 of the tile) is a
-// real token. Wave-uniform `full` short-cuts the common case.
-template <int MB>
-__device__ __forceinline__ uint32_t kv_valid_bits(const DevLayout& L, int tile, int tok0, int lane,
-                                                  int half, bool& full) {
-  const TileValid tv = tile_valid(L, tile);
-  bool f = tv.full;
-  if (!f && L.kind == 1) f = tok0 + 32 * MB <= tv.vlen;   // Skiparse: pads only at the tail
-  full = f;
-  if (f) return 0xFFFFFFFFu;
-  const bool v = lane < 32 * MB && row_is_real(L, tv, tok0 + lane);
-  const unsigned long long vm = __ballot(v);
-  uint32_t m = 0;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      m |= (uint32_t)((vm >> (32 * mb + 8 * g + 4 * half)) & 0xFull) << (16 * mb + 4 * g);
-  return m;
-}
-
 // Bit (16*mb + r) set iff the kv token this lane holds in register r of S^T
 // block mb (token tok0 + 32*mb + 8*(r/4) + 4*half + r%4 of the tile) is a
 // real token, for a block known to hold padding.
@@ -279,53 +231,6 @@ struct SchedWindow {
     return __builtin_amdgcn_readlane(flags_v, e - base);
   }
 };
-
-// Online-softmax step on one 32-row query group: scores s (raw dot products,
-// MB blocks of 16 per lane) become p = exp2(s * sl2 - m_run), in place.
-// sl2 >= 0 (a negative softmax scale is folded into Q by the caller).
-// MASKED: bit (16*mb + r) of `bits` says whether that key is real; masked
-// keys get p = 0. Returns the factor O must be multiplied by (1 when m_run
-// did not move).
-template <int MB, bool MASKED>
-__device__ __forceinline__ float softmax_core(f32x16_t (&s)[MB], uint32_t bits, float sl2,
-                                              float lazy, float& m_run, float& l_run) {
-  float hi = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if constexpr (MASKED) hi = fmaxf(hi, ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY);
-      else hi = fmaxf(hi, s[mb][r]);
-    }
-  hi = fmaxf(hi, __shfl_xor(hi, 32));
-  const float mx = hi * sl2;                             // max over the tile of s * sl2
-  float alpha = 1.0f;
-  if (mx > m_run + lazy) {
-    alpha = fast_exp2(m_run - mx);                       // 0 on the first tile
-    m_run = mx;
-    l_run *= alpha;
-  }
-  const float nm = -m_run;
-  float psum = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(fmaf(s[mb][r], sl2, nm));
-      if constexpr (MASKED) p = ((bits >> (16 * mb + r)) & 1u) ? p : 0.0f;
-      s[mb][r] = p;
-      psum += p;
-    }
-  l_run += psum;
-  return alpha;
-}
-
-template <int MB>
-__device__ __forceinline__ float softmax_step(f32x16_t (&s)[MB], bool full, uint32_t bits,
-                                              float sl2, float lazy, float& m_run, float& l_run) {
-  if (full) return softmax_core<MB, false>(s, bits, sl2, lazy, m_run, l_run);
-  return softmax_core<MB, true>(s, bits, sl2, lazy, m_run, l_run);
-}
 
 // ---------------------------------------------------------------------------
 // bf16 kernels. One wave owns 32 query rows (a 64-row query tile takes two
@@ -539,14 +444,6 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
-// Row max of the current block and the lazy running-max update; returns
-// the factor O must be multiplied by before this block's PV products.
-template <int KVH>
-__device__ __forceinline__ float bf_block_max(const f32x16_t (&scur)[KVH / 32], float sl2,
-                                              float lazy, float& m_run, float& l_run) {
-  return bf_update_max(bf_row_max<KVH / 32>(scur), sl2, lazy, m_run, l_run);
-}
-
 // exp2/pack and PV products of the current block, each 16-key group of P
 // feeding its MFMAs as soon as it is packed
 template <int KVH, int D>
@@ -559,24 +456,6 @@ __device__ __forceinline__ void bf_block_pv(const uint4* vb, const f32x16_t (&sc
   bf_pv<KVH, D, 0, NPS / 2>(vb, pk, oacc);
   bf_exp_pack<MB, NPS / 2, NPS>(scur, sl2, m_run, l_run, pk);
   bf_pv<KVH, D, NPS / 2, NPS>(vb, pk, oacc);
-}
-
-// One pipelined step: the score MFMAs of the next block and the PV MFMAs of
-// the current one, with the current block's exp2/pack work and the next
-// block's row maximum (taken without its pad mask) interleaved between them.
-// Returns that row maximum.
-template <int KVH, int D>
-__device__ __forceinline__ float bf_step_mfma(const uint4* kb, const uint4* vb,
-                                              const uint4 (&qf)[D / 16],
-                                              f32x16_t (&snext)[KVH / 32],
-                                              const f32x16_t (&scur)[KVH / 32], float sl2,
-                                              float m_run, float& l_run,
-                                              f32x16_t (&oacc)[D / 32]) {
-  bf_scores<KVH, D>(kb, qf, snext);
-  bf_block_pv<KVH, D>(vb, scur, sl2, m_run, l_run, oacc);
-  const float hi = bf_row_max<KVH / 32>(snext);
-  interleave_hint<(D / 16) * (KVH / 32) + (KVH / 16) * (D / 32), 3, 4>();
-  return hi;
 }
 
 // One pipelined step with the PV product one block behind: the score MFMAs
