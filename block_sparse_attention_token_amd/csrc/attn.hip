@@ -99,7 +99,10 @@ template <int QPW, int WPQ>
 __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs& a, int n_work,
                                               int wave) {
   WaveWork w;
-  const int item = xcd_remap(blockIdx.x, n_work);
+  // shared lists: contiguous ranges (query tiles sharing K/V share an L2);
+  // per-head lists: chunks dealt round the XCDs (per-head work differs)
+  const int item = a.kv_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
+                                                 : xcd_remap(blockIdx.x, n_work);
   const int wg_per_bh = (L.n_tiles + QPW - 1) / QPW;
   w.bh = item / wg_per_bh;
   w.slot = wave / WPQ;

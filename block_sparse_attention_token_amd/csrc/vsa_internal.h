@@ -108,6 +108,18 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return x * q + min(x, r) + j;
 }
 
+// Workgroup index -> work item in chunks of G consecutive items dealt to the
+// XCDs in turn, so that every XCD gets a slice of every head: for per-head
+// routed lists, whose lengths differ from head to head, this keeps the XCDs
+// equally loaded; neighbouring query tiles still share an L2 within a chunk.
+// The tail that does not fill a round of 8 chunks is split contiguously.
+__device__ __forceinline__ int xcd_chunked(int i, int n, int G) {
+  const int R = 8 * G, full = n / R;
+  const int x = i & 7, k = i >> 3;
+  if (k < full * G) return ((k / G) * 8 + x) * G + (k % G);
+  return full * R + xcd_remap(i - full * R, n - full * R);
+}
+
 // ----- launchers (return hipError_t of the launch) -----
 hipError_t launch_permute(const DevLayout& L, int esize, const void* src, void* dst, int inverse,
                           hipStream_t s);
