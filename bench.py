@@ -122,10 +122,11 @@ def build_workload(name, torch, np, vsa):
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(
                 lay, tq, tk, top_p=cfg.top_p, k_floor=cfg.k_floor))
             state["cnt"] = cnt
-            (qc, qs), (kc, ks), (vc, vs) = (timer.run("quant", lambda x=x: vsa.quant_fp8_tiles(lay, x))
-                                           for x in (tq, tk, tv))
+            # V quantised straight into the fp8 P.V operand layout
+            (qc, qs), (kc, ks), (vc, vs) = (timer.run("quant", lambda x=x, vop=vop: vsa.quant_fp8_tiles(
+                lay, x, v_operand=vop)) for x, vop in ((tq, False), (tk, False), (tv, True)))
             out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(
-                lay, qc, kc, vc, idx, cnt, scales=(qs, ks, vs)))
+                lay, qc, kc, vc, idx, cnt, scales=(qs, ks, vs), v_operand=True))
         timer.run("unpermute", lambda: vsa.tile_permute(lay, out, inverse=True))
 
     def step(timer):

@@ -20,13 +20,13 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_SKIPARSE2D, VSA_TILE3D,
-                   VsaError, VsaLayout, VsaLayoutInfo, check, lib)
+from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, VSA_SKIPARSE2D,
+                   VSA_TILE3D, VsaError, VsaLayout, VsaLayoutInfo, check, lib)
 
 __all__ = [
     "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
     "quant_fp8_tiles", "block_sparse_attn_fwd", "VsaError", "EXPORTED",
-    "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_TILE3D", "VSA_SKIPARSE2D",
+    "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
 ]
 
 
@@ -135,15 +135,19 @@ def build_mask_topk(lay: Layout, q_tiled: torch.Tensor, k_tiled: torch.Tensor,
     return kv_idx, kv_cnt, scores
 
 
-def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None):
-    """Per-tile e4m3 codes (uint8, same shape) and scales [B, heads, n_tiles] (vsa_quant_fp8_tiles)."""
+def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None, v_operand: bool = False):
+    """Per-tile e4m3 codes (uint8, same shape) and scales [B, heads, n_tiles].
+
+    vsa_quant_fp8_tiles, or with ``v_operand`` vsa_quant_fp8_tiles_v (each
+    tile's codes channel-major in the fp8 P.V operand order, for V).
+    """
     info = layout_info(lay)
     codes = torch.empty(x_tiled.shape, dtype=torch.uint8, device=x_tiled.device)
     scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32,
                          device=x_tiled.device)
     c = lay.c()
-    check(lib().vsa_quant_fp8_tiles(ctypes.byref(c), _ptr(x_tiled), _ptr(codes), _ptr(scales),
-                                    _stream(stream)))
+    fn = lib().vsa_quant_fp8_tiles_v if v_operand else lib().vsa_quant_fp8_tiles
+    check(fn(ctypes.byref(c), _ptr(x_tiled), _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
 
@@ -153,11 +157,12 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
                           softmax_scale: Optional[float] = None,
                           scales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                           want_lse: bool = False, out: Optional[torch.Tensor] = None,
-                          lse: Optional[torch.Tensor] = None, stream=None):
+                          lse: Optional[torch.Tensor] = None, stream=None, v_operand: bool = False):
     """Block-sparse attention forward (vsa_block_sparse_attn_fwd).
 
     q/k/v tiled; float32 -> float32 out, bfloat16 -> bfloat16 out, uint8 e4m3
-    codes (with ``scales`` = (q_scale, k_scale, v_scale)) -> bfloat16 out.
+    codes (with ``scales`` = (q_scale, k_scale, v_scale)) -> bfloat16 out;
+    ``v_operand``: v holds codes from quant_fp8_tiles(..., v_operand=True).
     kv_idx 2-D [n_tiles, max_kv] = one shared table; 4-D [B, heads, n_tiles,
     max_kv] = per-(b, head) lists; None = dense. Returns (out, lse or None).
     """
@@ -168,6 +173,10 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
         dtype, odt = VSA_FP8_E4M3, torch.bfloat16
         if scales is None:
             raise ValueError("fp8 codes need (q_scale, k_scale, v_scale)")
+        if v_operand:
+            dtype = VSA_FP8_E4M3_VOP
+    elif v_operand:
+        raise ValueError("v_operand applies to fp8 codes only")
     else:
         dtype, odt = _DT.get(q.dtype, -1), q.dtype
     if out is None:

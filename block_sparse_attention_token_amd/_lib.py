@@ -22,14 +22,15 @@ VSA_ERR_HIP = 4
 VSA_F32 = 0
 VSA_BF16 = 1
 VSA_FP8_E4M3 = 2
+VSA_FP8_E4M3_VOP = 3
 
 VSA_TILE3D = 0
 VSA_SKIPARSE2D = 1
 
 EXPORTED = (
     "vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window", "vsa_build_mask_topk",
-    "vsa_build_mask_topk_workspace", "vsa_quant_fp8_tiles", "vsa_block_sparse_attn_fwd",
-    "vsa_status_string", "vsa_last_error", "vsa_version",
+    "vsa_build_mask_topk_workspace", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
+    "vsa_block_sparse_attn_fwd", "vsa_status_string", "vsa_last_error", "vsa_version",
 )
 
 
@@ -75,9 +76,11 @@ def lib() -> ctypes.CDLL:
     L.vsa_build_mask_topk_workspace.argtypes = [LP]
     L.vsa_build_mask_topk_workspace.restype = SZ
     L.vsa_quant_fp8_tiles.argtypes = [LP, P, P, P, P]
+    L.vsa_quant_fp8_tiles_v.argtypes = [LP, P, P, P, P]
     L.vsa_block_sparse_attn_fwd.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, F32, P, P, P]
     for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window",
-                 "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_block_sparse_attn_fwd"):
+                 "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
+                 "vsa_block_sparse_attn_fwd"):
         getattr(L, name).restype = I32
     L.vsa_status_string.argtypes = [I32]
     L.vsa_status_string.restype = ctypes.c_char_p

@@ -797,8 +797,10 @@ __device__ __forceinline__ i32x8_t cat8(uint4 x, uint4 y) {
 
 // Register staging of an fp8 K/V tile and its stores into LDS (K row-major,
 // V transposed to V^T rows in the token order above, from 4-token x
-// 16-channel pieces).
-template <int THREADS>
+// 16-channel pieces). VOP: V codes arrive already in that V^T order (the
+// P.V operand layout written by the V-operand quantiser), so they are
+// copied row by row like K, with no byte permutes.
+template <int THREADS, bool VOP = false>
 struct F8Tile {
   static constexpr int TILE = 64, D = 128;
   static constexpr int K_PER_T = TILE * D / 16 / THREADS;   // 16-code chunks per thread
@@ -820,8 +822,15 @@ struct F8Tile {
       k_lds[(c >> 3) * kK8Stride + (c & 7)] = kreg[i];
     }
   }
+  static constexpr int VOP_PER_T = D * TILE / 16 / THREADS;    // 16-byte V^T chunks per thread
+  static_assert(!VOP || VOP_PER_T <= 4 * V_PER_T, "V^T staging fits the V registers");
   // piece u: tokens 4*(u % 16) .. +3 x channels 16*(u / 16) .. +15
   __device__ __forceinline__ void load_v(rsrc_t rv, uint32_t tile_off, int tid) {
+    if constexpr (VOP) {     // chunk c: V^T row c / 4 (a channel), bytes 16 (c % 4) ..
+#pragma unroll
+      for (int i = 0; i < VOP_PER_T; ++i) vreg[i / 4][i % 4] = bload(rv, tid * 16, tile_off + i * THREADS * 16);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
@@ -835,6 +844,14 @@ struct F8Tile {
   // tokens t0..t0+3 sit at V^T byte positions p0..p0+3 with
   // p0 = 32*h + 16*(t0/32) + 4*((t0/8)%4), h = (t0/4)%2
   __device__ __forceinline__ void store_v(uint4* v_lds, int tid) const {
+    if constexpr (VOP) {
+#pragma unroll
+      for (int i = 0; i < VOP_PER_T; ++i) {
+        const int c = tid + i * THREADS;
+        v_lds[(c >> 2) * kV8Stride + (c & 3)] = vreg[i / 4][i % 4];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
@@ -900,12 +917,12 @@ __device__ __forceinline__ void f8_pv(const uint4* vb, const i32x8_t& pk, f32x16
   }
 }
 
-template <int QPW>
+template <int QPW, bool VOP = false>
 __global__ __launch_bounds__(128 * QPW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int TILE = 64, D = 128, WPQ = 2, MB = 2, CB = 4, SUB = 1, KVH = 64;
   constexpr int THREADS = 64 * QPW * WPQ;
-  using IO = F8Tile<THREADS>;
+  using IO = F8Tile<THREADS, VOP>;
 
   __shared__ uint4 k_lds[2][IO::K_LDS];               // 64 rows x (128 + 16) B
   __shared__ uint4 v_lds[2][IO::V_LDS];               // V^T: 128 rows x (64 + 16) B
@@ -1123,11 +1140,11 @@ hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int QPW>
+template <int QPW, bool VOP = false>
 hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_fp8_kernel<QPW>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
+  hipLaunchKernelGGL((attn_fp8_kernel<QPW, VOP>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
@@ -1148,6 +1165,10 @@ hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStre
   // tiles, so four query tiles walk their union together. Routed lists: one
   // wave per query tile.
   const bool grouped = (a.kv_idx == nullptr || a.list_mode == 0) && L.n_tiles <= 4096;
+  if (dtype == 3) {   // e4m3 with V codes in the P.V operand layout
+    if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
+    return grouped ? launch_fp8<4, true>(L, a, s) : launch_fp8<1, true>(L, a, s);
+  }
   if (dtype == 2) {
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
     return grouped ? launch_fp8<4>(L, a, s) : launch_fp8<1>(L, a, s);

@@ -37,6 +37,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   return code | sign;
 }
 
+// VOP: 64-token tiles of d = 128 only. The tile's codes are gathered in LDS
+// and written channel-major, each 64-byte channel row holding the tile's
+// tokens in the order the fp8 P.V product takes them: position
+// p = 32 h + 16 A + 4 B + r holds token t = 32 A + 8 B + 4 h + r
+// (h, r in 0..1 and 0..3, A in 0..1, B in 0..3).
+template <bool VOP>
 __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint4* __restrict__ x,
                                                          uint2* __restrict__ codes,
                                                          float* __restrict__ scales) {
@@ -75,33 +81,59 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
     scales[(long long)(b * L.heads + head) * L.n_tiles + tile] =
         (a > 0.0f) ? __fdiv_rn(a, 448.0f) : 0.0f;
   }
+  __shared__ uint2 tl[VOP ? 64 * 128 / 8 : 1];       // VOP: the tile's codes, token-major
   for (int idx = threadIdx.x; idx < total; idx += kThreads) {
     const int r = idx / chunks;
     const long long off = (row0 + r) * chunks + (idx - r * chunks);
-    if (a == 0.0f || !row_is_real(L, tv, r)) {
-      codes[off] = make_uint2(0u, 0u);
-      continue;
-    }
-    const uint4 w = x[off];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t packed[2] = {0u, 0u};
+    uint2 out = make_uint2(0u, 0u);
+    if (a != 0.0f && row_is_real(L, tv, r)) {
+      const uint4 w = x[off];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
-      const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
-      packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
+        const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
+        packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
+      }
+      out = make_uint2(packed[0], packed[1]);
     }
-    codes[off] = make_uint2(packed[0], packed[1]);
+    if constexpr (VOP) tl[idx] = out;
+    else codes[off] = out;
+  }
+  if constexpr (VOP) {
+    __syncthreads();
+    const uint8_t* tb = reinterpret_cast<const uint8_t*>(tl);
+    uint4* dst = reinterpret_cast<uint4*>(codes + row0 * chunks);
+    // 16-byte piece q: channel q / 4, positions 16 (q % 4) .. +15
+    for (int q = threadIdx.x; q < 128 * 4; q += kThreads) {
+      const int c = q >> 2, p0 = 16 * (q & 3);
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int pp = p0 + e;
+        const int h = pp >> 5, A = (pp >> 4) & 1, B = (pp >> 2) & 3, rr = pp & 3;
+        const int t = 32 * A + 8 * B + 4 * h + rr;
+        w[e >> 2] |= (uint32_t)tb[t * 128 + c] << (8 * (e & 3));
+      }
+      dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
-                            hipStream_t s) {
+                            bool v_operand, hipStream_t s) {
   dim3 grid(L.n_tiles, L.heads, L.B);
-  hipLaunchKernelGGL(quant_kernel, grid, dim3(kThreads), 0, s, L, static_cast<const uint4*>(x),
-                     reinterpret_cast<uint2*>(codes), scales);
+  if (v_operand) {
+    if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_kernel<true>, grid, dim3(kThreads), 0, s, L,
+                       static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
+  } else {
+    hipLaunchKernelGGL(quant_kernel<false>, grid, dim3(kThreads), 0, s, L,
+                       static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
+  }
   return hipGetLastError();
 }
 

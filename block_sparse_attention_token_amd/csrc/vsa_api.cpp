@@ -197,17 +197,31 @@ vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, co
                     "vsa_build_mask_topk");
 }
 
-vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
-                               float* scales, void* stream) {
+static vsa_status quant_fp8(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                            float* scales, bool v_operand, void* stream, const char* name) {
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
   if (st != VSA_OK) return st;
   if (!x_tiled || !codes || !scales) return fail(VSA_ERR_INVALID, "x_tiled, codes and scales must be non-NULL");
-  if (!aligned16(x_tiled) || ((uintptr_t)codes & 7u)) return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (!aligned16(x_tiled) || ((uintptr_t)codes & (v_operand ? 15u : 7u)))
+    return fail(VSA_ERR_INVALID, "misaligned pointer");
   if (L.d % 8) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (v_operand && (L.C != 64 || L.d != 128))
+    return fail(VSA_ERR_UNSUPPORTED, "the P.V operand layout needs 64-token tiles and head_dim 128");
   if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large");
-  return hip_status(vsa::launch_quant_fp8(L, x_tiled, codes, scales, static_cast<hipStream_t>(stream)),
-                    "vsa_quant_fp8_tiles");
+  return hip_status(vsa::launch_quant_fp8(L, x_tiled, codes, scales, v_operand,
+                                          static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                               float* scales, void* stream) {
+  return quant_fp8(layout, x_tiled, codes, scales, false, stream, "vsa_quant_fp8_tiles");
+}
+
+vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                                 float* scales, void* stream) {
+  return quant_fp8(layout, x_tiled, codes, scales, true, stream, "vsa_quant_fp8_tiles_v");
 }
 
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
@@ -227,9 +241,9 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
   if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
   if (list_mode != 0 && list_mode != 1) return fail(VSA_ERR_INVALID, "list_mode must be 0 or 1");
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
-  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3)
+  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP)
     return fail(VSA_ERR_INVALID, "unknown dtype %d", dtype);
-  if (dtype == VSA_FP8_E4M3) {
+  if (dtype == VSA_FP8_E4M3 || dtype == VSA_FP8_E4M3_VOP) {
     if (!q_scale || !k_scale || !v_scale) return fail(VSA_ERR_INVALID, "fp8 needs q_scale, k_scale and v_scale");
     if (L.C != 64 || L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "fp8 attention needs 64-token tiles and head_dim 128");
   } else {

@@ -130,7 +130,7 @@ hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float 
                         int32_t* kv_cnt, float* scores, void* ws, hipStream_t s);
 size_t route_workspace_bytes(const DevLayout& L);
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
-                            hipStream_t s);
+                            bool v_operand, hipStream_t s);
 
 struct AttnArgs {
   const void* q;

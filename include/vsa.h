@@ -60,7 +60,10 @@ typedef enum vsa_status {
 typedef enum vsa_dtype {
   VSA_F32 = 0,       /* IEEE float32 */
   VSA_BF16 = 1,      /* bfloat16 */
-  VSA_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn": bias 7, max 448, no inf) codes + fp32 tile scales */
+  VSA_FP8_E4M3 = 2,  /* OCP FP8 E4M3 ("fn": bias 7, max 448, no inf) codes + fp32 tile scales */
+  /* As VSA_FP8_E4M3, with the V codes in the P.V operand layout written by
+   * vsa_quant_fp8_tiles_v (attention only; Q and K codes as before). */
+  VSA_FP8_E4M3_VOP = 3
 } vsa_dtype;
 
 /* ----- token layouts ------------------------------------------------------ */
@@ -168,6 +171,18 @@ size_t vsa_build_mask_topk_workspace(const vsa_layout* layout);
 vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
                                float* scales, void* stream);
 
+/* Same quantisation (bit-identical codes and scales) with the codes of each
+ * tile stored channel-major in the order the fp8 P.V product consumes V
+ * (FPSAttention, Approach: P.V in FP8): tile j of (b, head) occupies bytes
+ * [64*128*j, 64*128*(j+1)) of its [n_padded, d] slice; byte 64*c + p holds
+ * channel c of the tile's token t = 32*A + 8*B + 4*h + r, where position
+ * p = 32*h + 16*A + 4*B + r (h, A in 0..1; B, r in 0..3). Pad tokens have
+ * code 0. Needs tile_tokens 64 and head_dim 128 (VSA_ERR_UNSUPPORTED
+ * otherwise); codes must be 16-byte aligned. Pass the result as v with
+ * dtype VSA_FP8_E4M3_VOP. */
+vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
+                                 float* scales, void* stream);
+
 /* ----- S6: block-sparse attention forward --------------------------------------
  * The flash-style, FlashAttention-compatible sparse attention every page
  * builds on (OSP-Next wiki TL;DR; FPSAttention, Approach; VSA, Research
@@ -178,7 +193,9 @@ vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, ui
  *     dtype VSA_F32: float inputs (rounded to bf16 for the products), float out;
  *     dtype VSA_BF16: bf16 in, bf16 out;
  *     dtype VSA_FP8_E4M3: uint8 codes in with q_scale / k_scale / v_scale
- *       float [B, heads, n_tiles] from vsa_quant_fp8_tiles; bf16 out.
+ *       float [B, heads, n_tiles] from vsa_quant_fp8_tiles; bf16 out;
+ *     dtype VSA_FP8_E4M3_VOP: the same, with v from vsa_quant_fp8_tiles_v
+ *       (no byte transposition of V inside the kernel; identical output).
  *   kv_idx / kv_cnt: lists as written by vsa_build_mask_window (list_mode 0:
  *     one table [n_tiles, max_kv] shared by every batch and head) or by
  *     vsa_build_mask_topk (list_mode 1: [B, heads, n_tiles, max_kv]).
@@ -188,8 +205,8 @@ vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, ui
  *     are written as 0.
  *   lse (optional, may be NULL): float [B, heads, n_padded], natural-log
  *     sum_{j in A(i)} exp(sigma q_i.k_j); -inf for pad rows and empty lists.
- * Supported: tile_tokens in {32, 64}; head_dim in {64, 128}; VSA_FP8_E4M3
- * needs tile_tokens 64 and head_dim 128. */
+ * Supported: tile_tokens in {32, 64}; head_dim in {64, 128}; the fp8 dtypes
+ * need tile_tokens 64 and head_dim 128. */
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,

@@ -124,3 +124,32 @@ def dequantize_tiles(codes: np.ndarray, scales: np.ndarray, lay: Layout) -> np.n
                                               lay.head_dim)
     v = v * scales.astype(np.float64)[:, :, :, None, None]
     return v.reshape(B, lay.heads, lay.n_padded, lay.head_dim)
+
+
+def v_operand_order() -> np.ndarray:
+    """Token of a 64-token tile held at each position p (0..63) of the fp8 P.V operand.
+
+    Layout reading (the pages are silent; FPSAttention, "Approach", runs P.V in
+    FP8): per channel, position p = 32 h + 16 A + 4 B + r holds token
+    t = 32 A + 8 B + 4 h + r, with h, A in 0..1 and B, r in 0..3.
+    """
+    tok = np.empty(64, dtype=np.int64)
+    for h in range(2):
+        for a in range(2):
+            for b in range(4):
+                for r in range(4):
+                    tok[32 * h + 16 * a + 4 * b + r] = 32 * a + 8 * b + 4 * h + r
+    return tok
+
+
+def v_operand_layout(codes: np.ndarray, lay: Layout) -> np.ndarray:
+    """Per-tile codes stored channel-major in the P.V operand order.
+
+    64-token tiles, d = 128: tile j of each (b, head) keeps its 64 * 128 bytes,
+    byte 64 c + p holding channel c of token v_operand_order()[p].
+    """
+    assert lay.tile_tokens == 64 and lay.head_dim == 128
+    B = codes.shape[0]
+    x = np.asarray(codes).reshape(B, lay.heads, lay.n_tiles, 64, 128)
+    x = np.swapaxes(x[:, :, :, v_operand_order(), :], -1, -2)     # [.., channel, position]
+    return np.ascontiguousarray(x).reshape(B, lay.heads, lay.n_padded, lay.head_dim)

@@ -54,6 +54,38 @@ def test_quant_fp8_workload_bitexact():
         assert torch.equal(codes, codes2)                   # deterministic
 
 
+def test_quant_fp8_v_operand_bitexact():
+    """vsa_quant_fp8_tiles_v: the oracle's codes in the P.V operand layout,
+    the same scales; on a ragged grid with pads, an all-zero tile and
+    subnormal codes, and on the 720p workload's V."""
+    olay = OLayout(T=5, H=6, W=9, heads=2, head_dim=128, tile=(4, 4, 4))
+    blay = vsa.Layout(T=5, H=6, W=9, heads=2, head_dim=128, tile=(4, 4, 4))
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, olay.n_tokens, 2, 128)).astype(np.float32) * 2
+    x[0, :, 1, :] *= 1e-3
+    order = OL.token_order(olay).reshape(olay.n_tiles, 64)
+    x[0, order[0][order[0] >= 0], 0, :] = 0.0         # tile 0 of head 0 all zero
+    cases = [("ragged", round_to_bf16(x), olay, blay)]
+    cfg = CONFIGS["fp8_topp_720p"]
+    wo, wb = layouts(cfg)
+    cases.append((cfg.name, inputs(cfg.name)[2], wo, wb))
+    for name, xn, ol, bl in cases:
+        announce(f"quant v-operand {name}")
+        xt = vsa.tile_permute(bl, to_device(xn, "bf16"))
+        codes, scales = vsa.quant_fp8_tiles(bl, xt, v_operand=True)
+        torch.cuda.synchronize()
+        rc, rs = OF.quantize_tiles(OL.permute(xn, ol), ol)
+        assert np.array_equal(codes.cpu().numpy(), OF.v_operand_layout(rc, ol))
+        assert np.array_equal(scales.cpu().numpy().view(np.int32), rs.view(np.int32))
+
+
+def test_quant_fp8_v_operand_rejects_other_shapes():
+    lay = vsa.Layout(T=3, H=5, W=6, heads=2, head_dim=16, tile=(2, 4, 4))
+    x = torch.zeros((1, 2, vsa.layout_info(lay).n_padded, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(vsa.VsaError):
+        vsa.quant_fp8_tiles(lay, x, v_operand=True)
+
+
 def _accept_topk(gpu_row, ref_row, s, k):
     if gpu_row == ref_row:
         return True

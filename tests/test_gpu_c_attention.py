@@ -190,6 +190,31 @@ def test_topp_720p_fp8_sampled(topp_case):
     assert rl2_u <= 1.1 * rl2_q + 5e-3
 
 
+def test_topp_720p_fp8_v_operand_identical(topp_case):
+    """V codes in the P.V operand layout give the very same output as the
+    token-major codes (same arithmetic, only the staging differs)."""
+    cfg, olay, blay, idx, cnt, (qd, kd, vd), _ = topp_case
+    announce(f"attn {cfg.name} fp8 v-operand")
+    qc, qs = vsa.quant_fp8_tiles(blay, qd)
+    kc, ks = vsa.quant_fp8_tiles(blay, kd)
+    vc, vs = vsa.quant_fp8_tiles(blay, vd)
+    vo, vs2 = vsa.quant_fp8_tiles(blay, vd, v_operand=True)
+    di, dc = lists_to_device(idx, cnt)
+    o1, l1 = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs), want_lse=True)
+    o2, l2 = vsa.block_sparse_attn_fwd(blay, qc, kc, vo, di, dc, scales=(qs, ks, vs2), want_lse=True,
+                                       v_operand=True)
+    # shared lists too (the grouped kernel)
+    sh = OM.window_lists(olay, 1, 1, 1)
+    si, sc = lists_to_device(*table_from_lists(sh))
+    o3, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, si, sc, scales=(qs, ks, vs))
+    o4, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vo, si, sc, scales=(qs, ks, vs2), v_operand=True)
+    torch.cuda.synchronize()
+    assert torch.equal(vs, vs2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.equal(o3.view(torch.int16), o4.view(torch.int16))
+
+
 def test_topp_720p_bf16_sampled(topp_case):
     cfg, olay, blay, idx, cnt, (qd, kd, vd), (qo, ko, vo) = topp_case
     announce(f"attn {cfg.name} bf16 routed top-p")

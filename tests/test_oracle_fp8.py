@@ -108,3 +108,39 @@ def test_quantize_tiles_properties():
     bound = np.abs(xt) * 2.0 ** -4 * (1 + 1e-6) + \
         scales.repeat(C, axis=2)[..., None] * 2.0 ** -10 * (1 + 1e-6)
     assert np.all(err <= bound)
+
+
+def _golden_v_order():
+    return [tuple(int(x) for x in line.split(":")) for line in read_golden("fp8_v_operand_order.txt")]
+
+
+def test_v_operand_order_golden_and_inverse():
+    tok = F.v_operand_order()
+    assert sorted(tok.tolist()) == list(range(64))                  # a permutation
+    for p, t in _golden_v_order():
+        assert tok[p] == t, (p, t)
+    # the inverse written the other way round: token t sits at
+    # p = 32 ((t div 4) mod 2) + 16 (t div 32) + 4 ((t div 8) mod 4) + t mod 4
+    for t in range(64):
+        p = 32 * ((t // 4) % 2) + 16 * (t // 32) + 4 * ((t // 8) % 4) + t % 4
+        assert tok[p] == t
+
+
+def test_v_operand_layout_is_a_per_tile_transpose():
+    lay = Layout(T=4, H=8, W=8, heads=2, head_dim=128, tile=(4, 4, 4))
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 256, (1, 2, lay.n_padded, 128), dtype=np.uint8)
+    out = F.v_operand_layout(codes, lay)
+    assert out.shape == codes.shape and out.dtype == codes.dtype
+    tok = F.v_operand_order()
+    for h in range(2):
+        for j in range(lay.n_tiles):
+            tile_in = codes[0, h, 64 * j:64 * (j + 1)]               # [token, channel]
+            tile_out = out[0, h, 64 * j:64 * (j + 1)].reshape(-1)    # bytes 64 c + p
+            for c in (0, 1, 77, 127):
+                for p in (0, 5, 31, 32, 50, 63):
+                    assert tile_out[64 * c + p] == tile_in[tok[p], c]
+    # same multiset of bytes per tile: nothing lost or duplicated
+    a = np.sort(codes.reshape(1, 2, lay.n_tiles, -1), axis=-1)
+    b = np.sort(out.reshape(1, 2, lay.n_tiles, -1), axis=-1)
+    assert np.array_equal(a, b)
