@@ -16,9 +16,10 @@ Parity status of each part (what pins it, see ``tests/test_oracle_*.py``):
   top-p with floor ............ pinned (prefix-mass properties, brute force)
   e4m3 codec / quantiser ...... pinned (format definition, torch casts)
   attention ................... pinned (brute-force dense, torch SDPA, closed forms)
+  attention gradients ......... pinned (finite differences, torch autograd, closed forms)
   fp8 attention ............... parity unpinned beyond the tolerance gate
 """
 from .layout import Layout
-from . import layout, masks, routing, fp8, attention
+from . import layout, masks, routing, fp8, attention, attention_grad
 
-__all__ = ["Layout", "layout", "masks", "routing", "fp8", "attention"]
+__all__ = ["Layout", "layout", "masks", "routing", "fp8", "attention", "attention_grad"]
