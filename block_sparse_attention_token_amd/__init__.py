@@ -25,7 +25,8 @@ from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, 
 
 __all__ = [
     "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
-    "quant_fp8_tiles", "block_sparse_attn_fwd", "VsaError", "EXPORTED",
+    "quant_fp8_tiles", "block_sparse_attn_fwd", "build_transposed_lists", "bwd_workspace_bytes",
+    "block_sparse_attn_bwd", "VsaError", "EXPORTED",
     "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
 ]
 
@@ -197,3 +198,65 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
         _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode, float(softmax_scale), _ptr(out),
         _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def build_transposed_lists(lay: Layout, kv_idx: torch.Tensor, kv_cnt: torch.Tensor, stream=None):
+    """Per key tile, the ascending query tiles whose list holds it
+    (vsa_build_transposed_lists): (q_idx, q_cnt), 2-D / 1-D for a shared table,
+    4-D / 3-D for per-(b, head) lists."""
+    info = layout_info(lay)
+    n = info.n_tiles
+    list_mode = 0 if kv_idx.dim() == 2 else 1
+    lead = () if list_mode == 0 else (lay.batch, lay.heads)
+    q_idx = torch.empty(lead + (n, n), dtype=torch.int32, device=kv_idx.device)
+    q_cnt = torch.empty(lead + (n,), dtype=torch.int32, device=kv_idx.device)
+    c = lay.c()
+    check(lib().vsa_build_transposed_lists(ctypes.byref(c), _ptr(kv_idx), _ptr(kv_cnt),
+                                           int(kv_idx.shape[-1]), list_mode, _ptr(q_idx),
+                                           _ptr(q_cnt), _stream(stream)))
+    return q_idx, q_cnt
+
+
+def bwd_workspace_bytes(lay: Layout) -> int:
+    c = lay.c()
+    return int(lib().vsa_block_sparse_attn_bwd_workspace(ctypes.byref(c)))
+
+
+def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                          kv_idx: Optional[torch.Tensor] = None,
+                          kv_cnt: Optional[torch.Tensor] = None,
+                          q_idx: Optional[torch.Tensor] = None,
+                          q_cnt: Optional[torch.Tensor] = None,
+                          softmax_scale: Optional[float] = None,
+                          grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of block_sparse_attn_fwd (vsa_block_sparse_attn_bwd).
+
+    Same tensors, lists and scale as the forward call, plus its output and
+    lse and the upstream gradient ``dout``. The transposed lists are built
+    here when kv_idx is given and q_idx is not.
+    """
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    dtype = _DT.get(q.dtype, -1)
+    if kv_idx is not None and q_idx is None:
+        q_idx, q_cnt = build_transposed_lists(lay, kv_idx, kv_cnt, stream=stream)
+    if kv_idx is not None:
+        max_kv = kv_idx.shape[-1]
+        list_mode = 0 if kv_idx.dim() == 2 else 1
+    else:
+        max_kv, list_mode = 0, 0
+    if grads is None:
+        grads = tuple(torch.empty_like(x) for x in (q, k, v))
+    dq, dk, dv = grads
+    need = bwd_workspace_bytes(lay)
+    if workspace is None:
+        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=q.device)
+    c = lay.c()
+    check(lib().vsa_block_sparse_attn_bwd(
+        ctypes.byref(c), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), _ptr(q_idx), _ptr(q_cnt), list_mode,
+        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return dq, dk, dv

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["vsa_api.cpp", "permute.hip", "mask.hip", "route.hip", "quant.hip", "attn.hip"]
+SOURCES = ["vsa_api.cpp", "permute.hip", "mask.hip", "route.hip", "quant.hip", "attn.hip", "attn_bwd.hip"]
 
 # Packed-fp32 VALU forms are disabled for every HIP translation unit.
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

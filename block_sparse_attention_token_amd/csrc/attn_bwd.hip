@@ -1,0 +1,530 @@
+// Backward pass of the block-sparse attention on gfx950 MFMA: dQ, dK and dV
+// over the same key-tile lists as the forward. The pages train through this
+// attention (VSA, Research Type and Experiment Setup rows: a trainable
+// sparse attention used in DiT pretraining and fine-tuning; FPSAttention,
+// Approach: training-aware FP8 and tile sparsity). The gradients are the
+// chain rule of the forward's definition; with the forward's natural-log
+// lse and D_i = dO_i . O_i:
+//   P_ij  = exp(sigma q_i.k_j - lse_i)            (j in A(i))
+//   dV_j  = sum_i P_ij dO_i
+//   dS_ij = P_ij (dO_i.v_j - D_i)
+//   dQ_i  = sigma sum_j dS_ij k_j,   dK_j = sigma sum_i dS_ij q_i
+//
+// Three kernels, in stream order:
+//   rowstat: lse_i * log2(e) (+inf where the row has no weight) and D_i;
+//   dq:  one workgroup per query tile, walking the tile's forward list; a
+//        wave owns 32 query rows and computes the transposed products
+//          S^T = K . Q^T,  dP^T = V . dO^T,  dQ^T += K^T . dS^T
+//        so every lane holds one query row: its lse and D stay in registers;
+//   dkv: one workgroup per key tile, walking the transposed list (the query
+//        tiles whose lists hold it); a wave owns 32 key rows and computes
+//          S = Q . K^T,  dP = dO . V^T,  dV^T += dO^T . P,  dK^T += Q^T . dS
+//        so every lane holds one key column and its K, V operands stay in
+//        registers for the whole walk.
+// The walked tensors (K and V for dq, Q and dO for dkv) pass through LDS in
+// 32-token blocks: loaded into registers one block ahead, stored to padded
+// row-major LDS rows, double-buffered with one barrier per block. The
+// operands that contract over tokens (K^T, dO^T, Q^T) are read from those
+// same rows with ds_read_b64_tr_b16, whose transposition hands each lane
+// four consecutive token rows of one channel. The probabilities and dS
+// leave the score accumulators as B operands without moving between lanes:
+// the token contraction runs in the accumulator's row order, and the
+// transposed reads gather the tokens in that same order.
+#include <float.h>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// two floats -> two bf16 (round to nearest even) in one dword, lo first
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// Buffer-resource loads of one (b, head) slice: 32-bit offsets, reads past
+// the slice return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFFll ? bytes : 0x7FFFFFFFll),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// 8 consecutive elements at byte offset voff + soff as 8 bf16 (f32 input: rounded)
+template <bool F32IN>
+__device__ __forceinline__ uint4 bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (F32IN) {
+    const uint4 x = bload(r, voff, soff), y = bload(r, voff + 16, soff);
+    return make_uint4(pack2(__uint_as_float(x.x), __uint_as_float(x.y)),
+                      pack2(__uint_as_float(x.z), __uint_as_float(x.w)),
+                      pack2(__uint_as_float(y.x), __uint_as_float(y.y)),
+                      pack2(__uint_as_float(y.z), __uint_as_float(y.w)));
+  } else {
+    return bload(r, voff, soff);
+  }
+}
+
+__device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics. LPR = D/8 lanes per row, 8 elements each.
+template <int D, bool F32IN>
+__global__ __launch_bounds__(256) void rowstat_kernel(const void* out, const void* dout,
+                                                      const float* lse, float2* st, long long rows) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const long long e0 = row * D + part * 8;
+    if constexpr (F32IN) {
+      const float4* o = reinterpret_cast<const float4*>(static_cast<const float*>(out) + e0);
+      const float4* g = reinterpret_cast<const float4*>(static_cast<const float*>(dout) + e0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 x = o[i], y = g[i];
+        acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+      }
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(out) + e0);
+      const uint4 y = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dout) + e0);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += bf_lo(xs[i]) * bf_lo(ys[i]) + bf_hi(xs[i]) * bf_hi(ys[i]);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    const float l = lse[row];
+    const bool live = l > -INFINITY;      // -inf: pad row or empty key set
+    st[row] = make_float2(live ? l * kLog2e : INFINITY, live ? acc : 0.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed lists: one workgroup per (list head, key tile j) tests every
+// query tile's ascending list for j by binary search and compacts the hits
+// in ascending order (ballot prefix counts), so the result is deterministic.
+__global__ __launch_bounds__(256) void transpose_lists_kernel(int n_tiles, const int32_t* kv_idx,
+                                                              const int32_t* kv_cnt, int max_kv,
+                                                              int32_t* q_idx, int32_t* q_cnt) {
+  __shared__ int wcnt[4];
+  const int j = blockIdx.x;
+  const long long lh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int32_t* idx = kv_idx + lh * n_tiles * (long long)max_kv;
+  const int32_t* cnt = kv_cnt + lh * n_tiles;
+  int32_t* dst = q_idx + (lh * n_tiles + j) * (long long)n_tiles;
+  int total = 0;
+  for (int i0 = 0; i0 < n_tiles; i0 += 256) {
+    const int i = i0 + tid;
+    bool hit = false;
+    if (i < n_tiles) {
+      const int32_t* row = idx + (long long)i * max_kv;
+      const int c = min(max(cnt[i], 0), max_kv);
+      int lo = 0, hi = c;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      hit = lo < c && row[lo] == j;
+    }
+    const unsigned long long m = __ballot(hit);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += wcnt[w];
+    if (hit) dst[off + __popcll(m & ((1ull << lane) - 1ull))] = i;
+    total += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
+  }
+  if (tid == 0) q_cnt[lh * n_tiles + j] = total;
+}
+
+// ---------------------------------------------------------------------------
+// Register staging of one 32-token block (32 rows x D channels, row-major in
+// HBM) and its store into LDS rows padded by 16 bytes (the 16 rows a
+// half-wave reads at one column then start 16 bytes apart: all banks).
+template <int D, int THREADS, bool F32IN>
+struct RowBlock {
+  static constexpr int ES = F32IN ? 4 : 2;
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RS = CPR + 1;                // padded row stride, uint4
+  static constexpr int RSE = RS * 8;                // padded row stride, bf16 elements
+  static constexpr int CHUNKS = 32 * CPR;
+  static constexpr int PER_T = CHUNKS / THREADS;
+  static constexpr int LDS = 32 * RS;               // uint4 per buffer
+  static_assert(CHUNKS % THREADS == 0, "whole chunks per thread");
+  uint4 reg[PER_T];
+
+  // block_off: byte offset of the block's first row inside the (b, head) slice
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t block_off, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) reg[i] = bload8<F32IN>(r, (tid + i * THREADS) * 8 * ES, block_off);
+  }
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * THREADS;
+      lds[(c / CPR) * RS + c % CPR] = reg[i];
+    }
+  }
+};
+
+// Per-lane element offset for the transposed reads below: in each 16-lane
+// group, source lane i reads row 4*half + i/4 at channels 16*(group%2) +
+// 4*(i%4) .. +3, so that the transposition hands lane i rows 4*half + 0..3
+// of channel 16*(group%2) + i.
+template <int RSE>
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  return (4 * (g >> 1) + (i >> 2)) * RSE + 16 * (g & 1) + 4 * (i & 3);
+}
+
+__device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+}
+
+// A operand X^T (32 channels c0.., 16 tokens of chunk kc) from row-major X
+// rows in LDS, tokens in the score accumulator's row order: operand slot s
+// of half-wave h is token 16*kc + 8*(s/4) + 4*h + s%4.
+// base = LDS rows + tr_lane_offset(lane).
+template <int RSE>
+__device__ __forceinline__ uint4 frag_t(const uint16_t* base, int c0, int kc) {
+  const uint2 lo = lds_tr(base + (16 * kc) * RSE + c0);
+  const uint2 hi = lds_tr(base + (16 * kc + 8) * RSE + c0);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Bit r set iff token 8*(r/4) + 4*half + r%4 of the block (tokens tok0 ..
+// tok0+31 of tile `tile`) is real.
+__device__ __forceinline__ uint32_t block_real_bits(const DevLayout& L, int tile, int tok0, int lane,
+                                                    int half) {
+  const TileValid tv = tile_valid(L, tile);
+  if (tv.full) return 0xFFFFu;
+  const unsigned long long vm = __ballot(lane < 32 && row_is_real(L, tv, tok0 + lane));
+  uint32_t m = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) m |= (uint32_t)((vm >> (8 * g + 4 * half)) & 0xFull) << (4 * g);
+  return m;
+}
+
+// Write 32 rows x D of a transposed accumulator (lane holds row `row` and
+// channels 32*mt + 8*g + 4*half + 0..3) scaled by f, as bf16 or f32; rows
+// with real == false are written as zeros (whatever the accumulator holds).
+template <int D, bool F32IN>
+__device__ __forceinline__ void store_rows_t(void* dst, long long row, int half,
+                                             const f32x16_t (&acc)[D / 32], float f, bool real) {
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * mt + 8 * g + 4 * half;
+      const float x0 = real ? acc[mt][4 * g] * f : 0.0f, x1 = real ? acc[mt][4 * g + 1] * f : 0.0f;
+      const float x2 = real ? acc[mt][4 * g + 2] * f : 0.0f, x3 = real ? acc[mt][4 * g + 3] * f : 0.0f;
+      if constexpr (F32IN) {
+        *reinterpret_cast<float4*>(static_cast<float*>(dst) + row * D + c0) = make_float4(x0, x1, x2, x3);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + row * D + c0) =
+            make_uint2(pack2(x0, x1), pack2(x2, x3));
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup (C/32 waves) per (b, head, query tile).
+template <int C, int D, bool F32IN>
+__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
+  constexpr int THREADS = 2 * C, SUB = C / 32;
+  constexpr int ES = F32IN ? 4 : 2;
+  using RB = RowBlock<D, THREADS, F32IN>;
+  __shared__ uint4 k_lds[2][RB::LDS];
+  __shared__ uint4 v_lds[2][RB::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int item = a.kv_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
+                                                 : xcd_remap(blockIdx.x, n_work);
+  const int bh = item / L.n_tiles, qt = item - bh * L.n_tiles;
+  const long long row0 = (long long)bh * L.n_padded;
+  const long long slice = (long long)L.n_padded * D * ES;
+  const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + row0 * D * ES, slice);
+  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * D * ES, slice);
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * D * ES, slice);
+  const rsrc_t rg = make_rsrc(static_cast<const char*>(a.dout) + row0 * D * ES, slice);
+
+  const int32_t* list = nullptr;
+  int cnt = L.n_tiles;
+  if (a.kv_idx) {
+    const long long r = (a.list_mode ? (long long)bh * L.n_tiles : 0ll) + qt;
+    list = a.kv_idx + r * a.max_kv;
+    cnt = min(max(a.kv_cnt[r], 0), a.max_kv);
+  }
+
+  // B operands Q^T and dO^T: row qrow, channels 16*ks + 8*half .. +7
+  const int qrow = 32 * wave + l32;
+  const uint32_t qoff = (uint32_t)((qt * C + qrow) * D * ES);
+  uint4 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = bload8<F32IN>(rq, qoff + (16 * ks + 8 * half) * ES, 0);
+    gf[ks] = bload8<F32IN>(rg, qoff + (16 * ks + 8 * half) * ES, 0);
+  }
+  const float2 st = a.rowstat[row0 + qt * C + qrow];
+  const float nl = -st.x, dd = st.y;
+  const float sl2 = a.scale_log2;
+
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16_t{};
+
+  auto tile_of = [&](int b) -> int {
+    const int e = b / SUB;
+    return list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+  };
+  auto block_off = [&](int b) -> uint32_t {
+    return (uint32_t)((tile_of(b) * C + 32 * (b % SUB)) * D * ES);
+  };
+
+  RB kio, vio;
+  const int nblk = cnt * SUB;
+  if (nblk > 0) {
+    kio.load(rk, block_off(0), tid);
+    vio.load(rv, block_off(0), tid);
+    kio.store(k_lds[0], tid);
+    vio.store(v_lds[0], tid);
+  }
+  __syncthreads();
+  const int tro = tr_lane_offset<RB::RSE>(lane);
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    if (b + 1 < nblk) {
+      const uint32_t off = block_off(b + 1);
+      kio.load(rk, off, tid);
+      vio.load(rv, off, tid);
+    }
+    const uint32_t kbits = block_real_bits(L, tile_of(b), 32 * (b % SUB), lane, half);
+    const uint4* kb = k_lds[buf] + l32 * RB::RS + half;
+    const uint4* vb = v_lds[buf] + l32 * RB::RS + half;
+    f32x16_t s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mfma(kb[2 * ks], qf[ks], s);
+      dp = mfma(vb[2 * ks], gf[ks], dp);
+    }
+    uint4 dsp[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * c + i;
+        const float p = ((kbits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) : 0.0f;
+        x[i] = p * (dp[r] - dd);
+      }
+      dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    }
+    const uint16_t* kt = reinterpret_cast<const uint16_t*>(k_lds[buf]) + tro;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[mt] = mfma(frag_t<RB::RSE>(kt, 32 * mt, c), dsp[c], acc[mt]);
+    if (b + 1 < nblk) {
+      kio.store(k_lds[buf ^ 1], tid);
+      vio.store(v_lds[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  const bool real = row_is_real(L, tile_valid(L, qt), qrow);
+  store_rows_t<D, F32IN>(a.dq, row0 + qt * C + qrow, half, acc, a.scale, real);
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one workgroup (C/32 waves) per (b, head, key tile). One wave per
+// SIMD: the two accumulators and the K, V operands take most of 512 registers.
+template <int C, int D, bool F32IN>
+__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
+  constexpr int THREADS = 2 * C, SUB = C / 32;
+  constexpr int ES = F32IN ? 4 : 2;
+  using RB = RowBlock<D, THREADS, F32IN>;
+  __shared__ uint4 q_lds[2][RB::LDS];
+  __shared__ uint4 g_lds[2][RB::LDS];
+  __shared__ float4 st_lds[2][16];        // 32 rows of {lse2, D}
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int item = a.q_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
+                                                : xcd_remap(blockIdx.x, n_work);
+  const int bh = item / L.n_tiles, kt = item - bh * L.n_tiles;
+  const long long row0 = (long long)bh * L.n_padded;
+  const long long slice = (long long)L.n_padded * D * ES;
+  const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + row0 * D * ES, slice);
+  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * D * ES, slice);
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * D * ES, slice);
+  const rsrc_t rg = make_rsrc(static_cast<const char*>(a.dout) + row0 * D * ES, slice);
+  const float2* rst = a.rowstat + row0;
+
+  const int32_t* list = nullptr;
+  int cnt = L.n_tiles;
+  if (a.q_idx) {
+    const long long r = (a.list_mode ? (long long)bh * L.n_tiles : 0ll) + kt;
+    list = a.q_idx + r * L.n_tiles;
+    cnt = min(max(a.q_cnt[r], 0), L.n_tiles);
+  }
+
+  // B operands K^T and V^T: key row krow, channels 16*ks + 8*half .. +7
+  const int krow = 32 * wave + l32;
+  const uint32_t koff = (uint32_t)((kt * C + krow) * D * ES);
+  uint4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = bload8<F32IN>(rk, koff + (16 * ks + 8 * half) * ES, 0);
+    vf[ks] = bload8<F32IN>(rv, koff + (16 * ks + 8 * half) * ES, 0);
+  }
+  const float sl2 = a.scale_log2;
+
+  f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16_t{};
+
+  auto tile_of = [&](int b) -> int {
+    const int e = b / SUB;
+    return list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+  };
+  auto first_row = [&](int b) -> int { return tile_of(b) * C + 32 * (b % SUB); };
+
+  RB qio, gio;
+  float2 streg = make_float2(0.0f, 0.0f);
+  const int nblk = cnt * SUB;
+  if (nblk > 0) {
+    const int r = first_row(0);
+    qio.load(rq, (uint32_t)(r * D * ES), tid);
+    gio.load(rg, (uint32_t)(r * D * ES), tid);
+    if (tid < 32) streg = rst[r + tid];
+    qio.store(q_lds[0], tid);
+    gio.store(g_lds[0], tid);
+    if (tid < 32) reinterpret_cast<float2*>(st_lds[0])[tid] = streg;
+  }
+  __syncthreads();
+  const int tro = tr_lane_offset<RB::RSE>(lane);
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    if (b + 1 < nblk) {
+      const int r = first_row(b + 1);
+      qio.load(rq, (uint32_t)(r * D * ES), tid);
+      gio.load(rg, (uint32_t)(r * D * ES), tid);
+      if (tid < 32) streg = rst[r + tid];
+    }
+    const uint4* qb = q_lds[buf] + l32 * RB::RS + half;
+    const uint4* gb = g_lds[buf] + l32 * RB::RS + half;
+    f32x16_t s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mfma(qb[2 * ks], kf[ks], s);
+      dp = mfma(gb[2 * ks], vf[ks], dp);
+    }
+    // rows of this lane: query 8*g + 4*half + i of the block, g = 0..3
+    uint4 pp[2], dsp[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8], x[8];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * c + gg;
+        const float4 s01 = st_lds[buf][4 * g + 2 * half];       // rows 8g+4half+0, +1
+        const float4 s23 = st_lds[buf][4 * g + 2 * half + 1];   // rows 8g+4half+2, +3
+        const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
+        const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          p[4 * gg + i] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l2[i]));
+          x[4 * gg + i] = p[4 * gg + i] * (dp[r] - dd[i]);
+        }
+      }
+      pp[c] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+      dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    }
+    const uint16_t* gt = reinterpret_cast<const uint16_t*>(g_lds[buf]) + tro;
+    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(q_lds[buf]) + tro;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dv[mt] = mfma(frag_t<RB::RSE>(gt, 32 * mt, c), pp[c], dv[mt]);
+        dk[mt] = mfma(frag_t<RB::RSE>(qt_, 32 * mt, c), dsp[c], dk[mt]);
+      }
+    if (b + 1 < nblk) {
+      qio.store(q_lds[buf ^ 1], tid);
+      gio.store(g_lds[buf ^ 1], tid);
+      if (tid < 32) reinterpret_cast<float2*>(st_lds[buf ^ 1])[tid] = streg;
+    }
+    __syncthreads();
+  }
+  const bool real = row_is_real(L, tile_valid(L, kt), krow);
+  const long long orow = row0 + kt * C + krow;
+  store_rows_t<D, F32IN>(a.dk, orow, half, dk, a.scale, real);
+  store_rows_t<D, F32IN>(a.dv, orow, half, dv, 1.0f, real);
+}
+
+template <int C, int D, bool F32IN>
+hipError_t launch_bwd_shape(const DevLayout& L, const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)L.B * L.heads * L.n_padded;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((rowstat_kernel<D, F32IN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                     0, s, a.out, a.dout, a.lse, a.rowstat, rows);
+  const int n_work = L.B * L.heads * L.n_tiles;
+  hipLaunchKernelGGL((dq_kernel<C, D, F32IN>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
+  hipLaunchKernelGGL((dkv_kernel<C, D, F32IN>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
+  return hipGetLastError();
+}
+
+template <bool F32IN>
+hipError_t launch_bwd_dtype(const DevLayout& L, const BwdArgs& a, hipStream_t s) {
+  if (L.C == 64) return L.d == 128 ? launch_bwd_shape<64, 128, F32IN>(L, a, s)
+                                   : launch_bwd_shape<64, 64, F32IN>(L, a, s);
+  return L.d == 128 ? launch_bwd_shape<32, 128, F32IN>(L, a, s) : launch_bwd_shape<32, 64, F32IN>(L, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_transpose_lists(const DevLayout& L, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                  int max_kv, int list_mode, int32_t* q_idx, int32_t* q_cnt,
+                                  hipStream_t s) {
+  const int lh = list_mode ? L.B * L.heads : 1;
+  hipLaunchKernelGGL(transpose_lists_kernel, dim3(L.n_tiles, lh), dim3(256), 0, s, L.n_tiles, kv_idx,
+                     kv_cnt, max_kv, q_idx, q_cnt);
+  return hipGetLastError();
+}
+
+size_t attn_bwd_workspace_bytes(const DevLayout& L) {
+  return (size_t)L.B * L.heads * L.n_padded * sizeof(float2);
+}
+
+hipError_t launch_attn_bwd(const DevLayout& L, int dtype, const BwdArgs& a, hipStream_t s) {
+  return dtype == 0 ? launch_bwd_dtype<true>(L, a, s) : launch_bwd_dtype<false>(L, a, s);
+}
+
+}  // namespace vsa

@@ -270,6 +270,88 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
                     "vsa_block_sparse_attn_fwd");
 }
 
+vsa_status vsa_build_transposed_lists(const vsa_layout* layout, const int32_t* kv_idx,
+                                      const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
+                                      int32_t* q_idx, int32_t* q_cnt, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!kv_idx || !kv_cnt || !q_idx || !q_cnt)
+    return fail(VSA_ERR_INVALID, "kv_idx, kv_cnt, q_idx and q_cnt must be non-NULL");
+  if (max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
+  if (list_mode != 0 && list_mode != 1) return fail(VSA_ERR_INVALID, "list_mode must be 0 or 1");
+  const long long lh = list_mode ? (long long)L.B * L.heads : 1;
+  if (lh > 65535) return fail(VSA_ERR_UNSUPPORTED, "more than 65535 list heads");
+  return hip_status(vsa::launch_transpose_lists(L, kv_idx, kv_cnt, max_kv, list_mode, q_idx, q_cnt,
+                                                static_cast<hipStream_t>(stream)),
+                    "vsa_build_transposed_lists");
+}
+
+size_t vsa_block_sparse_attn_bwd_workspace(const vsa_layout* layout) {
+  vsa::DevLayout L;
+  if (derive(layout, &L, nullptr) != VSA_OK) return 0;
+  return vsa::attn_bwd_workspace_bytes(L);
+}
+
+vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, const void* q,
+                                     const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, const int32_t* kv_idx,
+                                     const int32_t* kv_cnt, int32_t max_kv, const int32_t* q_idx,
+                                     const int32_t* q_cnt, int32_t list_mode, float softmax_scale,
+                                     void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(VSA_ERR_INVALID, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
+  const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(VSA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (dq == dk || dq == dv || dk == dv) return fail(VSA_ERR_INVALID, "dq, dk and dv must be distinct");
+  for (const void* g : {dq, dk, dv})
+    for (const void* x : {q, k, v, out, dout})
+      if (g == x) return fail(VSA_ERR_INVALID, "gradients must not alias the inputs");
+  const bool lists = kv_idx || kv_cnt || q_idx || q_cnt;
+  if (lists && !(kv_idx && kv_cnt && q_idx && q_cnt))
+    return fail(VSA_ERR_INVALID, "kv_idx, kv_cnt, q_idx and q_cnt must all be set or all be NULL");
+  if (lists && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
+  if (list_mode != 0 && list_mode != 1) return fail(VSA_ERR_INVALID, "list_mode must be 0 or 1");
+  if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
+  if (dtype != VSA_F32 && dtype != VSA_BF16)
+    return fail(VSA_ERR_UNSUPPORTED, "the backward pass takes VSA_F32 or VSA_BF16");
+  if (L.C != 32 && L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
+  if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
+  const long long work = (long long)L.B * L.heads * L.n_tiles;
+  if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  const size_t need = vsa::attn_bwd_workspace_bytes(L);
+  if (!workspace || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+    return fail(VSA_ERR_INVALID, "workspace must be 8-byte aligned");
+  vsa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = lists ? max_kv : L.n_tiles;
+  a.q_idx = q_idx;
+  a.q_cnt = q_cnt;
+  a.list_mode = list_mode;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.rowstat = static_cast<float2*>(workspace);
+  return hip_status(vsa::launch_attn_bwd(L, dtype, a, static_cast<hipStream_t>(stream)),
+                    "vsa_block_sparse_attn_bwd");
+}
+
 const char* vsa_status_string(int32_t status) {
   switch (status) {
     case VSA_OK: return "VSA_OK";

@@ -149,4 +149,33 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStream_t s);
 
+// For every key tile j (per list head): the ascending query tiles whose
+// list holds j. q_idx [LH, n_tiles, n_tiles], q_cnt [LH, n_tiles].
+hipError_t launch_transpose_lists(const DevLayout& L, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                  int max_kv, int list_mode, int32_t* q_idx, int32_t* q_cnt,
+                                  hipStream_t s);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const int32_t* kv_idx;   // forward lists (null: dense)
+  const int32_t* kv_cnt;
+  int max_kv;
+  const int32_t* q_idx;    // transposed lists (null: dense)
+  const int32_t* q_cnt;
+  int list_mode;           // 0 shared tables, 1 per (batch, head)
+  float scale;             // softmax scale
+  float scale_log2;        // softmax scale * log2(e)
+  void* dq;
+  void* dk;
+  void* dv;
+  float2* rowstat;         // workspace: per row {lse * log2(e) (+inf: no weight), dO . O}
+};
+size_t attn_bwd_workspace_bytes(const DevLayout& L);
+hipError_t launch_attn_bwd(const DevLayout& L, int dtype, const BwdArgs& a, hipStream_t s);
+
 }  // namespace vsa

@@ -214,6 +214,58 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
                                      int32_t list_mode, float softmax_scale, void* out, float* lse,
                                      void* stream);
 
+/* ----- S6 backward: gradients of the block-sparse attention -------------------
+ * The pages train through this attention: VSA ("Faster Video Diffusion with
+ * Trainable Sparse Attention", Research Type and Experiment Setup rows) is a
+ * trainable sparse attention used to pretrain and fine-tune video DiTs, and
+ * FPSAttention (Approach) trains jointly with FP8 and tile sparsity. The
+ * gradients are the chain rule of the forward's definition: for real query
+ * token i with key set A(i), P_ij = exp(sigma q_i.k_j - lse_i) and
+ * D_i = dO_i . O_i,
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i.v_j - D_i),
+ *   dQ_i = sigma sum_j dS_ij k_j,   dK_j = sigma sum_i dS_ij q_i.
+ *
+ * vsa_build_transposed_lists: for every key tile j, the ascending query
+ * tiles whose list holds j (the walk order of the dK/dV kernel).
+ *   kv_idx / kv_cnt: forward lists as for vsa_block_sparse_attn_fwd
+ *     (list_mode 0: [n_tiles, max_kv]; 1: [B, heads, n_tiles, max_kv]); each
+ *     list must be strictly ascending (as the mask builders write them).
+ *   q_idx: int32 [LH, n_tiles, n_tiles] and q_cnt: int32 [LH, n_tiles],
+ *     LH = 1 (list_mode 0) or B * heads (list_mode 1). Row j of q_idx holds
+ *     q_cnt[j] query tiles; the rest of the row is left unwritten.
+ * Deterministic; builds once per set of lists and may be cached with them. */
+vsa_status vsa_build_transposed_lists(const vsa_layout* layout, const int32_t* kv_idx,
+                                      const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
+                                      int32_t* q_idx, int32_t* q_cnt, void* stream);
+
+/* Bytes of device workspace vsa_block_sparse_attn_bwd needs: 8 bytes per
+ * padded row of every (batch, head); 0 for an invalid layout. */
+size_t vsa_block_sparse_attn_bwd_workspace(const vsa_layout* layout);
+
+/* vsa_block_sparse_attn_bwd: dq, dk, dv of the forward call with the same
+ * layout, dtype, q, k, v, lists and softmax_scale.
+ *   dtype: VSA_BF16 (bf16 tensors and gradients) or VSA_F32 (float tensors,
+ *     rounded to bf16 for the products; float gradients).
+ *   out, lse: the forward's output and its (non-NULL) lse.
+ *   dout: upstream gradient of out, tiled [B, heads, n_padded, d]; its pad
+ *     rows are ignored.
+ *   kv_idx / kv_cnt / max_kv: the forward lists; q_idx / q_cnt: their
+ *     transposition from vsa_build_transposed_lists with the same list_mode.
+ *     All four NULL: dense attention.
+ *   dq, dk, dv: [B, heads, n_padded, d], fully written: pad rows get 0. They
+ *     must not alias the inputs.
+ *   workspace: device memory of at least vsa_block_sparse_attn_bwd_workspace()
+ *     bytes (VSA_ERR_WORKSPACE otherwise), 8-byte aligned.
+ * Supported: tile_tokens in {32, 64}; head_dim in {64, 128}. No atomics:
+ * repeated calls give bit-identical results. */
+vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, const void* q,
+                                     const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, const int32_t* kv_idx,
+                                     const int32_t* kv_cnt, int32_t max_kv, const int32_t* q_idx,
+                                     const int32_t* q_cnt, int32_t list_mode, float softmax_scale,
+                                     void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ----- diagnostics --------------------------------------------------------- */
 const char* vsa_status_string(int32_t status);
 /* Message for the last failing call on this thread ("" if none). */

@@ -83,3 +83,46 @@ def transposed_lists(lay: Layout, lists: ListFn, B: int = 1):
                 for kt in sorted(set(int(t) for t in lists(b, h, qt))):
                     out[b][h][kt].append(qt)
     return out
+
+
+def key_tile_gradients(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, lay: Layout,
+                       lists: ListFn, sigma: float, b: int, h: int, kt: int, query_tiles=None):
+    """dK and dV rows [C, d] of key tile kt in (b, head h), from the same
+    definition as attention_backward restricted to that tile's columns: for
+    each query tile whose list holds kt, the weights P and the row sums
+    sum_l P_il dP_il are formed over the tile's full key set, and only the
+    columns of kt are accumulated. ``query_tiles`` (the query tiles whose
+    lists hold kt) is computed when not given.
+    """
+    C = lay.tile_tokens
+    order = token_order(lay).reshape(lay.n_tiles, C)
+    real = order >= 0
+    if query_tiles is None:
+        query_tiles = [qt for qt in range(lay.n_tiles) if kt in set(int(t) for t in lists(b, h, qt))]
+    dk = np.zeros((C, lay.head_dim))
+    dv = np.zeros((C, lay.head_dim))
+    own = np.nonzero(real[kt])[0]
+    for qt in query_tiles:
+        live = real[qt]
+        if not live.any():
+            continue
+        rows = slice(qt * C, (qt + 1) * C)
+        key_pos: List[int] = []
+        for t in lists(b, h, qt):
+            key_pos.extend(t * C + np.nonzero(real[t])[0])
+        key_pos = np.asarray(key_pos, dtype=np.int64)
+        qi = q[b, h, rows].astype(np.float64)[live]
+        do = dout[b, h, rows].astype(np.float64)[live]
+        kj = k[b, h, key_pos].astype(np.float64)
+        vj = v[b, h, key_pos].astype(np.float64)
+        _, _, p = attend_block(qi, kj, vj, sigma)
+        rowsum = (p * (do @ vj.T)).sum(axis=1, keepdims=True)
+        for pos in own:
+            cols = np.nonzero(key_pos == kt * C + pos)[0]
+            for c in cols:
+                pc = p[:, c]
+                dpc = do @ vj[c]
+                dsc = pc * (dpc - rowsum[:, 0])
+                dk[pos] += sigma * (dsc @ qi)
+                dv[pos] += pc @ do
+    return dk, dv

@@ -146,3 +146,16 @@ def head_sigmas(cfg: Workload, seed: Optional[int] = None) -> np.ndarray:
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     lo, hi = cfg.head_std_range
     return rng.uniform(lo, hi, size=cfg.heads)
+
+
+def make_grad(cfg: Workload, seed: Optional[int] = None, batch: Optional[int] = None,
+              std: float = 1.0):
+    """Upstream gradient dO: float32 [B, T*H*W, heads, d] in natural order,
+    i.i.d. N(0, std^2) from its own stream (seed + 7919 by default), rounded
+    to bf16 for bf16 workloads."""
+    b = cfg.batch if batch is None else batch
+    rng = np.random.default_rng((cfg.seed if seed is None else seed) + 7919)
+    x = rng.standard_normal((b, cfg.n_tokens, cfg.heads, cfg.head_dim), dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return round_to_bf16(x) if cfg.dtype == "bf16" else x

@@ -107,3 +107,47 @@ def test_workspace_query():
     assert n >= 40 * 1440 * 1440 * 4
     bad = vsa.Layout(T=0, H=45, W=80, heads=40, head_dim=128).c()
     assert B.lib().vsa_build_mask_topk_workspace(ctypes.byref(bad)) == 0
+
+
+def _fake(i):
+    """Distinct aligned fake device addresses (never dereferenced)."""
+    return ctypes.c_void_p(0x100000 + 0x1000 * i)
+
+
+def test_backward_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    ws = B.lib().vsa_block_sparse_attn_bwd_workspace(L)
+    assert ws == 2 * 24 * 32 * 52 * 8
+    q, k, v, o, do, lse, dq, dk, dv, w = (_fake(i) for i in range(10))
+    ok_tail = [ctypes.c_float(0.1), dq, dk, dv, w, ws, None]
+
+    def bwd(dtype=B.VSA_BF16, lists=(None, None, 0, None, None), mode=0, tail=None, lay_ref=L,
+            ptrs=None):
+        p = ptrs or (q, k, v, o, do, lse)
+        return _status("vsa_block_sparse_attn_bwd", lay_ref, dtype, *p, *lists, mode,
+                       *(tail or ok_tail))
+
+    # missing lse, partial lists, bad list_mode, fp8 dtype, NaN scale
+    assert bwd(ptrs=(q, k, v, o, do, None)) == B.VSA_ERR_INVALID
+    assert bwd(lists=(_fake(20), _fake(21), 8, None, None)) == B.VSA_ERR_INVALID
+    assert bwd(lists=(_fake(20), _fake(21), 8, _fake(22), _fake(23)), mode=2) == B.VSA_ERR_INVALID
+    assert bwd(dtype=B.VSA_FP8_E4M3) == B.VSA_ERR_UNSUPPORTED
+    assert bwd(tail=[ctypes.c_float(float("nan")), dq, dk, dv, w, ws, None]) == B.VSA_ERR_INVALID
+    # gradients aliasing inputs or each other, misaligned pointer
+    assert bwd(tail=[ctypes.c_float(0.1), q, dk, dv, w, ws, None]) == B.VSA_ERR_INVALID
+    assert bwd(tail=[ctypes.c_float(0.1), dq, dq, dv, w, ws, None]) == B.VSA_ERR_INVALID
+    assert bwd(ptrs=(ctypes.c_void_p(0x100008), k, v, o, do, lse)) == B.VSA_ERR_INVALID
+    # workspace missing / too small / misaligned
+    assert bwd(tail=[ctypes.c_float(0.1), dq, dk, dv, None, ws, None]) == B.VSA_ERR_WORKSPACE
+    assert bwd(tail=[ctypes.c_float(0.1), dq, dk, dv, w, ws - 1, None]) == B.VSA_ERR_WORKSPACE
+    assert bwd(tail=[ctypes.c_float(0.1), dq, dk, dv, ctypes.c_void_p(0x100004), ws, None]) \
+        == B.VSA_ERR_INVALID
+    # unsupported head_dim
+    lay96 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=96).c()
+    assert bwd(lay_ref=ctypes.byref(lay96)) == B.VSA_ERR_UNSUPPORTED
+    # transposed lists: null outputs, bad max_kv, bad list_mode
+    tl = "vsa_build_transposed_lists"
+    assert _status(tl, L, _fake(20), _fake(21), 8, 0, None, _fake(22), None) == B.VSA_ERR_INVALID
+    assert _status(tl, L, _fake(20), _fake(21), 0, 0, _fake(22), _fake(23), None) == B.VSA_ERR_INVALID
+    assert _status(tl, L, _fake(20), _fake(21), 8, 3, _fake(22), _fake(23), None) == B.VSA_ERR_INVALID

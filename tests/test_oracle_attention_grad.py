@@ -190,3 +190,16 @@ def test_items_restriction_and_transposed_lists(window_case):
             for qt in qts:
                 r = slice(qt * C, (qt + 1) * C)
                 assert np.array_equal(part[0][0, h, r], full[0][0, h, r])
+
+
+def test_key_tile_gradients_match_full(window_case):
+    """The one-key-tile form used for sampled checks at full size equals the
+    rows of the full backward."""
+    lay, B, lists, q, k, v, do = window_case
+    _, dK, dV = G.attention_backward(q, k, v, do, lay, lists, 0.45)
+    C = lay.tile_tokens
+    for h in range(lay.heads):
+        for kt in (0, 5, lay.n_tiles - 1):
+            dk, dv = G.key_tile_gradients(q, k, v, do, lay, lists, 0.45, 0, h, kt)
+            assert np.allclose(dk, dK[0, h, kt * C:(kt + 1) * C], atol=1e-12, rtol=1e-10)
+            assert np.allclose(dv, dV[0, h, kt * C:(kt + 1) * C], atol=1e-12, rtol=1e-10)
