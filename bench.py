@@ -13,7 +13,9 @@ whole timed step (permutes included in the time); roofline = the attention
 kernel's executed FLOP per launch / its average launch time (HIP events on
 the launch stream) against the 2.5 PFLOP/s dense bf16 peak; cpu_baseline =
 the fp64 oracle timed on this host on a seeded sample of (head, query tile)
-items of the sparse layer.
+items of the sparse layer. "backward" = the sparse layer's backward pass
+(dQ, dK, dV over the same lists) with its own roofline (algorithmic FLOP =
+2.5x the forward's) and the gradient oracle timed the same way.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                        [--only-headline] [--no-cpu-baseline] [--calib-copy]
@@ -105,6 +107,7 @@ def build_workload(name, torch, np, vsa):
         kv_idx, kv_cnt = vsa.build_mask_window(lay, radius)      # cached: built once per shape
         torch.cuda.synchronize()
         pairs_sparse = int(kv_cnt.sum().item()) * cfg.heads
+        state["lists"] = (kv_idx, kv_cnt)
 
     def layer(timer, dense=False):
         tq, tk, tv = (timer.run("permute", lambda x=x: vsa.tile_permute(lay, x)) for x in nat)
@@ -183,6 +186,63 @@ def build_workload(name, torch, np, vsa):
     return state
 
 
+def measure_backward(state, torch, vsa, steps, warmup):
+    """Backward of the sparse layer: the forward's output and lse, a seeded
+    upstream gradient, the transposed lists (built once per shape, like the
+    fixed lists), then `steps` timed calls of the whole backward (row
+    statistics, dQ and dK/dV kernels) with HIP events on the launch stream."""
+    cfg, lay = state["cfg"], state["lay"]
+    if cfg.mask not in ("window", "skiparse"):
+        return None
+    kv_idx, kv_cnt = state["lists"]
+    tq, tk, tv = (vsa.tile_permute(lay, x) for x in state["nat"])
+    out, lse = vsa.block_sparse_attn_fwd(lay, tq, tk, tv, kv_idx, kv_cnt, want_lse=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    dout = torch.randn(out.shape, generator=gen, device="cuda").to(out.dtype)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    q_idx, q_cnt = vsa.build_transposed_lists(lay, kv_idx, kv_cnt)
+    e1.record()
+    torch.cuda.synchronize()
+    t_lists = e0.elapsed_time(e1)
+    grads = tuple(torch.empty_like(x) for x in (tq, tk, tv))
+    ws = torch.empty(vsa.bwd_workspace_bytes(lay), dtype=torch.uint8, device="cuda")
+
+    def call():
+        vsa.block_sparse_attn_bwd(lay, tq, tk, tv, out, dout, lse, kv_idx, kv_cnt, q_idx, q_cnt,
+                                  grads=grads, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fwd_flops = state["flops"]()[1]["attn"]
+    alg, exe = 2.5 * fwd_flops, 3.5 * fwd_flops
+    del tq, tk, tv, out, lse, dout, grads, ws
+    return {
+        "workload": f"{cfg.name} sparse layer backward (dQ, dK, dV)",
+        "ms_per_layer": round(ms, 3),
+        "transposed_lists_ms": round(t_lists, 4),
+        "steps": steps,
+        "algorithmic_tflop": round(alg / 1e12, 3),
+        "executed_tflop": round(exe / 1e12, 3),
+        "executed_tflops": round(exe / (ms * 1e-3) / 1e12, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(alg / (ms * 1e-3) / 1e12, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alg / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+
+
 def measure(state, torch, steps, warmup):
     timer = Timer(torch)
     for _ in range(warmup):
@@ -203,8 +263,10 @@ def measure(state, torch, steps, warmup):
     return ms_step, wall, timer
 
 
-def cpu_baseline(name, np, seconds=12.0):
-    """Time the fp64 oracle on a seeded sample of sparse-layer (head, query tile) items."""
+def cpu_baseline(name, np, seconds=12.0, bwd_seconds=0.0):
+    """Time the fp64 oracle on a seeded sample of sparse-layer (head, query tile)
+    items: the forward, and for bwd_seconds > 0 also the gradient oracle.
+    Returns (forward record, backward record or None)."""
     from oracle import attention as OA
     from oracle import layout as OL
     from oracle import masks as OM
@@ -240,7 +302,7 @@ def cpu_baseline(name, np, seconds=12.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    return {
+    fwd = {
         "value": exec_flops(done_pairs, cfg.head_dim, lay.tile_tokens) / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -248,6 +310,29 @@ def cpu_baseline(name, np, seconds=12.0):
         "sample": f"{n_items} seeded (head, query-tile) items of the {name} sparse layer, "
                   f"fp64 numpy, {el:.1f}s wall",
     }
+    if bwd_seconds <= 0:
+        return fwd, None
+    # the gradient oracle on the same items' kind: one query tile's share of dQ, dK, dV
+    from oracle import attention_grad as OG
+    g = rng.standard_normal(xs[0].shape)
+    done_pairs = n_items = 0
+    t0 = time.time()
+    while time.time() - t0 < bwd_seconds:
+        h = int(rng.integers(0, len(heads)))
+        t = int(rng.integers(0, lay.n_tiles))
+        OG.attention_backward(*xs, g, lay, OA.shared_lists(lists), sigma, items=[(0, h, t)])
+        done_pairs += len(lists[t])
+        n_items += 1
+    el = time.time() - t0
+    bwd = {
+        "value": 2.5 * exec_flops(done_pairs, cfg.head_dim, lay.tile_tokens) / el / 1e12,
+        "unit": "TFLOP/s (algorithmic: 2.5x the forward's FLOP)",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n_items} seeded (head, query-tile) items of the {name} sparse layer backward, "
+                  f"fp64 numpy, {el:.1f}s wall",
+    }
+    return fwd, bwd
 
 
 def traffic_from_profiles(kernel_src_hash):
@@ -375,6 +460,9 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 2),
     }
+    if not args.only_headline:
+        log("timing the sparse layer backward")
+        out["backward"] = measure_backward(head, torch, vsa, args.steps, args.warmup)
     del head
     torch.cuda.empty_cache()
 
@@ -411,7 +499,11 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores")
-        out["cpu_baseline"] = cpu_baseline(args.workload, np)
+        fwd, bwd = cpu_baseline(args.workload, np,
+                                bwd_seconds=0.0 if args.only_headline else 6.0)
+        out["cpu_baseline"] = fwd
+        if bwd is not None and out.get("backward"):
+            out["backward"]["cpu_baseline"] = bwd
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
