@@ -32,6 +32,8 @@
 // transposed reads gather the tokens in that same order.
 #include <float.h>
 
+#include <type_traits>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -361,17 +363,64 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
 }
 
 // ---------------------------------------------------------------------------
+// Scheduling hint for a region of NM MFMAs: PRE LDS reads first, then after
+// each MFMA up to DS more LDS reads and NV VALU instructions.
+template <int NM, int PRE, int DS, int NV>
+__device__ __forceinline__ void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);          // DS reads
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);         // VALU
+  }
+}
+
+// Direct copies from HBM into LDS (buffer_load ... lds): each 64-lane copy
+// writes 1 KB of LDS, lane i at byte 16*i from the wave-uniform base.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+// s_waitcnt with vmcnt <= N (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // dK and dV: one workgroup (C/32 waves) per (b, head, key tile). One wave per
-// SIMD: the two accumulators and the K, V operands take most of 512 registers.
+// SIMD: the two accumulators and the K, V operands take most of 512 registers,
+// so the walk is software-pipelined inside the wave instead: step s is one
+// scheduling region holding the score MFMAs (S, dP) of block s, the VALU
+// work of block s (P, dS and their bf16 packing) and the dV / dK MFMAs of
+// block s-1, which do not depend on that VALU work. The
+// query blocks live in a ring of four LDS slots (block j in slot j % 4):
+// step s reads slots s (rows, row statistics) and s-1 (transposed reads).
+// bf16 inputs are copied straight into LDS two blocks ahead (step s starts
+// the copies of block s+2 and, before its barrier, waits for this wave's
+// copies of block s+1), so no staging registers are needed; fp32 inputs,
+// rounded on the way, go through registers one block ahead. Before the first
+// step the slot of "block -1" and its operands are zero, so the first step's
+// dV / dK products add nothing.
 template <int C, int D, bool F32IN>
 __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
-  constexpr int THREADS = 2 * C, SUB = C / 32;
+  constexpr int THREADS = 2 * C, WAVES = C / 32, SUB = C / 32, NBUF = 4;
   constexpr int ES = F32IN ? 4 : 2;
+  constexpr bool DMA = !F32IN;
   using RB = RowBlock<D, THREADS, F32IN>;
-  __shared__ uint4 q_lds[2][RB::LDS];
-  __shared__ uint4 g_lds[2][RB::LDS];
-  __shared__ float4 st_lds[2][16];        // 32 rows of {lse2, D}
+  // copies per 32-row block and tensor: RB::LDS chunks of 16 bytes, 64 a copy
+  constexpr int NI = (RB::LDS + 63) / 64;
+  constexpr int NIW0 = (NI + WAVES - 1) / WAVES;          // copies of wave 0 (the most)
+  constexpr int NIW1 = NI / WAVES;                        // of wave 1 (if any)
+  constexpr int VM0 = 2 * NIW0 + 1, VM1 = 2 * NIW1;       // per block, stats by wave 0
+  __shared__ uint4 q_s0[RB::LDS], q_s1[RB::LDS], q_s2[RB::LDS], q_s3[RB::LDS];
+  __shared__ uint4 g_s0[RB::LDS], g_s1[RB::LDS], g_s2[RB::LDS], g_s3[RB::LDS];
+  __shared__ float4 st_s0[16], st_s1[16], st_s2[16], st_s3[16];   // 32 rows of {lse2, D}
+  auto qbuf = [&](int i) -> uint4* { return i == 0 ? q_s0 : i == 1 ? q_s1 : i == 2 ? q_s2 : q_s3; };
+  auto gbuf = [&](int i) -> uint4* { return i == 0 ? g_s0 : i == 1 ? g_s1 : i == 2 ? g_s2 : g_s3; };
+  auto sbuf = [&](int i) -> float4* { return i == 0 ? st_s0 : i == 1 ? st_s1 : i == 2 ? st_s2 : st_s3; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -384,6 +433,7 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
   const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * D * ES, slice);
   const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * D * ES, slice);
   const rsrc_t rg = make_rsrc(static_cast<const char*>(a.dout) + row0 * D * ES, slice);
+  const rsrc_t rs = make_rsrc(a.rowstat + row0, (long long)L.n_padded * 8);
   const float2* rst = a.rowstat + row0;
 
   const int32_t* list = nullptr;
@@ -409,52 +459,90 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16_t{};
 
-  auto tile_of = [&](int b) -> int {
+  const int nblk = cnt * SUB;
+  // first query row of block b (clamped to the last block); wave-uniform
+  auto first_row = [&](int b) -> int {
+    b = min(b, nblk - 1);
     const int e = b / SUB;
-    return list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+    const int t = list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+    return __builtin_amdgcn_readfirstlane(t * C + 32 * (b % SUB));
   };
-  auto first_row = [&](int b) -> int { return tile_of(b) * C + 32 * (b % SUB); };
-
+  // copy j of this wave covers LDS chunks 64*(wave + WAVES*j) + lane: row
+  // p / RS, chunk p % RS of the padded rows (the pad chunk takes a copy of
+  // the row's last chunk; it is never read)
+  uint32_t cvoff[NIW0];
+  bool cvalid[NIW0];
+#pragma unroll
+  for (int j = 0; j < NIW0; ++j) {
+    const int p = 64 * (wave + WAVES * j) + lane;
+    const int r = p / RB::RS, c = p % RB::RS;
+    cvalid[j] = (wave + WAVES * j) < NI && p < RB::LDS;
+    cvoff[j] = (uint32_t)(r * D * ES + min(c, RB::CPR - 1) * 16);
+  }
   RB qio, gio;
   float2 streg = make_float2(0.0f, 0.0f);
-  const int nblk = cnt * SUB;
-  if (nblk > 0) {
-    const int r = first_row(0);
-    qio.load(rq, (uint32_t)(r * D * ES), tid);
-    gio.load(rg, (uint32_t)(r * D * ES), tid);
-    if (tid < 32) streg = rst[r + tid];
-    qio.store(q_lds[0], tid);
-    gio.store(g_lds[0], tid);
-    if (tid < 32) reinterpret_cast<float2*>(st_lds[0])[tid] = streg;
-  }
-  __syncthreads();
-  const int tro = tr_lane_offset<RB::RSE>(lane);
-  for (int b = 0; b < nblk; ++b) {
-    const int buf = b & 1;
-    if (b + 1 < nblk) {
-      const int r = first_row(b + 1);
+  auto copy_blk = [&](int b, uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
+    const int r = first_row(b);
+    if constexpr (DMA) {
+      const uint32_t soff = (uint32_t)(r * D * ES);
+#pragma unroll
+      for (int j = 0; j < NIW0; ++j) {
+        const int k = wave + WAVES * j;
+        if (j < NIW1 || wave == 0) {
+          if (cvalid[j]) {
+            dma16(rq, reinterpret_cast<char*>(qd) + 1024 * k, cvoff[j], soff);
+            dma16(rg, reinterpret_cast<char*>(gd) + 1024 * k, cvoff[j], soff);
+          }
+        }
+      }
+      if (wave == 0 && lane < 16) dma16(rs, sd, lane * 16, (uint32_t)(r * 8));
+    } else {
       qio.load(rq, (uint32_t)(r * D * ES), tid);
       gio.load(rg, (uint32_t)(r * D * ES), tid);
       if (tid < 32) streg = rst[r + tid];
     }
-    const uint4* qb = q_lds[buf] + l32 * RB::RS + half;
-    const uint4* gb = g_lds[buf] + l32 * RB::RS + half;
-    f32x16_t s = {}, dp = {};
+  };
+  auto store_regs = [&](uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
+    if constexpr (!DMA) {
+      qio.store(qd, tid);
+      gio.store(gd, tid);
+      if (tid < 32) reinterpret_cast<float2*>(sd)[tid] = streg;
+    }
+  };
+  // this wave's copies older than the last `batches` blocks' are complete
+  auto wait_copies = [&](auto batches) __attribute__((always_inline)) {
+    if constexpr (DMA) {
+      constexpr int NB = decltype(batches)::value;
+      if (wave == 0) wait_vmcnt<NB * VM0>();
+      else wait_vmcnt<NB * VM1>();
+    }
+  };
+  const int tro = tr_lane_offset<RB::RSE>(lane);
+  // S = Q . K^T and dP = dO . V^T of the block in slot (qs, gs)
+  auto scores = [&](const uint4* qs, const uint4* gs, f32x16_t& s, f32x16_t& dp)
+      __attribute__((always_inline)) {
+    const uint4* qb = qs + l32 * RB::RS + half;
+    const uint4* gb = gs + l32 * RB::RS + half;
+    s = f32x16_t{};
+    dp = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       s = mfma(qb[2 * ks], kf[ks], s);
       dp = mfma(gb[2 * ks], vf[ks], dp);
     }
-    // rows of this lane: query 8*g + 4*half + i of the block, g = 0..3
-    uint4 pp[2], dsp[2];
+  };
+  // P and dS as bf16 B operands (chunk c: rows 16*c + 8*(i/4) + 4*half + i%4
+  // of the block, i = 0..7)
+  auto grads = [&](const float4* st, const f32x16_t& s, const f32x16_t& dp, uint4 (&pk)[4])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float p[8], x[8];
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int g = 2 * c + gg;
-        const float4 s01 = st_lds[buf][4 * g + 2 * half];       // rows 8g+4half+0, +1
-        const float4 s23 = st_lds[buf][4 * g + 2 * half + 1];   // rows 8g+4half+2, +3
+        const float4 s01 = st[4 * g + 2 * half];       // rows 8g+4half+0, +1
+        const float4 s23 = st[4 * g + 2 * half + 1];   // rows 8g+4half+2, +3
         const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
         const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
@@ -464,25 +552,85 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
           x[4 * gg + i] = p[4 * gg + i] * (dp[r] - dd[i]);
         }
       }
-      pp[c] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
-      dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+      pk[c] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+      pk[2 + c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
     }
-    const uint16_t* gt = reinterpret_cast<const uint16_t*>(g_lds[buf]) + tro;
-    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(q_lds[buf]) + tro;
+  };
+  // dV^T += dO^T . P and dK^T += Q^T . dS for the block in slot (qs, gs)
+  auto accumulate = [&](const uint4* qs, const uint4* gs, const uint4 (&pk)[4])
+      __attribute__((always_inline)) {
+    const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro;
+    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dv[mt] = mfma(frag_t<RB::RSE>(gt, 32 * mt, c), pp[c], dv[mt]);
-        dk[mt] = mfma(frag_t<RB::RSE>(qt_, 32 * mt, c), dsp[c], dk[mt]);
+        dv[mt] = mfma(frag_t<RB::RSE>(gt, 32 * mt, c), pk[c], dv[mt]);
+        dk[mt] = mfma(frag_t<RB::RSE>(qt_, 32 * mt, c), pk[2 + c], dk[mt]);
       }
-    if (b + 1 < nblk) {
-      qio.store(q_lds[buf ^ 1], tid);
-      gio.store(g_lds[buf ^ 1], tid);
-      if (tid < 32) reinterpret_cast<float2*>(st_lds[buf ^ 1])[tid] = streg;
+  };
+
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  f32x16_t sc, dpc;
+  uint4 pk_a[4], pk_b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk_b[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (nblk > 0) {
+    for (int i = tid; i < RB::LDS; i += THREADS) {
+      q_s3[i] = make_uint4(0u, 0u, 0u, 0u);
+      g_s3[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    copy_blk(0, q_s0, g_s0, st_s0);
+    store_regs(q_s0, g_s0, st_s0);
+    if constexpr (DMA) {
+      copy_blk(1, q_s1, g_s1, st_s1);
+      wait_copies(C1{});
     }
     __syncthreads();
   }
+  // I = s % NBUF; even steps take (pk_b -> pk_a), odd ones the reverse
+  auto step = [&](auto phase, int s, const uint4 (&pprev)[4], uint4 (&pcur)[4])
+      __attribute__((always_inline)) {
+    constexpr int I = decltype(phase)::value;
+    constexpr int IN = (I + (DMA ? 2 : 1)) % NBUF;     // slot of the block copied in this step
+    constexpr int IP = (I + NBUF - 1) % NBUF;
+    copy_blk(s + (DMA ? 2 : 1), qbuf(IN), gbuf(IN), sbuf(IN));
+    scores(qbuf(I), gbuf(I), sc, dpc);
+    grads(sbuf(I), sc, dpc, pcur);
+    accumulate(qbuf(IP), gbuf(IP), pprev);
+    interleave_hint<2 * (D / 16) + 4 * (D / 32), 4, 2, 5>();
+    __builtin_amdgcn_sched_barrier(0);    // the staging stores wait for their loads here
+    store_regs(qbuf(IN), gbuf(IN), sbuf(IN));
+    wait_copies(C1{});                    // block s+1 is in LDS (this wave's share)
+    __syncthreads();
+  };
+  // the last block's operands end up in pk_b
+  for (int s = 0; s < nblk; s += NBUF) {
+    step(C0{}, s, pk_b, pk_a);
+    if (s + 1 >= nblk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk_b[i] = pk_a[i];
+      break;
+    }
+    step(C1{}, s + 1, pk_a, pk_b);
+    if (s + 2 >= nblk) break;
+    step(C2{}, s + 2, pk_b, pk_a);
+    if (s + 3 >= nblk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk_b[i] = pk_a[i];
+      break;
+    }
+    step(C3{}, s + 3, pk_a, pk_b);
+  }
+  if (nblk > 0) {
+    const int il = (nblk - 1) % NBUF;
+    accumulate(qbuf(il), gbuf(il), pk_b);
+  }
+  wait_copies(C0{});                      // no copy into LDS outlives the workgroup
+
   const bool real = row_is_real(L, tile_valid(L, kt), krow);
   const long long orow = row0 + kt * C + krow;
   store_rows_t<D, F32IN>(a.dk, orow, half, dk, a.scale, real);
