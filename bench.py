@@ -18,7 +18,7 @@ items of the sparse layer. "backward" = the sparse layer's backward pass
 2.5x the forward's) and the gradient oracle timed the same way.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                       [--only-headline] [--no-cpu-baseline] [--calib-copy]
+                       [--only-headline] [--backward] [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -238,7 +238,7 @@ def measure_backward(state, torch, vsa, steps, warmup):
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(alg / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": bwd_traffic_from_profiles(),
         },
     }
 
@@ -357,6 +357,26 @@ def traffic_from_profiles(kernel_src_hash):
     return int(rec["bytes_per_launch"])
 
 
+def bwd_traffic_from_profiles():
+    """HBM bytes per backward call (row statistics, dQ and dK/dV kernels) from
+    the committed counter summary, or None if the backward source changed."""
+    path = os.path.join(ROOT, "profiles", "attn_bwd_skiparse_768p_pmc.md")
+    with open(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn_bwd.hip"), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {}
+    try:
+        with open(path) as f:
+            for line in f:
+                if ":" in line and line.split(":", 1)[0] in ("bwd_source_sha256", "bytes_per_call"):
+                    k, v = line.split(":", 1)
+                    rec[k] = v.strip()
+    except OSError:
+        return None
+    if rec.get("bwd_source_sha256") != sha or "bytes_per_call" not in rec:
+        return None
+    return int(rec["bytes_per_call"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +387,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mall-cold", action="store_true",
                     help="skip the attention launches timed after a 512 MB scratch write")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the sparse-layer backward also with --only-headline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -460,7 +482,7 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 2),
     }
-    if not args.only_headline:
+    if not args.only_headline or args.backward:
         log("timing the sparse layer backward")
         out["backward"] = measure_backward(head, torch, vsa, args.steps, args.warmup)
     del head
