@@ -174,21 +174,23 @@ struct RowBlock {
   static constexpr int RS = CPR + 1;                // padded row stride, uint4
   static constexpr int RSE = RS * 8;                // padded row stride, bf16 elements
   static constexpr int CHUNKS = 32 * CPR;
-  static constexpr int PER_T = CHUNKS / THREADS;
+  static constexpr int PER_T = (CHUNKS + THREADS - 1) / THREADS;
   static constexpr int LDS = 32 * RS;               // uint4 per buffer
-  static_assert(CHUNKS % THREADS == 0, "whole chunks per thread");
+  static_assert(CHUNKS % THREADS == 0 || THREADS % CHUNKS == 0, "even split of the chunks");
   uint4 reg[PER_T];
 
   // block_off: byte offset of the block's first row inside the (b, head) slice
   __device__ __forceinline__ void load(rsrc_t r, uint32_t block_off, int tid) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) reg[i] = bload8<F32IN>(r, (tid + i * THREADS) * 8 * ES, block_off);
+    for (int i = 0; i < PER_T; ++i)
+      if (CHUNKS >= THREADS || tid < CHUNKS)
+        reg[i] = bload8<F32IN>(r, (tid + i * THREADS) * 8 * ES, block_off);
   }
   __device__ __forceinline__ void store(uint4* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int c = tid + i * THREADS;
-      lds[(c / CPR) * RS + c % CPR] = reg[i];
+      if (CHUNKS >= THREADS || c < CHUNKS) lds[(c / CPR) * RS + c % CPR] = reg[i];
     }
   }
 };
@@ -254,46 +256,115 @@ __device__ __forceinline__ void store_rows_t(void* dst, long long row, int half,
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup (C/32 waves) per (b, head, query tile).
-template <int C, int D, bool F32IN>
-__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Union of the QPW query-tile slots' lists (slot i's list: `list`, `cnt` of
+// the waves of slot i; null list = every tile) written to sched[] in
+// ascending order, each entry tile | (mask of slots listing it) << 24;
+// returns its length and sets `shared` when every entry is listed by every
+// active slot. `marks` (one byte per tile) and `scan` (one int per thread)
+// are scratch the caller may alias onto LDS it only uses afterwards.
+template <int QPW, int WPQ>
+__device__ int union_lists(int n_tiles, const int32_t* list, int cnt, int slot, bool active_slot,
+                           int active_mask, uint32_t* marks, int* scan, int* sched, int tid,
+                           int lane, bool& shared) {
+  constexpr int THREADS = 64 * QPW * WPQ;
+  const int words = (n_tiles + 3) >> 2;
+  for (int t = tid; t < words; t += THREADS) marks[t] = 0;
+  __syncthreads();
+  if (active_slot && (tid >> 6) % WPQ == 0) {
+    for (int i = lane; i < cnt; i += 64) {
+      const int t = list ? min(max(list[i], 0), n_tiles - 1) : i;
+      atomicOr(&marks[t >> 2], 1u << (8 * (t & 3) + slot));
+    }
+  }
+  __syncthreads();
+  auto mark = [&](int t) -> int { return (marks[t >> 2] >> (8 * (t & 3))) & 0xFF; };
+  const int per = (n_tiles + THREADS - 1) / THREADS;
+  const int lo = min(tid * per, n_tiles), hi = min(lo + per, n_tiles);
+  int mine = 0;
+  for (int t = lo; t < hi; ++t) mine += mark(t) != 0;
+  scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < THREADS; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int pos = scan[tid] - mine;
+  const int len = scan[THREADS - 1];
+  bool same = true;
+  for (int t = lo; t < hi; ++t) {
+    const int m = mark(t);
+    if (m) sched[pos++] = t | (m << 24);
+    same = same && (m == 0 || m == active_mask);
+  }
+  shared = __syncthreads_and(same) != 0;
+  return len;
+}
+
+// dQ: QPW consecutive query tiles per workgroup (C/32 waves each). With
+// QPW = 4 (shared and dense lists) the tiles walk the ascending union of
+// their lists once, each K/V block staged in LDS once for all of them; a
+// wave whose tile's list lacks a block skips its math. QPW = 1 walks one
+// tile's own list (per-head routed lists, where neighbouring tiles share
+// few key tiles). K and V go through registers into double-buffered padded
+// LDS rows, one barrier per 32-key block.
+template <int C, int D, bool F32IN, int QPW>
+__global__ __launch_bounds__(2 * C * QPW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
-  constexpr int THREADS = 2 * C, SUB = C / 32;
+  constexpr int WPQ = C / 32, THREADS = 64 * WPQ * QPW, SUB = C / 32;
   constexpr int ES = F32IN ? 4 : 2;
   using RB = RowBlock<D, THREADS, F32IN>;
   __shared__ uint4 k_lds[2][RB::LDS];
   __shared__ uint4 v_lds[2][RB::LDS];
+  __shared__ int sched[QPW > 1 ? 4096 : 1];
+  static_assert(QPW == 1 || THREADS * 4 <= RB::LDS * 16, "scan scratch fits one K buffer");
+  static_assert(QPW == 1 || 4096 <= RB::LDS * 16, "marks of 4096 tiles fit one V buffer");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
+  const int slot = wave / WPQ, rg = wave % WPQ;
   const int item = a.kv_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
                                                  : xcd_remap(blockIdx.x, n_work);
-  const int bh = item / L.n_tiles, qt = item - bh * L.n_tiles;
+  const int wg_per_bh = (L.n_tiles + QPW - 1) / QPW;
+  const int bh = item / wg_per_bh;
+  const int qt0 = (item - bh * wg_per_bh) * QPW;
+  const int qt = qt0 + slot;
+  const bool active = qt < L.n_tiles;
   const long long row0 = (long long)bh * L.n_padded;
   const long long slice = (long long)L.n_padded * D * ES;
   const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + row0 * D * ES, slice);
   const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * D * ES, slice);
   const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * D * ES, slice);
-  const rsrc_t rg = make_rsrc(static_cast<const char*>(a.dout) + row0 * D * ES, slice);
+  const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.dout) + row0 * D * ES, slice);
 
   const int32_t* list = nullptr;
   int cnt = L.n_tiles;
-  if (a.kv_idx) {
+  if (a.kv_idx && active) {
     const long long r = (a.list_mode ? (long long)bh * L.n_tiles : 0ll) + qt;
     list = a.kv_idx + r * a.max_kv;
     cnt = min(max(a.kv_cnt[r], 0), a.max_kv);
   }
+  int len = active ? cnt : 0;
+  bool shared = true;
+  if constexpr (QPW > 1) {
+    const int active_mask = (1 << min(max(L.n_tiles - qt0, 0), QPW)) - 1;
+    len = union_lists<QPW, WPQ>(L.n_tiles, a.kv_idx ? list : nullptr, cnt, slot, active,
+                                active_mask, reinterpret_cast<uint32_t*>(v_lds[1]),
+                                reinterpret_cast<int*>(k_lds[1]), sched, tid, lane, shared);
+  }
 
   // B operands Q^T and dO^T: row qrow, channels 16*ks + 8*half .. +7
-  const int qrow = 32 * wave + l32;
-  const uint32_t qoff = (uint32_t)((qt * C + qrow) * D * ES);
+  const int qrow = 32 * rg + l32;
+  const uint32_t qoff = (uint32_t)((min(qt, L.n_tiles - 1) * C + qrow) * D * ES);
   uint4 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     qf[ks] = bload8<F32IN>(rq, qoff + (16 * ks + 8 * half) * ES, 0);
-    gf[ks] = bload8<F32IN>(rg, qoff + (16 * ks + 8 * half) * ES, 0);
+    gf[ks] = bload8<F32IN>(rg_, qoff + (16 * ks + 8 * half) * ES, 0);
   }
-  const float2 st = a.rowstat[row0 + qt * C + qrow];
+  const float2 st = a.rowstat[row0 + min(qt, L.n_tiles - 1) * C + qrow];
   const float nl = -st.x, dd = st.y;
   const float sl2 = a.scale_log2;
 
@@ -301,19 +372,21 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16_t{};
 
-  auto tile_of = [&](int b) -> int {
+  const int nblk = len * SUB;
+  auto entry = [&](int b) -> int {
     const int e = b / SUB;
-    return list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+    if constexpr (QPW > 1) return sched[e];
+    else return (list ? min(max(list[e], 0), L.n_tiles - 1) : e) | (1 << 24);
   };
   auto block_off = [&](int b) -> uint32_t {
-    return (uint32_t)((tile_of(b) * C + 32 * (b % SUB)) * D * ES);
+    return (uint32_t)(((entry(b) & 0xFFFFFF) * C + 32 * (b % SUB)) * D * ES);
   };
 
   RB kio, vio;
-  const int nblk = cnt * SUB;
   if (nblk > 0) {
-    kio.load(rk, block_off(0), tid);
-    vio.load(rv, block_off(0), tid);
+    const uint32_t off = block_off(0);
+    kio.load(rk, off, tid);
+    vio.load(rv, off, tid);
     kio.store(k_lds[0], tid);
     vio.store(v_lds[0], tid);
   }
@@ -326,40 +399,45 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
       kio.load(rk, off, tid);
       vio.load(rv, off, tid);
     }
-    const uint32_t kbits = block_real_bits(L, tile_of(b), 32 * (b % SUB), lane, half);
-    const uint4* kb = k_lds[buf] + l32 * RB::RS + half;
-    const uint4* vb = v_lds[buf] + l32 * RB::RS + half;
-    f32x16_t s = {}, dp = {};
+    const int ent = entry(b);
+    if (QPW == 1 || (active && ((ent >> (24 + slot)) & 1))) {
+      const uint32_t kbits = block_real_bits(L, ent & 0xFFFFFF, 32 * (b % SUB), lane, half);
+      const uint4* kb = k_lds[buf] + l32 * RB::RS + half;
+      const uint4* vb = v_lds[buf] + l32 * RB::RS + half;
+      f32x16_t s = {}, dp = {};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      s = mfma(kb[2 * ks], qf[ks], s);
-      dp = mfma(vb[2 * ks], gf[ks], dp);
-    }
-    uint4 dsp[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * c + i;
-        const float p = ((kbits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) : 0.0f;
-        x[i] = p * (dp[r] - dd);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = mfma(kb[2 * ks], qf[ks], s);
+        dp = mfma(vb[2 * ks], gf[ks], dp);
       }
-      dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+      uint4 dsp[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * c + i;
+          const float p = ((kbits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) : 0.0f;
+          x[i] = p * (dp[r] - dd);
+        }
+        dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+      }
+      const uint16_t* kt = reinterpret_cast<const uint16_t*>(k_lds[buf]) + tro;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[mt] = mfma(frag_t<RB::RSE>(kt, 32 * mt, c), dsp[c], acc[mt]);
     }
-    const uint16_t* kt = reinterpret_cast<const uint16_t*>(k_lds[buf]) + tro;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[mt] = mfma(frag_t<RB::RSE>(kt, 32 * mt, c), dsp[c], acc[mt]);
     if (b + 1 < nblk) {
       kio.store(k_lds[buf ^ 1], tid);
       vio.store(v_lds[buf ^ 1], tid);
     }
     __syncthreads();
   }
-  const bool real = row_is_real(L, tile_valid(L, qt), qrow);
-  store_rows_t<D, F32IN>(a.dq, row0 + qt * C + qrow, half, acc, a.scale, real);
+  if (active) {
+    const bool real = row_is_real(L, tile_valid(L, qt), qrow);
+    store_rows_t<D, F32IN>(a.dq, row0 + qt * C + qrow, half, acc, a.scale, real);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -644,7 +722,12 @@ hipError_t launch_bwd_shape(const DevLayout& L, const BwdArgs& a, hipStream_t s)
   hipLaunchKernelGGL((rowstat_kernel<D, F32IN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
                      0, s, a.out, a.dout, a.lse, a.rowstat, rows);
   const int n_work = L.B * L.heads * L.n_tiles;
-  hipLaunchKernelGGL((dq_kernel<C, D, F32IN>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
+  if (a.list_mode == 1 || L.n_tiles > 4096) {
+    hipLaunchKernelGGL((dq_kernel<C, D, F32IN, 1>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
+  } else {
+    const int n_grp = L.B * L.heads * ((L.n_tiles + 3) / 4);
+    hipLaunchKernelGGL((dq_kernel<C, D, F32IN, 4>), dim3(n_grp), dim3(8 * C), 0, s, L, a, n_grp);
+  }
   hipLaunchKernelGGL((dkv_kernel<C, D, F32IN>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
   return hipGetLastError();
 }
