@@ -116,6 +116,49 @@ def quantize_tiles(x_tiled: np.ndarray, lay: Layout):
     return codes.reshape(B, lay.heads, lay.n_padded, d), scales
 
 
+def quantize_tiles_grouped(x_tiled: np.ndarray, lay: Layout, group):
+    """e4m3 quantisation with one scale per group of tiles (3D tiles only).
+
+    FPSAttention summary, Approach: FP8 quantisation on the same (big) tiles
+    as the sparsity, e.g. (6,8,8) tiles built from (1,8,8) ones. Reading: a
+    is the absmax over the real tokens of every tile in the group; scale
+    and codes then follow quantize_tiles with that a, and the group's scale
+    is stored for each of its tiles. Returns (codes, scales) as
+    quantize_tiles.
+    """
+    from .layout import tile_coords
+    order = token_order(lay).reshape(lay.n_tiles, lay.tile_tokens)
+    B = x_tiled.shape[0]
+    C, d = lay.tile_tokens, lay.head_dim
+    x = np.asarray(x_tiled, dtype=np.float32).reshape(B, lay.heads, lay.n_tiles, C, d)
+    gt, gh, gw = group
+    key = [tuple(c // g for c, g in zip(tile_coords(lay, t), (gt, gh, gw))) for t in range(lay.n_tiles)]
+    members = {}
+    for t, k in enumerate(key):
+        members.setdefault(k, []).append(t)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros((B, lay.heads, lay.n_tiles), dtype=np.float32)
+    f448 = np.float32(E4M3_MAX)
+    for tiles in members.values():
+        amax = np.zeros((B, lay.heads), dtype=np.float32)
+        for t in tiles:
+            real = order[t] >= 0
+            if real.any():
+                amax = np.maximum(amax, np.abs(x[:, :, t][:, :, real, :]).max(axis=(2, 3)))
+        nz = amax > 0
+        safe = np.where(nz, amax, np.float32(1.0)).astype(np.float32)
+        inv = np.where(nz, f448 / safe, np.float32(0.0)).astype(np.float32)   # fp32 divide
+        for t in tiles:
+            real = order[t] >= 0
+            y = (x[:, :, t] * inv[:, :, None, None]).astype(np.float32)          # fp32 multiply
+            y[:, :, ~real, :] = 0.0
+            c = e4m3_encode_array(y)
+            c[~nz] = 0
+            codes[:, :, t] = c
+            scales[:, :, t] = np.where(nz, safe / f448, np.float32(0.0)).astype(np.float32)
+    return codes.reshape(B, lay.heads, lay.n_padded, d), scales
+
+
 def dequantize_tiles(codes: np.ndarray, scales: np.ndarray, lay: Layout) -> np.ndarray:
     """decode(code) * scale, in float64, [B, heads, N_pad, d]."""
     table = decode_table()
