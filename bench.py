@@ -16,6 +16,8 @@ the fp64 oracle timed on this host on a seeded sample of (head, query tile)
 items of the sparse layer. "backward" = the sparse layer's backward pass
 (dQ, dK, dV over the same lists) with its own roofline (algorithmic FLOP =
 2.5x the forward's) and the gradient oracle timed the same way.
+"big_tiles_480p" = attention over FPSAttention-style (6,8,8) big-tile windows
+((6,6,6), (6,6,1), (3,3,1) and dense) at the 480p latent, bf16 and fp8.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                        [--only-headline] [--backward] [--no-cpu-baseline] [--calib-copy]
@@ -241,6 +243,68 @@ def measure_backward(state, torch, vsa, steps, warmup):
             "traffic": bwd_traffic_from_profiles(),
         },
     }
+
+
+def measure_big_tiles(torch, np, vsa, reps=5):
+    """480p latent (21x30x52, 12 heads, d = 128) on (1,8,8) tiles grouped six
+    along t into (6,8,8) big tiles: attention over the big-tile windows of
+    the pages' ablation ((6,6,6), (6,6,1), (3,3,1)) and dense, bf16, and the
+    (6,6,1) window in fp8 with one scale per big tile. Lists are built once
+    per window (as a denoising-step schedule would, switching between them);
+    each attention launch is timed with HIP events."""
+    from synth import CONFIGS, make_qkv
+    cfg = CONFIGS["window_480p"]
+    q, k, v = make_qkv(cfg)
+    lay = vsa.Layout(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, head_dim=cfg.head_dim,
+                     tile=(1, 8, 8))
+    info = vsa.layout_info(lay)
+    tq, tk, tv = (vsa.tile_permute(lay, to_dev(x, "bf16", torch, np)) for x in (q, k, v))
+    del q, k, v
+    group = (6, 1, 1)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {"workload": "21x30x52 latent, 12 heads, d=128, (1,8,8) tiles in (6,1,1) groups = (6,8,8) big tiles",
+           "windows": {}}
+    dense_ms = timed(lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv))
+    n = info.n_tiles
+    res["windows"]["dense"] = {"attn_ms": round(dense_ms, 4),
+                               "tflops": round(exec_flops(n * n * cfg.heads, 128, 64) / (dense_ms * 1e-3) / 1e12, 2)}
+    for ext in ((6, 6, 6), (6, 6, 1), (3, 3, 1)):
+        idx, cnt = vsa.build_mask_window_grouped(lay, group, ext)
+        pairs = int(cnt.sum().item()) * cfg.heads
+        # big-tile windows differ between neighbouring query tiles (which lie
+        # along w), so each tile walks its own list (list_mode 2)
+        per_tile = True
+        ms = timed(lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv, idx, cnt, per_tile_walk=per_tile))
+        f = exec_flops(pairs, 128, 64)
+        entry = {"attn_ms": round(ms, 4), "density": round(pairs / (n * n * cfg.heads), 4),
+                 "walk": "per query tile",
+                 "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                 "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "speedup_vs_dense": round(dense_ms / ms, 3)}
+        if ext == (6, 6, 1):
+            (qc, qs), (kc, ks) = (vsa.quant_fp8_tiles_grouped(lay, x, group) for x in (tq, tk))
+            vc, vs = vsa.quant_fp8_tiles_grouped(lay, tv, group, v_operand=True)
+            qms = timed(lambda: vsa.quant_fp8_tiles_grouped(lay, tq, group))
+            fms = timed(lambda: vsa.block_sparse_attn_fwd(lay, qc, kc, vc, idx, cnt, scales=(qs, ks, vs),
+                                                          v_operand=True, per_tile_walk=per_tile))
+            entry["fp8"] = {"attn_ms": round(fms, 4), "quant_ms_per_tensor": round(qms, 4),
+                            "tflops": round(f / (fms * 1e-3) / 1e12, 2),
+                            "frac_of_fp8_peak": round(f / (fms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                            "speedup_vs_dense_bf16": round(dense_ms / fms, 3)}
+        res["windows"]["x".join(str(e) for e in ext)] = entry
+    del tq, tk, tv
+    return res
 
 
 def measure(state, torch, steps, warmup):
@@ -518,6 +582,9 @@ def main():
             del st
             torch.cuda.empty_cache()
         out["per_workload"] = per
+        log("timing big-tile windows")
+        out["big_tiles_480p"] = measure_big_tiles(torch, np, vsa)
+        log(f"big tiles: {out['big_tiles_480p']}")
 
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores")

@@ -25,7 +25,8 @@ from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, 
 
 __all__ = [
     "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
-    "quant_fp8_tiles", "block_sparse_attn_fwd", "build_transposed_lists", "bwd_workspace_bytes",
+    "quant_fp8_tiles", "block_sparse_attn_fwd", "build_mask_window_grouped",
+    "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
     "block_sparse_attn_bwd", "VsaError", "EXPORTED",
     "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
 ]
@@ -104,6 +105,42 @@ def build_mask_window(lay: Layout, radius: Tuple[int, int, int], max_kv: Optiona
     return kv_idx, kv_cnt
 
 
+def build_mask_window_grouped(lay: Layout, group: Tuple[int, int, int],
+                              extent: Tuple[int, int, int], max_kv: Optional[int] = None,
+                              stream=None):
+    """Big-tile window lists (vsa_build_mask_window_grouped): groups of `group`
+    layout tiles, window extents counted in groups. Returns (kv_idx, kv_cnt)."""
+    info = layout_info(lay)
+    n = info.n_tiles
+    if max_kv is None:
+        grid = (info.tiles_t, info.tiles_h, info.tiles_w)
+        max_kv = 1
+        for m, g, e in zip(grid, group, extent):
+            max_kv *= min(m, g * e)
+    kv_idx = torch.empty((n, max_kv), dtype=torch.int32, device="cuda")
+    kv_cnt = torch.empty((n,), dtype=torch.int32, device="cuda")
+    c = lay.c()
+    check(lib().vsa_build_mask_window_grouped(ctypes.byref(c), *(int(x) for x in group),
+                                              *(int(x) for x in extent), int(max_kv),
+                                              _ptr(kv_idx), _ptr(kv_cnt), _stream(stream)))
+    return kv_idx, kv_cnt
+
+
+def quant_fp8_tiles_grouped(lay: Layout, x_tiled: torch.Tensor, group: Tuple[int, int, int],
+                            stream=None, v_operand: bool = False):
+    """e4m3 codes with one scale per group of tiles (vsa_quant_fp8_tiles_grouped);
+    the group's scale is stored for each of its tiles."""
+    info = layout_info(lay)
+    codes = torch.empty(x_tiled.shape, dtype=torch.uint8, device=x_tiled.device)
+    scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32,
+                         device=x_tiled.device)
+    c = lay.c()
+    check(lib().vsa_quant_fp8_tiles_grouped(ctypes.byref(c), *(int(x) for x in group), _ptr(x_tiled),
+                                            _ptr(codes), _ptr(scales), int(bool(v_operand)),
+                                            _stream(stream)))
+    return codes, scales
+
+
 def topk_workspace_bytes(lay: Layout) -> int:
     c = lay.c()
     return int(lib().vsa_build_mask_topk_workspace(ctypes.byref(c)))
@@ -158,14 +195,17 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
                           softmax_scale: Optional[float] = None,
                           scales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                           want_lse: bool = False, out: Optional[torch.Tensor] = None,
-                          lse: Optional[torch.Tensor] = None, stream=None, v_operand: bool = False):
+                          lse: Optional[torch.Tensor] = None, stream=None, v_operand: bool = False,
+                          per_tile_walk: bool = False):
     """Block-sparse attention forward (vsa_block_sparse_attn_fwd).
 
     q/k/v tiled; float32 -> float32 out, bfloat16 -> bfloat16 out, uint8 e4m3
     codes (with ``scales`` = (q_scale, k_scale, v_scale)) -> bfloat16 out;
     ``v_operand``: v holds codes from quant_fp8_tiles(..., v_operand=True).
     kv_idx 2-D [n_tiles, max_kv] = one shared table; 4-D [B, heads, n_tiles,
-    max_kv] = per-(b, head) lists; None = dense. Returns (out, lse or None).
+    max_kv] = per-(b, head) lists; None = dense. ``per_tile_walk`` (2-D
+    tables only): each query tile walks its own list (list_mode 2).
+    Returns (out, lse or None).
     """
     info = layout_info(lay)
     if softmax_scale is None:
@@ -188,7 +228,7 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
                           device=q.device)
     if kv_idx is not None:
         max_kv = kv_idx.shape[-1]
-        list_mode = 0 if kv_idx.dim() == 2 else 1
+        list_mode = (2 if per_tile_walk else 0) if kv_idx.dim() == 2 else 1
     else:
         max_kv, list_mode = 0, 0
     qs, ks, vs = scales if scales is not None else (None, None, None)

@@ -113,7 +113,7 @@ __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs
   w.cnt = 0;
   if (w.active) {
     if (a.kv_idx) {
-      const long long row = (a.list_mode ? (long long)w.bh * L.n_tiles : 0ll) + w.qt;
+      const long long row = (a.list_mode == 1 ? (long long)w.bh * L.n_tiles : 0ll) + w.qt;
       w.list = a.kv_idx + row * a.max_kv;
       w.cnt = min(max(a.kv_cnt[row], 0), a.max_kv);
     } else {
@@ -1162,8 +1162,9 @@ hipError_t launch_bf16_shape(const DevLayout& L, const AttnArgs& a, bool grouped
 
 hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStream_t s) {
   // Shared (head-invariant) or dense lists: neighbouring query tiles share key
-  // tiles, so four query tiles walk their union together. Routed lists: one
-  // wave per query tile.
+  // tiles, so four query tiles walk their union together. Routed lists, and
+  // shared tables the caller marks as walked per tile (list_mode 2): one
+  // query tile per workgroup.
   const bool grouped = (a.kv_idx == nullptr || a.list_mode == 0) && L.n_tiles <= 4096;
   if (dtype == 3) {   // e4m3 with V codes in the P.V operand layout
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;

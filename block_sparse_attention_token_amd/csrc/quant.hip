@@ -42,7 +42,10 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
 // tokens in the order the fp8 P.V product takes them: position
 // p = 32 h + 16 A + 4 B + r holds token t = 32 A + 8 B + 4 h + r
 // (h, r in 0..1 and 0..3, A in 0..1, B in 0..3).
-template <bool VOP>
+// PRESET: the tile's absmax a was written into scales[] by group_absmax_kernel
+// (one a per group of tiles); the kernel reads it, then overwrites the entry
+// with the scale, so each entry is touched by its own workgroup only.
+template <bool VOP, bool PRESET>
 __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint4* __restrict__ x,
                                                          uint2* __restrict__ codes,
                                                          float* __restrict__ scales) {
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
 
   __shared__ float red[kThreads / 64];
   float amax = 0.0f;
-  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+  for (int idx = threadIdx.x; !PRESET && idx < total; idx += kThreads) {
     const int r = idx / chunks;
     if (!row_is_real(L, tv, r)) continue;
     const uint4 w = x[(row0 + r) * chunks + (idx - r * chunks)];
@@ -75,6 +78,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
   float a = red[0];
 #pragma unroll
   for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+  if constexpr (PRESET) a = scales[(long long)(b * L.heads + head) * L.n_tiles + tile];
+  __syncthreads();                                   // every thread has read the preset a
 
   const float inv = (a > 0.0f) ? __fdiv_rn(448.0f, a) : 0.0f;
   if (threadIdx.x == 0) {
@@ -121,17 +126,84 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
   }
 }
 
+// One workgroup per (batch, head, group of gt x gh x gw tiles): the absmax
+// over the real rows of every tile of the group, written to scales[] for
+// each member tile (3D tiles only).
+__global__ __launch_bounds__(kThreads) void group_absmax_kernel(DevLayout L, int gt, int gh, int gw,
+                                                                const uint4* __restrict__ x,
+                                                                float* __restrict__ scales) {
+  const int ngh = (L.nth + gh - 1) / gh, ngw = (L.ntw + gw - 1) / gw;
+  const int grp = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int A = grp / (ngh * ngw), Bg = (grp / ngw) % ngh, Cg = grp % ngw;
+  const int a0 = A * gt, a1 = min(a0 + gt, L.ntt);
+  const int b0 = Bg * gh, b1 = min(b0 + gh, L.nth);
+  const int c0 = Cg * gw, c1 = min(c0 + gw, L.ntw);
+  const int chunks = L.d >> 3;
+  const int total = L.C * chunks;
+  const long long bh = (long long)(b * L.heads + head);
+  float amax = 0.0f;
+  for (int ta = a0; ta < a1; ++ta)
+    for (int tb = b0; tb < b1; ++tb)
+      for (int tc = c0; tc < c1; ++tc) {
+        const int tile = (ta * L.nth + tb) * L.ntw + tc;
+        const TileValid tv = tile_valid(L, tile);
+        const long long row0 = bh * L.n_padded + (long long)tile * L.C;
+        for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+          const int r = idx / chunks;
+          if (!row_is_real(L, tv, r)) continue;
+          const uint4 w = x[(row0 + r) * chunks + (idx - r * chunks)];
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            amax = fmaxf(amax, fabsf(bf16_lo(ws[e])));
+            amax = fmaxf(amax, fabsf(bf16_hi(ws[e])));
+          }
+        }
+      }
+  __shared__ float red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  float a = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+  const int members = (a1 - a0) * (b1 - b0) * (c1 - c0);
+  for (int m = threadIdx.x; m < members; m += kThreads) {
+    const int nb = b1 - b0, nc = c1 - c0;
+    const int ta = a0 + m / (nb * nc), tb = b0 + (m / nc) % nb, tc = c0 + m % nc;
+    scales[bh * L.n_tiles + (ta * L.nth + tb) * L.ntw + tc] = a;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_fp8_grouped(const DevLayout& L, int gt, int gh, int gw, const void* x,
+                                    uint8_t* codes, float* scales, bool v_operand, hipStream_t s) {
+  const int ng = ((L.ntt + gt - 1) / gt) * ((L.nth + gh - 1) / gh) * ((L.ntw + gw - 1) / gw);
+  hipLaunchKernelGGL(group_absmax_kernel, dim3(ng, L.heads, L.B), dim3(kThreads), 0, s, L, gt, gh, gw,
+                     static_cast<const uint4*>(x), scales);
+  dim3 grid(L.n_tiles, L.heads, L.B);
+  if (v_operand) {
+    if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(kThreads), 0, s, L,
+                       static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
+  } else {
+    hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(kThreads), 0, s, L,
+                       static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
                             bool v_operand, hipStream_t s) {
   dim3 grid(L.n_tiles, L.heads, L.B);
   if (v_operand) {
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_kernel<true>, grid, dim3(kThreads), 0, s, L,
+    hipLaunchKernelGGL((quant_kernel<true, false>), grid, dim3(kThreads), 0, s, L,
                        static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
   } else {
-    hipLaunchKernelGGL(quant_kernel<false>, grid, dim3(kThreads), 0, s, L,
+    hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(kThreads), 0, s, L,
                        static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
   }
   return hipGetLastError();

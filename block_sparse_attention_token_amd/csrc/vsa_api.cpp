@@ -159,6 +159,40 @@ vsa_status vsa_build_mask_window(const vsa_layout* layout, int32_t rt, int32_t r
                     "vsa_build_mask_window");
 }
 
+// Longest list of a grouped window: per axis the most tiles any query's
+// window covers, multiplied over the axes (the window is a box).
+static int longest_grouped_list(const vsa::DevLayout& L, int gt, int gh, int gw, int et, int eh,
+                                int ew) {
+  auto axis = [](int n, int g, int e) {
+    const int ng = (n + g - 1) / g;
+    int best = 0;
+    for (int X = 0; X < ng; ++X) {
+      const int lo = std::max(X - (e - 1) / 2, 0), hi = std::min(X - (e - 1) / 2 + e - 1, ng - 1);
+      best = std::max(best, std::min((hi + 1) * g, n) - lo * g);
+    }
+    return best;
+  };
+  return axis(L.ntt, gt, et) * axis(L.nth, gh, eh) * axis(L.ntw, gw, ew);
+}
+
+vsa_status vsa_build_mask_window_grouped(const vsa_layout* layout, int32_t gt, int32_t gh,
+                                         int32_t gw, int32_t et, int32_t eh, int32_t ew,
+                                         int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt,
+                                         void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (L.kind != VSA_TILE3D) return fail(VSA_ERR_UNSUPPORTED, "grouped windows need VSA_TILE3D");
+  if (!kv_idx || !kv_cnt) return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must be non-NULL");
+  if (gt < 1 || gh < 1 || gw < 1 || et < 1 || eh < 1 || ew < 1)
+    return fail(VSA_ERR_INVALID, "group sizes and extents must be >= 1");
+  const int need = longest_grouped_list(L, gt, gh, gw, et, eh, ew);
+  if (max_kv < need) return fail(VSA_ERR_INVALID, "max_kv %d < longest list %d", max_kv, need);
+  return hip_status(vsa::launch_mask_window_grouped(L, gt, gh, gw, et, eh, ew, max_kv, kv_idx, kv_cnt,
+                                                    static_cast<hipStream_t>(stream)),
+                    "vsa_build_mask_window_grouped");
+}
+
 size_t vsa_build_mask_topk_workspace(const vsa_layout* layout) {
   vsa::DevLayout L;
   if (derive(layout, &L, nullptr) != VSA_OK) return 0;
@@ -224,6 +258,26 @@ vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, 
   return quant_fp8(layout, x_tiled, codes, scales, true, stream, "vsa_quant_fp8_tiles_v");
 }
 
+vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int32_t gh, int32_t gw,
+                                       const void* x_tiled, uint8_t* codes, float* scales,
+                                       int32_t v_operand, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (L.kind != VSA_TILE3D) return fail(VSA_ERR_UNSUPPORTED, "grouped scales need VSA_TILE3D");
+  if (gt < 1 || gh < 1 || gw < 1) return fail(VSA_ERR_INVALID, "group sizes must be >= 1");
+  if (!x_tiled || !codes || !scales) return fail(VSA_ERR_INVALID, "x_tiled, codes and scales must be non-NULL");
+  if (!aligned16(x_tiled) || ((uintptr_t)codes & (v_operand ? 15u : 7u)))
+    return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (L.d % 8) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (v_operand && (L.C != 64 || L.d != 128))
+    return fail(VSA_ERR_UNSUPPORTED, "the P.V operand layout needs 64-token tiles and head_dim 128");
+  if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large");
+  return hip_status(vsa::launch_quant_fp8_grouped(L, gt, gh, gw, x_tiled, codes, scales, v_operand != 0,
+                                                  static_cast<hipStream_t>(stream)),
+                    "vsa_quant_fp8_tiles_grouped");
+}
+
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,
@@ -239,7 +293,7 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
   if ((kv_idx == nullptr) != (kv_cnt == nullptr))
     return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
   if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
-  if (list_mode != 0 && list_mode != 1) return fail(VSA_ERR_INVALID, "list_mode must be 0 or 1");
+  if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
   if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP)
     return fail(VSA_ERR_INVALID, "unknown dtype %d", dtype);

@@ -131,6 +131,11 @@ hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float 
 size_t route_workspace_bytes(const DevLayout& L);
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
                             bool v_operand, hipStream_t s);
+hipError_t launch_mask_window_grouped(const DevLayout& L, int gt, int gh, int gw, int et, int eh,
+                                      int ew, int max_kv, int32_t* kv_idx, int32_t* kv_cnt,
+                                      hipStream_t s);
+hipError_t launch_quant_fp8_grouped(const DevLayout& L, int gt, int gh, int gw, const void* x,
+                                    uint8_t* codes, float* scales, bool v_operand, hipStream_t s);
 
 struct AttnArgs {
   const void* q;
@@ -142,7 +147,7 @@ struct AttnArgs {
   const int32_t* kv_idx;   // null: dense
   const int32_t* kv_cnt;
   int max_kv;
-  int list_mode;           // 0 shared table, 1 per (batch, head)
+  int list_mode;           // 0 shared table, 1 per (batch, head), 2 shared table walked per tile
   float scale_log2;        // softmax scale * log2(e)
   void* out;
   float* lse;

@@ -134,6 +134,27 @@ vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void*
 vsa_status vsa_build_mask_window(const vsa_layout* layout, int32_t rt, int32_t rh, int32_t rw,
                                  int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, void* stream);
 
+/* ----- big tiles: grouped windows ---------------------------------------------
+ * FPSAttention (Approach, and its ablation table): sparsity and quantisation
+ * share one tile granularity, changed across denoising steps; larger,
+ * hardware-friendly (6,8,8) tiles and asymmetric windows such as (6,6,1).
+ * A big tile is a group of gt x gh x gw consecutive tiles of a VSA_TILE3D
+ * layout (e.g. (6,1,1) groups of (1,8,8) tiles = (6,8,8) tiles, the last
+ * group along an axis possibly shorter), so the attention kernels keep their
+ * 64-token tiles. A window extent e (per axis, >= 1) counts groups: around
+ * the query tile's group X it covers groups X - (e-1)/2 .. X - (e-1)/2 + e - 1
+ * (integer division; the extra group of an even extent on the high side),
+ * clipped at the grid edge without shifting. Each query tile lists every
+ * tile of every covered group, ascending.
+ *   kv_idx int32 [n_tiles, max_kv], kv_cnt int32 [n_tiles] (head-invariant,
+ *   list_mode 0 for the attention call).
+ * VSA_ERR_INVALID if max_kv is smaller than the longest list, a group size or
+ * an extent is < 1; VSA_ERR_UNSUPPORTED for VSA_SKIPARSE2D layouts. */
+vsa_status vsa_build_mask_window_grouped(const vsa_layout* layout, int32_t gt, int32_t gh,
+                                         int32_t gw, int32_t et, int32_t eh, int32_t ew,
+                                         int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt,
+                                         void* stream);
+
 /* ----- S3 / S4: adaptive routing ---------------------------------------------
  * VSA page, Research Type row (coarse selection of key blocks per query
  * block); FVAttn summary (Top-p routing with a Top-k safety floor, per head).
@@ -183,6 +204,17 @@ vsa_status vsa_quant_fp8_tiles(const vsa_layout* layout, const void* x_tiled, ui
 vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,
                                  float* scales, void* stream);
 
+/* vsa_quant_fp8_tiles_grouped: as vsa_quant_fp8_tiles (v_operand 0) or
+ * vsa_quant_fp8_tiles_v (v_operand 1), with one scale per big tile: a is the
+ * absmax over the real tokens of all gt x gh x gw tiles of the group (see
+ * vsa_build_mask_window_grouped), and the group's scale fl32(a / 448) is
+ * written for each of its tiles, so the attention call takes the result
+ * unchanged (FPSAttention, Approach: FP8 on the same tiles as the sparsity).
+ * VSA_TILE3D layouts only; VSA_ERR_INVALID for group sizes < 1. */
+vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int32_t gh, int32_t gw,
+                                       const void* x_tiled, uint8_t* codes, float* scales,
+                                       int32_t v_operand, void* stream);
+
 /* ----- S6: block-sparse attention forward --------------------------------------
  * The flash-style, FlashAttention-compatible sparse attention every page
  * builds on (OSP-Next wiki TL;DR; FPSAttention, Approach; VSA, Research
@@ -199,6 +231,10 @@ vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, 
  *   kv_idx / kv_cnt: lists as written by vsa_build_mask_window (list_mode 0:
  *     one table [n_tiles, max_kv] shared by every batch and head) or by
  *     vsa_build_mask_topk (list_mode 1: [B, heads, n_tiles, max_kv]).
+ *     list_mode 2 takes a list_mode 0 table but walks each query tile's list
+ *     on its own instead of four neighbouring tiles' union (faster where
+ *     neighbouring query tiles share few key tiles, e.g. narrow big-tile
+ *     windows); the result is the same.
  *     Both NULL: dense attention (every tile). Indices must lie in
  *     [0, n_tiles) and counts in [0, max_kv]; the kernel does not re-check them.
  *   out: [B, heads, n_padded, d]; pad query rows and rows with an empty list

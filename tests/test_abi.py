@@ -85,7 +85,7 @@ def test_argument_errors_before_launch():
     args = [FAKE, FAKE, FAKE, None, None, None]
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, None, 8, 0,
                    ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
-    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 2,
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 3,
                    ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_FP8_E4M3, *args, FAKE, FAKE, 8, 0,
                    ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
@@ -151,3 +151,25 @@ def test_backward_argument_errors_before_launch():
     assert _status(tl, L, _fake(20), _fake(21), 8, 0, None, _fake(22), None) == B.VSA_ERR_INVALID
     assert _status(tl, L, _fake(20), _fake(21), 0, 0, _fake(22), _fake(23), None) == B.VSA_ERR_INVALID
     assert _status(tl, L, _fake(20), _fake(21), 8, 3, _fake(22), _fake(23), None) == B.VSA_ERR_INVALID
+
+
+def test_big_tile_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128, tile=(1, 8, 8)).c()
+    L = ctypes.byref(lay)
+    g = "vsa_build_mask_window_grouped"
+    # (6,1,1) groups of (1,8,8) tiles, extents (6,6,1): the longest list is 4*4*1 groups
+    # = 21 frames (all 4 groups along t) * 4 rows * 1 column
+    assert _status(g, L, 6, 1, 1, 6, 6, 1, 83, _fake(1), _fake(2), None) == B.VSA_ERR_INVALID
+    assert _status(g, L, 6, 1, 1, 6, 6, 0, 84, _fake(1), _fake(2), None) == B.VSA_ERR_INVALID
+    assert _status(g, L, 0, 1, 1, 6, 6, 1, 84, _fake(1), _fake(2), None) == B.VSA_ERR_INVALID
+    assert _status(g, L, 6, 1, 1, 6, 6, 1, 84, None, _fake(2), None) == B.VSA_ERR_INVALID
+    sk = vsa.Layout(T=21, H=48, W=80, heads=2, head_dim=128, kind="skiparse2d").c()
+    assert _status(g, ctypes.byref(sk), 1, 1, 1, 1, 1, 1, 315, _fake(1), _fake(2), None) \
+        == B.VSA_ERR_UNSUPPORTED
+    q = "vsa_quant_fp8_tiles_grouped"
+    assert _status(q, L, 6, 0, 1, _fake(1), _fake(2), _fake(3), 0, None) == B.VSA_ERR_INVALID
+    assert _status(q, L, 6, 1, 1, None, _fake(2), _fake(3), 0, None) == B.VSA_ERR_INVALID
+    assert _status(q, L, 6, 1, 1, _fake(1), ctypes.c_void_p(0x100008), _fake(3), 1, None) \
+        == B.VSA_ERR_INVALID
+    assert _status(q, ctypes.byref(sk), 1, 1, 1, _fake(1), _fake(2), _fake(3), 0, None) \
+        == B.VSA_ERR_UNSUPPORTED
