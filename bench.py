@@ -117,8 +117,11 @@ def build_workload(name, torch, np, vsa):
             if dense:
                 out, _ = timer.run("attn_dense", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv))
             else:
-                out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv,
-                                                                              kv_idx, kv_cnt))
+                # 3D windows differ between neighbouring query tiles: each tile walks its
+                # own list (list_mode 2); Skiparse tiles of a group share one list and
+                # walk it four at a time
+                out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(
+                    lay, tq, tk, tv, kv_idx, kv_cnt, per_tile_walk=cfg.mask == "window"))
         elif cfg.mask == "topk":
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(lay, tq, tk, top_k=cfg.top_k))
             state["cnt"] = cnt
@@ -282,13 +285,14 @@ def measure_big_tiles(torch, np, vsa, reps=5):
     for ext in ((6, 6, 6), (6, 6, 1), (3, 3, 1)):
         idx, cnt = vsa.build_mask_window_grouped(lay, group, ext)
         pairs = int(cnt.sum().item()) * cfg.heads
-        # big-tile windows differ between neighbouring query tiles (which lie
-        # along w), so each tile walks its own list (list_mode 2)
-        per_tile = True
+        # neighbouring query tiles lie along w: with a narrow w extent their
+        # lists barely overlap, so each tile walks its own list (list_mode 2);
+        # a wide one keeps the union walk of four tiles
+        per_tile = ext[2] < 3
         ms = timed(lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv, idx, cnt, per_tile_walk=per_tile))
         f = exec_flops(pairs, 128, 64)
         entry = {"attn_ms": round(ms, 4), "density": round(pairs / (n * n * cfg.heads), 4),
-                 "walk": "per query tile",
+                 "walk": "per query tile" if per_tile else "unions of four query tiles",
                  "tflops": round(f / (ms * 1e-3) / 1e12, 2),
                  "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "speedup_vs_dense": round(dense_ms / ms, 3)}

@@ -65,7 +65,7 @@ def _compare(out_gpu, O_ref, lse_gpu, L_ref, olay, items, rel_gate=REL_L2, abs_g
     return mae, rl2
 
 
-def _run_shared(name, radius, n_items, dense=False, seed=0, full=False):
+def _run_shared(name, radius, n_items, dense=False, seed=0, full=False, per_tile=False):
     cfg = CONFIGS[name]
     olay, blay = layouts(cfg)
     q, k, v = inputs(name)
@@ -80,7 +80,8 @@ def _run_shared(name, radius, n_items, dense=False, seed=0, full=False):
         out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, want_lse=True)
     else:
         di, dc = lists_to_device(idx, cnt)
-        out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True)
+        out, lse = vsa.block_sparse_attn_fwd(blay, qd, kd, vd, di, dc, want_lse=True,
+                                             per_tile_walk=per_tile)
     torch.cuda.synchronize()
     items = None if full else _items(olay, n_items, seed,
                                      must=[(0, 0, 0), (0, olay.heads - 1, olay.n_tiles - 1)])
@@ -98,6 +99,12 @@ def test_tiny_f32_full():
 
 def test_window_480p_sampled():
     _run_shared("window_480p", (1, 2, 2), 150, seed=3)
+
+
+def test_window_480p_per_tile_walk_sampled():
+    """The launch bench.py times for the 480p window workload: the shared
+    table walked per query tile (list_mode 2)."""
+    _run_shared("window_480p", (1, 2, 2), 150, seed=13, per_tile=True)
 
 
 def test_skiparse_768p_sparse_sampled():
