@@ -563,7 +563,7 @@ def main():
             if name == args.workload:
                 continue
             st = build_workload(name, torch, np, vsa)
-            ms, _, tm = measure(st, torch, 3, 1)
+            ms, _, tm = measure(st, torch, 20, 3)
             f, pl = st["flops"]()
             pk = FP8_PEAK_TFLOPS if st["cfg"].fp8 else BF16_PEAK_TFLOPS
             a_ms = tm.total["attn"] / tm.count["attn"]
