@@ -273,3 +273,41 @@ def test_skiparse_768p_sampled():
     rel = (sum_dv - sum_do).norm() / sum_do.norm()
     print(f"sum dV vs sum dO rel={float(rel):.3e}")
     assert float(rel) < 1e-2
+
+
+def test_more_than_4096_tiles():
+    """A grid of 4,352 query tiles (past the 4,096-tile limit of the grouped
+    walks): the forward and the dQ kernel walk per tile, the transposed lists
+    cover every key tile; sampled rows against the oracle."""
+    T, H, W, heads, d = 34, 64, 64, 1, 64
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(2, 4, 4))
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(2, 4, 4))
+    assert olay.n_tiles == 4352
+    rng = np.random.default_rng(3101)
+    q, k, v, g = _small_inputs(olay, 1, "bf16", rng)
+    announce("bwd 4352 tiles")
+    # a shared table of random ascending lists (the lists are inputs here;
+    # the mask builders are tested on their own)
+    n = olay.n_tiles
+    lists = [sorted(rng.choice(n, int(rng.integers(1, 12)), replace=False).tolist()) for _ in range(n)]
+    lists[0] = [0, 5, 4350]
+    idx, cnt = table_from_lists(lists)
+    c = Case(olay, blay, q, k, v, g, "bf16", OA.shared_lists(lists), idx, cnt)
+    C = olay.tile_tokens
+    items = [(0, 0, t) for t in (0, 1, 2177, 4351)]
+    O, _ = OA.attention(c.qo, c.ko, c.vo, olay, OA.shared_lists(lists), c.sigma, items=items)
+    go = np.concatenate([_np(c.out[0, 0, t * C:(t + 1) * C]) for _, _, t in items])
+    ro = np.concatenate([O[0, 0, t * C:(t + 1) * C] for _, _, t in items])
+    mae, rl2 = errors(go, ro)
+    assert mae <= 2e-2 and rl2 <= 1e-2
+    dq_r, _, _ = OG.attention_backward(c.qo, c.ko, c.vo, c.go, olay, OA.shared_lists(lists), c.sigma,
+                                       items=items)
+    _check("dq sampled", np.concatenate([_np(c.grads[0][0, 0, t * C:(t + 1) * C]) for _, _, t in items]),
+           np.concatenate([dq_r[0, 0, t * C:(t + 1) * C] for _, _, t in items]), "bf16")
+    for kt in (5, 4350):
+        qts = [t for t in range(n) if kt in lists[t]]
+        assert qts
+        dk_r, dv_r = OG.key_tile_gradients(c.qo, c.ko, c.vo, c.go, olay, OA.shared_lists(lists), c.sigma,
+                                           0, 0, kt, query_tiles=qts)
+        _check("dk sampled", _np(c.grads[1][0, 0, kt * C:(kt + 1) * C]), dk_r, "bf16")
+        _check("dv sampled", _np(c.grads[2][0, 0, kt * C:(kt + 1) * C]), dv_r, "bf16")
