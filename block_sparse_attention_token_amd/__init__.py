@@ -25,7 +25,7 @@ from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, 
 
 __all__ = [
     "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
-    "quant_fp8_tiles", "block_sparse_attn_fwd", "build_mask_window_grouped",
+    "quant_fp8_tiles", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat", "build_mask_window_grouped",
     "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
     "block_sparse_attn_bwd", "VsaError", "EXPORTED",
     "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
@@ -300,3 +300,33 @@ def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
         float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return dq, dk, dv
+
+
+def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              kv_idx: Optional[torch.Tensor] = None,
+                              kv_cnt: Optional[torch.Tensor] = None,
+                              softmax_scale: Optional[float] = None, want_lse: bool = False,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              stream=None, per_tile_walk: bool = False):
+    """Forward with natural-order Q in and O out (vsa_block_sparse_attn_fwd_nat):
+    q_nat and the returned out are [B, T*H*W, heads, d]; k and v tiled.
+    Returns (out, lse or None); lse in the tiled order."""
+    info = layout_info(lay)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    dtype = _DT.get(q_nat.dtype, -1)
+    if out is None:
+        out = torch.empty_like(q_nat)
+    if want_lse and lse is None:
+        lse = torch.empty((lay.batch, lay.heads, info.n_padded), dtype=torch.float32,
+                          device=q_nat.device)
+    if kv_idx is not None:
+        max_kv = kv_idx.shape[-1]
+        list_mode = (2 if per_tile_walk else 0) if kv_idx.dim() == 2 else 1
+    else:
+        max_kv, list_mode = 0, 0
+    c = lay.c()
+    check(lib().vsa_block_sparse_attn_fwd_nat(
+        ctypes.byref(c), dtype, _ptr(q_nat), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt),
+        int(max_kv), list_mode, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse

@@ -30,7 +30,8 @@ VSA_SKIPARSE2D = 1
 EXPORTED = (
     "vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window", "vsa_build_mask_topk",
     "vsa_build_mask_topk_workspace", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
-    "vsa_block_sparse_attn_fwd", "vsa_build_mask_window_grouped", "vsa_quant_fp8_tiles_grouped",
+    "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat", "vsa_build_mask_window_grouped",
+    "vsa_quant_fp8_tiles_grouped",
     "vsa_build_transposed_lists", "vsa_block_sparse_attn_bwd_workspace",
     "vsa_block_sparse_attn_bwd", "vsa_status_string", "vsa_last_error", "vsa_version",
 )
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
     L.vsa_quant_fp8_tiles.argtypes = [LP, P, P, P, P]
     L.vsa_quant_fp8_tiles_v.argtypes = [LP, P, P, P, P]
     L.vsa_block_sparse_attn_fwd.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, F32, P, P, P]
+    L.vsa_block_sparse_attn_fwd_nat.argtypes = [LP, I32, P, P, P, P, P, I32, I32, F32, P, P, P]
     L.vsa_build_mask_window_grouped.argtypes = [LP, I32, I32, I32, I32, I32, I32, I32, P, P, P]
     L.vsa_quant_fp8_tiles_grouped.argtypes = [LP, I32, I32, I32, P, P, P, I32, P]
     L.vsa_build_transposed_lists.argtypes = [LP, P, P, I32, I32, P, P, P]
@@ -89,7 +91,8 @@ def lib() -> ctypes.CDLL:
                                             P, P, P, P, SZ, P]
     for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window",
                  "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
-                 "vsa_block_sparse_attn_fwd", "vsa_build_mask_window_grouped", "vsa_quant_fp8_tiles_grouped",
+                 "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat", "vsa_build_mask_window_grouped",
+    "vsa_quant_fp8_tiles_grouped",
     "vsa_build_transposed_lists",
                  "vsa_block_sparse_attn_bwd"):
         getattr(L, name).restype = I32

@@ -485,11 +485,12 @@ __device__ __forceinline__ float bf_step_lag(const uint4* kb, const uint4* vb,
 
 // Q^T fragments for query row 32*rg + l32 of tile qt; a negative softmax
 // scale is folded into Q (sign flip) so the softmax only needs a maximum.
-template <int TILE, int D, bool F32IN>
-__device__ __forceinline__ void bf_load_q(rsrc_t rq, int qt, int rg, int l32, int half,
+// row_off: byte offset of the row in rq (past its end for a row that does
+// not exist, which then reads as zeros).
+template <int D, bool F32IN>
+__device__ __forceinline__ void bf_load_q(rsrc_t rq, uint32_t row_off, int half,
                                           uint32_t qsign, uint4 (&qf)[D / 16]) {
   constexpr int ES = F32IN ? 4 : 2;
-  const uint32_t row_off = (uint32_t)((qt * TILE + 32 * rg + l32) * D * ES);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const uint4 x = bload8<F32IN>(rq, row_off + (ks * 16 + half * 8) * ES, 0);
@@ -497,8 +498,10 @@ __device__ __forceinline__ void bf_load_q(rsrc_t rq, int qt, int rg, int l32, in
   }
 }
 
-// Normalise and write this wave's 32 output rows (and lse)
-template <int TILE, int D, bool F32IN>
+// Normalise and write this wave's 32 output rows (and lse). NAT: the rows go
+// to their natural positions in out [B, T*H*W, heads, d] (pad rows have none
+// and are not written); lse stays in the tiled order.
+template <int TILE, int D, bool F32IN, bool NAT = false>
 __device__ __forceinline__ void bf_epilogue(const DevLayout& L, const AttnArgs& a, const WaveWork& ww,
                                             int rg, int l32, int half, const f32x16_t (&oacc)[D / 32],
                                             float m_run, float l_run) {
@@ -508,18 +511,27 @@ __device__ __forceinline__ void bf_epilogue(const DevLayout& L, const AttnArgs& 
   const bool real = row_is_real(L, tq, qrow);
   const float inv = (real && lt > 0.0f) ? 1.0f / lt : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
+  long long obase = orow;
+  bool store = true;
+  if constexpr (NAT) {
+    const int n = natural_index(L, ww.qt, qrow);
+    const int b = ww.bh / L.heads, h = ww.bh - b * L.heads;
+    store = n >= 0;
+    obase = ((long long)b * L.n_tokens + max(n, 0)) * L.heads + h;
+  }
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      if (!store) break;
       const int c0 = 32 * cb + 8 * g + 4 * half;
       const float o0 = oacc[cb][4 * g + 0] * inv, o1 = oacc[cb][4 * g + 1] * inv;
       const float o2 = oacc[cb][4 * g + 2] * inv, o3 = oacc[cb][4 * g + 3] * inv;
       if constexpr (F32IN) {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * D + c0) =
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase * D + c0) =
             make_float4(o0, o1, o2, o3);
       } else {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase * D + c0) =
             make_uint2(pack2(o0, o1), pack2(o2, o3));
       }
     }
@@ -538,7 +550,10 @@ constexpr float kLazyBf16 = 8.0f;
 // Two walks: the pipelined one when every wave owns every block (routed
 // lists, dense lists, query tiles sharing one list), and a plain
 // double-buffered one for unions whose blocks some waves skip.
-template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF>
+// NAT: Q is read from and O written to the natural order [B, T*H*W, heads, d]
+// (the tile permute of Q and the inverse permute of O fused into the
+// kernel's first load and last store); K and V stay tiled.
+template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF, bool NAT>
 __global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int WPQ = TILE / 32;         // waves per query tile
@@ -575,16 +590,30 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   else len = ww.cnt;
 
   const long long head_bytes = L.n_padded * D * IO::ES;
-  const char* qb = static_cast<const char*>(a.q) + ww.head_row0 * D * IO::ES;
-  const rsrc_t rq = make_rsrc(qb, head_bytes);
+  rsrc_t rq;
+  uint32_t q_row_off;
+  {
+    const int qrow = 32 * rg + l32, qt = min(ww.qt, L.n_tiles - 1);
+    if constexpr (NAT) {
+      // one (b, head) of natural Q: rows n at stride heads * d elements
+      const int b = ww.bh / L.heads, h = ww.bh - b * L.heads;
+      const long long first = ((long long)b * L.n_tokens * L.heads + h) * D * IO::ES;
+      rq = make_rsrc(static_cast<const char*>(a.q) + first,
+                     ((long long)L.n_tokens * L.heads - h) * D * IO::ES);
+      const int n = natural_index(L, qt, qrow);
+      q_row_off = n < 0 ? 0x7FFFFF00u : (uint32_t)((long long)n * L.heads * D * IO::ES);
+    } else {
+      rq = make_rsrc(static_cast<const char*>(a.q) + ww.head_row0 * D * IO::ES, head_bytes);
+      q_row_off = (uint32_t)((qt * TILE + qrow) * D * IO::ES);
+    }
+  }
   const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + ww.head_row0 * D * IO::ES, head_bytes);
   const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + ww.head_row0 * D * IO::ES, head_bytes);
 
   // kept > 0 (a zero scale gives uniform weights) so a masked -inf stays -inf
   const float sl2 = fmaxf(fabsf(a.scale_log2), FLT_MIN);
   uint4 qf[D / 16];
-  bf_load_q<TILE, D, F32IN>(rq, min(ww.qt, L.n_tiles - 1), rg, l32, half,
-                            a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
+  bf_load_q<D, F32IN>(rq, q_row_off, half, a.scale_log2 < 0.0f ? 0x80008000u : 0u, qf);
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16_t{};
@@ -759,7 +788,7 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
     }
   }
   if (!ww.active) return;
-  bf_epilogue<TILE, D, F32IN>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
+  bf_epilogue<TILE, D, F32IN, NAT>(L, a, ww, rg, l32, half, oacc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -1135,8 +1164,12 @@ template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF = 2>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF>), dim3(n_work),
-                     dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
+  if (a.natural_io)
+    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, true>), dim3(n_work),
+                       dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, false>), dim3(n_work),
+                       dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
@@ -1166,6 +1199,7 @@ hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStre
   // shared tables the caller marks as walked per tile (list_mode 2): one
   // query tile per workgroup.
   const bool grouped = (a.kv_idx == nullptr || a.list_mode == 0) && L.n_tiles <= 4096;
+  if (a.natural_io && dtype != 0 && dtype != 1) return hipErrorInvalidValue;
   if (dtype == 3) {   // e4m3 with V codes in the P.V operand layout
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
     return grouped ? launch_fp8<4, true>(L, a, s) : launch_fp8<1, true>(L, a, s);

@@ -406,6 +406,46 @@ vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, co
                     "vsa_block_sparse_attn_bwd");
 }
 
+vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,
+                                         const void* k, const void* v, const int32_t* kv_idx,
+                                         const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
+                                         float softmax_scale, void* out, float* lse, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (dtype != VSA_F32 && dtype != VSA_BF16)
+    return fail(VSA_ERR_UNSUPPORTED, "natural-order attention takes VSA_F32 or VSA_BF16");
+  const long long es = dtype == VSA_F32 ? 4 : 2;
+  if ((long long)L.n_tokens * L.heads * L.d * es > 0x7FFFFFFFll)
+    return fail(VSA_ERR_UNSUPPORTED, "one batch of natural Q must stay below 2 GiB");
+  if (!q || !k || !v || !out) return fail(VSA_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr))
+    return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
+  if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
+  if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
+  if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
+  if (L.C != 32 && L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
+  if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
+  const long long work = (long long)L.B * L.heads * L.n_tiles;
+  if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  vsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = kv_idx ? max_kv : L.n_tiles;
+  a.list_mode = list_mode;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  a.natural_io = 1;
+  return hip_status(vsa::launch_attn(L, dtype, a, static_cast<hipStream_t>(stream)),
+                    "vsa_block_sparse_attn_fwd_nat");
+}
+
 const char* vsa_status_string(int32_t status) {
   switch (status) {
     case VSA_OK: return "VSA_OK";

@@ -151,6 +151,7 @@ struct AttnArgs {
   float scale_log2;        // softmax scale * log2(e)
   void* out;
   float* lse;
+  int natural_io;          // q read from / out written to [B, T*H*W, heads, d]
 };
 hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStream_t s);
 

@@ -250,6 +250,21 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
                                      int32_t list_mode, float softmax_scale, void* out, float* lse,
                                      void* stream);
 
+/* vsa_block_sparse_attn_fwd_nat: vsa_block_sparse_attn_fwd with the tile
+ * permute of Q and the inverse permute of O fused into the kernel (one
+ * full-tensor pass each saved; FVAttn summary: video-aware block
+ * organisation of the tokens). q and out are in the natural order
+ * [B, T*H*W, heads, d]; k and v stay tiled [B, heads, n_padded, d] (from
+ * vsa_tile_permute); lse, if given, is in the tiled order as for the
+ * forward. Every real token of out is written; the result equals the
+ * forward's followed by vsa_tile_permute(inverse). dtype VSA_F32 or
+ * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise, and when one batch of q exceeds
+ * 2 GiB); lists, list_mode and scale as for vsa_block_sparse_attn_fwd. */
+vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,
+                                         const void* k, const void* v, const int32_t* kv_idx,
+                                         const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
+                                         float softmax_scale, void* out, float* lse, void* stream);
+
 /* ----- S6 backward: gradients of the block-sparse attention -------------------
  * The pages train through this attention: VSA ("Faster Video Diffusion with
  * Trainable Sparse Attention", Research Type and Experiment Setup rows) is a

@@ -482,3 +482,76 @@ def test_batch_and_softmax_scales(dtype, mode, scale):
         assert rl2 <= REL_L2_FP8
     else:
         assert mae <= MAX_ABS and rl2 <= REL_L2
+
+
+@pytest.mark.parametrize("kind,tile,d,dtype,mode", [
+    ("tile3d", (4, 4, 4), 128, "bf16", "shared"), ("tile3d", (4, 4, 4), 64, "f32", "routed"),
+    ("tile3d", (2, 4, 4), 128, "bf16", "dense"), ("tile3d", (4, 4, 4), 128, "bf16", "per_tile"),
+    ("skiparse2d", (4, 4, 4), 128, "bf16", "shared")])
+def test_natural_io_forward(kind, tile, d, dtype, mode):
+    """Q read and O written in the natural order inside the kernel: the output
+    is bit-identical to the tiled forward followed by the inverse permute, and
+    matches the oracle; batch 2, ragged grids (and Skiparse group tails)."""
+    T, H, W, heads, B = (5, 9, 13, 2, 2) if kind == "tile3d" else (3, 10, 12, 2, 2)
+    kw = dict(T=T, H=H, W=W, heads=heads, head_dim=d, tile=tile, kind=kind, stride=(2, 2))
+    olay, blay = OL.Layout(**kw, batch=B), vsa.Layout(**kw, batch=B)
+    rng = np.random.default_rng(3300 + d + len(mode) + (kind == "skiparse2d"))
+    xs = [rng.standard_normal((B, olay.n_tokens, heads, d)).astype(np.float32) for _ in range(3)]
+    if dtype == "bf16":
+        from synth import round_to_bf16
+        xs = [round_to_bf16(x) for x in xs]
+    announce(f"natural io {kind} tile={tile} d={d} {dtype} {mode}")
+    qn, kn, vn = (to_device(x, dtype) for x in xs)
+    qt, kt, vt = (vsa.tile_permute(blay, x) for x in (qn, kn, vn))
+    n = olay.n_tiles
+    if mode in ("shared", "per_tile"):
+        lists = OM.skiparse_lists(olay) if kind == "skiparse2d" else OM.window_lists(olay, 1, 1, 1)
+        idx, cnt = table_from_lists(lists)
+        fn = OA.shared_lists(lists)
+    elif mode == "routed":
+        width = max(1, n // 2)
+        idx = np.full((B, heads, n, width), -1, dtype=np.int32)
+        cnt = np.zeros((B, heads, n), dtype=np.int32)
+        for b in range(B):
+            for h in range(heads):
+                for t in range(n):
+                    c = int(rng.integers(0, width + 1))
+                    idx[b, h, t, :c] = np.sort(rng.choice(n, c, replace=False))
+                    cnt[b, h, t] = c
+        fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    else:
+        idx = cnt = None
+        fn = OA.shared_lists(OM.dense_lists(olay))
+    di, dc = lists_to_device(idx, cnt) if idx is not None else (None, None)
+    pt = mode == "per_tile"
+    out_t, lse_t = vsa.block_sparse_attn_fwd(blay, qt, kt, vt, di, dc, want_lse=True, per_tile_walk=pt)
+    ref_nat = vsa.tile_permute(blay, out_t, inverse=True)
+    out_n, lse_n = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, di, dc, want_lse=True, per_tile_walk=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n.view(torch.int16) if dtype == "bf16" else out_n.view(torch.int32),
+                       ref_nat.view(torch.int16) if dtype == "bf16" else ref_nat.view(torch.int32))
+    assert torch.equal(lse_n, lse_t)
+    O, _ = OA.attention(*(OL.permute(x, olay).astype(np.float64) for x in xs), olay, fn, 1.0 / math.sqrt(d))
+    mae, rl2 = errors(out_n.float().cpu().numpy(), OL.unpermute(O, olay))
+    assert mae <= 2e-2 and rl2 <= 1e-2, (mae, rl2)
+
+
+def test_natural_io_skiparse_768p_identical():
+    """The launch bench.py times for the 768p Skiparse sparse layer: natural
+    Q in, natural O out, bit-identical to the tiled forward + inverse permute."""
+    cfg = CONFIGS["skiparse_768p"]
+    olay, blay = layouts(cfg)
+    q, k, v = inputs(cfg.name)
+    announce("natural io skiparse 768p")
+    qn, kn, vn = (to_device(x, cfg.dtype) for x in (q, k, v))
+    qt, kt, vt = (vsa.tile_permute(blay, x) for x in (qn, kn, vn))
+    idx, cnt = vsa.build_mask_window(blay, (0, 0, 0))
+    out_t, _ = vsa.block_sparse_attn_fwd(blay, qt, kt, vt, idx, cnt)
+    ref = vsa.tile_permute(blay, out_t, inverse=True)
+    out_n, _ = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt)
+    dense_t, _ = vsa.block_sparse_attn_fwd(blay, qt, kt, vt)
+    dense_ref = vsa.tile_permute(blay, dense_t, inverse=True)
+    dense_n, _ = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(dense_n.view(torch.int16), dense_ref.view(torch.int16))
