@@ -173,3 +173,23 @@ def test_big_tile_argument_errors_before_launch():
         == B.VSA_ERR_INVALID
     assert _status(q, ctypes.byref(sk), 1, 1, 1, _fake(1), _fake(2), _fake(3), 0, None) \
         == B.VSA_ERR_UNSUPPORTED
+
+
+def test_natural_forward_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    f = "vsa_block_sparse_attn_fwd_nat"
+    q, k, v, o = (_fake(i) for i in range(4))
+    # fp8 codes cannot be read in the natural order; null q; bad list_mode; NaN scale
+    assert _status(f, L, B.VSA_FP8_E4M3, q, k, v, None, None, 0, 0, ctypes.c_float(0.1), o, None,
+                   None) == B.VSA_ERR_UNSUPPORTED
+    assert _status(f, L, B.VSA_BF16, None, k, v, None, None, 0, 0, ctypes.c_float(0.1), o, None,
+                   None) == B.VSA_ERR_INVALID
+    assert _status(f, L, B.VSA_BF16, q, k, v, _fake(8), _fake(9), 8, 3, ctypes.c_float(0.1), o, None,
+                   None) == B.VSA_ERR_INVALID
+    assert _status(f, L, B.VSA_BF16, q, k, v, None, None, 0, 0, ctypes.c_float(float("nan")), o, None,
+                   None) == B.VSA_ERR_INVALID
+    # one batch of natural Q past 2 GiB (f32, 40 heads, d = 128, 120k tokens)
+    big = vsa.Layout(T=30, H=64, W=64, heads=40, head_dim=128).c()
+    assert _status(f, ctypes.byref(big), B.VSA_F32, q, k, v, None, None, 0, 0, ctypes.c_float(0.1), o,
+                   None, None) == B.VSA_ERR_UNSUPPORTED
