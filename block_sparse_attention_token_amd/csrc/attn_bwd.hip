@@ -17,13 +17,14 @@
 //          S^T = K . Q^T,  dP^T = V . dO^T,  dQ^T += K^T . dS^T
 //        so every lane holds one query row: its lse and D stay in registers;
 //   dkv: one workgroup per key tile, walking the transposed list (the query
-//        tiles whose lists hold it); a wave owns 32 key rows and computes
+//        tiles whose lists hold it); a wave owns 16 key rows and computes
 //          S = Q . K^T,  dP = dO . V^T,  dV^T += dO^T . P,  dK^T += Q^T . dS
 //        so every lane holds one key column and its K, V operands stay in
 //        registers for the whole walk.
 // The walked tensors (K and V for dq, Q and dO for dkv) pass through LDS in
-// 32-token blocks: loaded into registers one block ahead, stored to padded
-// row-major LDS rows, double-buffered with one barrier per block. The
+// 32-token blocks of padded row-major rows, one barrier per block: K and V
+// through registers one block ahead, Q and dO (bf16) copied straight into a
+// four-slot ring two blocks ahead. The
 // operands that contract over tokens (K^T, dO^T, Q^T) are read from those
 // same rows with ds_read_b64_tr_b16, whose transposition hands each lane
 // four consecutive token rows of one channel. The probabilities and dS
@@ -42,6 +43,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -441,19 +443,6 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
 }
 
 // ---------------------------------------------------------------------------
-// Scheduling hint for a region of NM MFMAs: PRE LDS reads first, then after
-// each MFMA up to DS more LDS reads and NV VALU instructions.
-template <int NM, int PRE, int DS, int NV>
-__device__ __forceinline__ void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);          // DS reads
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);         // VALU
-  }
-}
-
 // Direct copies from HBM into LDS (buffer_load ... lds): each 64-lane copy
 // writes 1 KB of LDS, lane i at byte 16*i from the wave-uniform base.
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -467,32 +456,71 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// dK and dV: one workgroup (C/32 waves) per (b, head, key tile). One wave per
-// SIMD: the two accumulators and the K, V operands take most of 512 registers,
-// so the walk is software-pipelined inside the wave instead: step s is one
-// scheduling region holding the score MFMAs (S, dP) of block s, the VALU
-// work of block s (P, dS and their bf16 packing) and the dV / dK MFMAs of
-// block s-1, which do not depend on that VALU work. The
-// query blocks live in a ring of four LDS slots (block j in slot j % 4):
-// step s reads slots s (rows, row statistics) and s-1 (transposed reads).
-// bf16 inputs are copied straight into LDS two blocks ahead (step s starts
-// the copies of block s+2 and, before its barrier, waits for this wave's
-// copies of block s+1), so no staging registers are needed; fp32 inputs,
-// rounded on the way, go through registers one block ahead. Before the first
-// step the slot of "block -1" and its operands are zero, so the first step's
-// dV / dK products add nothing.
+// Copies of one 32-row block into padded LDS rows (RowBlock's layout) by the
+// WAVES waves of a workgroup: copy j of a wave covers LDS chunks
+// 64*(wave + WAVES*j) + lane, i.e. row p / RS, chunk p % RS (the pad chunk
+// takes a copy of the row's last chunk; it is never read).
+template <int D, int WAVES>
+struct BlockCopy {
+  static constexpr int CPR = D / 8, RS = CPR + 1, CHUNKS = 32 * RS;
+  static constexpr int NI = (CHUNKS + 63) / 64;           // copies per block
+  static constexpr int NIW0 = (NI + WAVES - 1) / WAVES;   // copies of wave 0 (the most)
+  static constexpr int NIW1 = NI / WAVES;                 // of the last wave
+  uint32_t voff[NIW0];
+  bool valid[NIW0];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NIW0; ++j) {
+      const int p = 64 * (wave + WAVES * j) + lane;
+      valid[j] = (wave + WAVES * j) < NI && p < CHUNKS;
+      voff[j] = (uint32_t)((p / RS) * D * 2 + min(p % RS, CPR - 1) * 16);
+    }
+  }
+  // the 32 rows starting at byte offset soff (wave-uniform) of r, into lds
+  __device__ __forceinline__ void issue(rsrc_t r, uint4* lds, uint32_t soff, int wave) const {
+#pragma unroll
+    for (int j = 0; j < NIW0; ++j)
+      if ((j < NIW1 || wave == 0) && valid[j])
+        dma16(r, reinterpret_cast<char*>(lds) + 1024 * (wave + WAVES * j), voff[j], soff);
+  }
+};
+
+// dK and dV: one workgroup per (b, head, key tile), 16 key rows per wave
+// (v_mfma_f32_16x16x32_bf16, C/16 waves per tile). A wave holds its K and V
+// operands and both accumulators in about 150 registers, so two waves share
+// each SIMD and cover each other's latencies (owning 32 keys with 32x32
+// products needs more than 256 registers, one wave per SIMD). Per 32-query
+// block a wave computes
+//   S = Q . K^T, dP = dO . V^T          (2 query tiles x 4 channel chunks each)
+//   dV^T += dO^T . P, dK^T += Q^T . dS  (8 channel tiles each, the 32 queries
+//                                        as one contraction chunk)
+// 16x16x32 operand layouts: A lane l holds row l%16, k = 8*(l/16) .. +7; B
+// lane l holds column l%16, the same k; C lane l holds rows 4*(l/16) + i,
+// column l%16. The 32 queries of P and dS (C rows 4g + i of the two query
+// tiles, g = l/16) are the contraction slots: slot s of lane group g is query
+// 4g + s (s < 4) or 16 + 4g + s - 4, and the transposed LDS reads of dO and
+// Q gather the same queries. Q and dO blocks are copied into a four-slot LDS
+// ring two blocks ahead (bf16) or staged through registers one block ahead
+// (fp32 inputs).
+template <int RSE>
+__device__ __forceinline__ int tr16_lane_offset(int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  return (4 * g + (i >> 2)) * RSE + 4 * (i & 3);
+}
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 template <int C, int D, bool F32IN>
-__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
-  constexpr int THREADS = 2 * C, WAVES = C / 32, SUB = C / 32, NBUF = 4;
+__global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
+  constexpr int WAVES = C / 16, THREADS = 64 * WAVES, SUB = C / 32, NBUF = 4;
   constexpr int ES = F32IN ? 4 : 2;
   constexpr bool DMA = !F32IN;
   using RB = RowBlock<D, THREADS, F32IN>;
-  // copies per 32-row block and tensor: RB::LDS chunks of 16 bytes, 64 a copy
-  constexpr int NI = (RB::LDS + 63) / 64;
-  constexpr int NIW0 = (NI + WAVES - 1) / WAVES;          // copies of wave 0 (the most)
-  constexpr int NIW1 = NI / WAVES;                        // of wave 1 (if any)
-  constexpr int VM0 = 2 * NIW0 + 1, VM1 = 2 * NIW1;       // per block, stats by wave 0
+  using BC = BlockCopy<D, WAVES>;
+  constexpr int RSE = RB::RSE;
   __shared__ uint4 q_s0[RB::LDS], q_s1[RB::LDS], q_s2[RB::LDS], q_s3[RB::LDS];
   __shared__ uint4 g_s0[RB::LDS], g_s1[RB::LDS], g_s2[RB::LDS], g_s3[RB::LDS];
   __shared__ float4 st_s0[16], st_s1[16], st_s2[16], st_s3[16];   // 32 rows of {lse2, D}
@@ -500,8 +528,9 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
   auto gbuf = [&](int i) -> uint4* { return i == 0 ? g_s0 : i == 1 ? g_s1 : i == 2 ? g_s2 : g_s3; };
   auto sbuf = [&](int i) -> float4* { return i == 0 ? st_s0 : i == 1 ? st_s1 : i == 2 ? st_s2 : st_s3; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
   const int item = a.q_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
                                                 : xcd_remap(blockIdx.x, n_work);
   const int bh = item / L.n_tiles, kt = item - bh * L.n_tiles;
@@ -522,57 +551,38 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
     cnt = min(max(a.q_cnt[r], 0), L.n_tiles);
   }
 
-  // B operands K^T and V^T: key row krow, channels 16*ks + 8*half .. +7
-  const int krow = 32 * wave + l32;
+  // B operands K^T and V^T: key krow, channels 32*kc + 8*g .. +7
+  const int krow = 16 * wave + l16;
   const uint32_t koff = (uint32_t)((kt * C + krow) * D * ES);
-  uint4 kf[D / 16], vf[D / 16];
+  uint4 kf[D / 32], vf[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = bload8<F32IN>(rk, koff + (16 * ks + 8 * half) * ES, 0);
-    vf[ks] = bload8<F32IN>(rv, koff + (16 * ks + 8 * half) * ES, 0);
+  for (int kc = 0; kc < D / 32; ++kc) {
+    kf[kc] = bload8<F32IN>(rk, koff + (32 * kc + 8 * g) * ES, 0);
+    vf[kc] = bload8<F32IN>(rv, koff + (32 * kc + 8 * g) * ES, 0);
   }
   const float sl2 = a.scale_log2;
-
-  f32x16_t dk[D / 32], dv[D / 32];
+  f32x4_t dk[D / 16], dv[D / 16];
 #pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16_t{};
+  for (int dt = 0; dt < D / 16; ++dt) dk[dt] = dv[dt] = f32x4_t{};
 
   const int nblk = cnt * SUB;
-  // first query row of block b (clamped to the last block); wave-uniform
   auto first_row = [&](int b) -> int {
     b = min(b, nblk - 1);
     const int e = b / SUB;
     const int t = list ? min(max(list[e], 0), L.n_tiles - 1) : e;
     return __builtin_amdgcn_readfirstlane(t * C + 32 * (b % SUB));
   };
-  // copy j of this wave covers LDS chunks 64*(wave + WAVES*j) + lane: row
-  // p / RS, chunk p % RS of the padded rows (the pad chunk takes a copy of
-  // the row's last chunk; it is never read)
-  uint32_t cvoff[NIW0];
-  bool cvalid[NIW0];
-#pragma unroll
-  for (int j = 0; j < NIW0; ++j) {
-    const int p = 64 * (wave + WAVES * j) + lane;
-    const int r = p / RB::RS, c = p % RB::RS;
-    cvalid[j] = (wave + WAVES * j) < NI && p < RB::LDS;
-    cvoff[j] = (uint32_t)(r * D * ES + min(c, RB::CPR - 1) * 16);
-  }
+  BC cp;
+  if constexpr (DMA) cp.init(wave, lane);
   RB qio, gio;
   float2 streg = make_float2(0.0f, 0.0f);
+  constexpr int VM0 = 2 * BC::NIW0 + 1, VM1 = 2 * BC::NIW1;
   auto copy_blk = [&](int b, uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
     const int r = first_row(b);
     if constexpr (DMA) {
       const uint32_t soff = (uint32_t)(r * D * ES);
-#pragma unroll
-      for (int j = 0; j < NIW0; ++j) {
-        const int k = wave + WAVES * j;
-        if (j < NIW1 || wave == 0) {
-          if (cvalid[j]) {
-            dma16(rq, reinterpret_cast<char*>(qd) + 1024 * k, cvoff[j], soff);
-            dma16(rg, reinterpret_cast<char*>(gd) + 1024 * k, cvoff[j], soff);
-          }
-        }
-      }
+      cp.issue(rq, qd, soff, wave);
+      cp.issue(rg, gd, soff, wave);
       if (wave == 0 && lane < 16) dma16(rs, sd, lane * 16, (uint32_t)(r * 8));
     } else {
       qio.load(rq, (uint32_t)(r * D * ES), tid);
@@ -587,7 +597,6 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
       if (tid < 32) reinterpret_cast<float2*>(sd)[tid] = streg;
     }
   };
-  // this wave's copies older than the last `batches` blocks' are complete
   auto wait_copies = [&](auto batches) __attribute__((always_inline)) {
     if constexpr (DMA) {
       constexpr int NB = decltype(batches)::value;
@@ -595,72 +604,56 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
       else wait_vmcnt<NB * VM1>();
     }
   };
-  const int tro = tr_lane_offset<RB::RSE>(lane);
-  // S = Q . K^T and dP = dO . V^T of the block in slot (qs, gs)
-  auto scores = [&](const uint4* qs, const uint4* gs, f32x16_t& s, f32x16_t& dp)
-      __attribute__((always_inline)) {
-    const uint4* qb = qs + l32 * RB::RS + half;
-    const uint4* gb = gs + l32 * RB::RS + half;
-    s = f32x16_t{};
-    dp = f32x16_t{};
+  const int tro = tr16_lane_offset<RSE>(lane);
+
+  auto step = [&](int s, const uint4* qs, const uint4* gs, const float4* st) __attribute__((always_inline)) {
+    // S and dP: two 16-query tiles
+    f32x4_t sc[2], dp[2];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      s = mfma(qb[2 * ks], kf[ks], s);
-      dp = mfma(gb[2 * ks], vf[ks], dp);
-    }
-  };
-  // P and dS as bf16 B operands (chunk c: rows 16*c + 8*(i/4) + 4*half + i%4
-  // of the block, i = 0..7)
-  auto grads = [&](const float4* st, const f32x16_t& s, const f32x16_t& dp, uint4 (&pk)[4])
-      __attribute__((always_inline)) {
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint4* qb = qs + (16 * mt + l16) * RB::RS + g;
+      const uint4* gb = gs + (16 * mt + l16) * RB::RS + g;
+      sc[mt] = f32x4_t{};
+      dp[mt] = f32x4_t{};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float p[8], x[8];
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * c + gg;
-        const float4 s01 = st[4 * g + 2 * half];       // rows 8g+4half+0, +1
-        const float4 s23 = st[4 * g + 2 * half + 1];   // rows 8g+4half+2, +3
-        const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
-        const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          p[4 * gg + i] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l2[i]));
-          x[4 * gg + i] = p[4 * gg + i] * (dp[r] - dd[i]);
-        }
+      for (int kc = 0; kc < D / 32; ++kc) {
+        sc[mt] = mfma16(qb[4 * kc], kf[kc], sc[mt]);
+        dp[mt] = mfma16(gb[4 * kc], vf[kc], dp[mt]);
       }
-      pk[c] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
-      pk[2 + c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
     }
-  };
-  // dV^T += dO^T . P and dK^T += Q^T . dS for the block in slot (qs, gs)
-  auto accumulate = [&](const uint4* qs, const uint4* gs, const uint4 (&pk)[4])
-      __attribute__((always_inline)) {
+    // P and dS for queries 16*mt + 4g + i, packed as the 32-query B operands
+    float p[8], x[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const float4 s01 = st[8 * mt + 2 * g];         // rows 16mt+4g+0, +1
+      const float4 s23 = st[8 * mt + 2 * g + 1];     // rows 16mt+4g+2, +3
+      const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
+      const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * mt + i] = __builtin_amdgcn_exp2f(fmaf(sc[mt][i], sl2, -l2[i]));
+        x[4 * mt + i] = p[4 * mt + i] * (dp[mt][i] - dd[i]);
+      }
+    }
+    const uint4 pp = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+    const uint4 dsp = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    // dV^T += dO^T . P and dK^T += Q^T . dS over 16-channel tiles
     const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro;
     const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro;
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        dv[mt] = mfma(frag_t<RB::RSE>(gt, 32 * mt, c), pk[c], dv[mt]);
-        dk[mt] = mfma(frag_t<RB::RSE>(qt_, 32 * mt, c), pk[2 + c], dk[mt]);
-      }
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint2 glo = lds_tr(gt + 16 * dt), ghi = lds_tr(gt + 16 * RSE + 16 * dt);
+      const uint2 qlo = lds_tr(qt_ + 16 * dt), qhi = lds_tr(qt_ + 16 * RSE + 16 * dt);
+      dv[dt] = mfma16(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pp, dv[dt]);
+      dk[dt] = mfma16(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsp, dk[dt]);
+    }
+    (void)s;
   };
 
-  using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
-  f32x16_t sc, dpc;
-  uint4 pk_a[4], pk_b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pk_b[i] = make_uint4(0u, 0u, 0u, 0u);
+  using C0 = std::integral_constant<int, 0>;
+  constexpr int AHEAD = DMA ? 2 : 1;
   if (nblk > 0) {
-    for (int i = tid; i < RB::LDS; i += THREADS) {
-      q_s3[i] = make_uint4(0u, 0u, 0u, 0u);
-      g_s3[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
     copy_blk(0, q_s0, g_s0, st_s0);
     store_regs(q_s0, g_s0, st_s0);
     if constexpr (DMA) {
@@ -669,50 +662,36 @@ void dkv_kernel(DevLayout L, BwdArgs a, int n_work) {
     }
     __syncthreads();
   }
-  // I = s % NBUF; even steps take (pk_b -> pk_a), odd ones the reverse
-  auto step = [&](auto phase, int s, const uint4 (&pprev)[4], uint4 (&pcur)[4])
-      __attribute__((always_inline)) {
-    constexpr int I = decltype(phase)::value;
-    constexpr int IN = (I + (DMA ? 2 : 1)) % NBUF;     // slot of the block copied in this step
-    constexpr int IP = (I + NBUF - 1) % NBUF;
-    copy_blk(s + (DMA ? 2 : 1), qbuf(IN), gbuf(IN), sbuf(IN));
-    scores(qbuf(I), gbuf(I), sc, dpc);
-    grads(sbuf(I), sc, dpc, pcur);
-    accumulate(qbuf(IP), gbuf(IP), pprev);
-    interleave_hint<2 * (D / 16) + 4 * (D / 32), 4, 2, 5>();
-    __builtin_amdgcn_sched_barrier(0);    // the staging stores wait for their loads here
-    store_regs(qbuf(IN), gbuf(IN), sbuf(IN));
-    wait_copies(C1{});                    // block s+1 is in LDS (this wave's share)
+  for (int s = 0; s < nblk; ++s) {
+    const int in = (s + AHEAD) % NBUF, cur = s % NBUF;
+    copy_blk(s + AHEAD, qbuf(in), gbuf(in), sbuf(in));
+    step(s, qbuf(cur), gbuf(cur), sbuf(cur));
+    store_regs(qbuf(in), gbuf(in), sbuf(in));
+    wait_copies(C1{});
     __syncthreads();
-  };
-  // the last block's operands end up in pk_b
-  for (int s = 0; s < nblk; s += NBUF) {
-    step(C0{}, s, pk_b, pk_a);
-    if (s + 1 >= nblk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk_b[i] = pk_a[i];
-      break;
-    }
-    step(C1{}, s + 1, pk_a, pk_b);
-    if (s + 2 >= nblk) break;
-    step(C2{}, s + 2, pk_b, pk_a);
-    if (s + 3 >= nblk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk_b[i] = pk_a[i];
-      break;
-    }
-    step(C3{}, s + 3, pk_a, pk_b);
-  }
-  if (nblk > 0) {
-    const int il = (nblk - 1) % NBUF;
-    accumulate(qbuf(il), gbuf(il), pk_b);
   }
   wait_copies(C0{});                      // no copy into LDS outlives the workgroup
 
   const bool real = row_is_real(L, tile_valid(L, kt), krow);
   const long long orow = row0 + kt * C + krow;
-  store_rows_t<D, F32IN>(a.dk, orow, half, dk, a.scale, real);
-  store_rows_t<D, F32IN>(a.dv, orow, half, dv, 1.0f, real);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int c0 = 16 * dt + 4 * g;
+    const float f = a.scale;
+    const float k0 = real ? dk[dt][0] * f : 0.0f, k1 = real ? dk[dt][1] * f : 0.0f;
+    const float k2 = real ? dk[dt][2] * f : 0.0f, k3 = real ? dk[dt][3] * f : 0.0f;
+    const float v0 = real ? dv[dt][0] : 0.0f, v1 = real ? dv[dt][1] : 0.0f;
+    const float v2 = real ? dv[dt][2] : 0.0f, v3 = real ? dv[dt][3] : 0.0f;
+    if constexpr (F32IN) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.dk) + orow * D + c0) = make_float4(k0, k1, k2, k3);
+      *reinterpret_cast<float4*>(static_cast<float*>(a.dv) + orow * D + c0) = make_float4(v0, v1, v2, v3);
+    } else {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dk) + orow * D + c0) =
+          make_uint2(pack2(k0, k1), pack2(k2, k3));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dv) + orow * D + c0) =
+          make_uint2(pack2(v0, v1), pack2(v2, v3));
+    }
+  }
 }
 
 template <int C, int D, bool F32IN>
@@ -728,7 +707,7 @@ hipError_t launch_bwd_shape(const DevLayout& L, const BwdArgs& a, hipStream_t s)
     const int n_grp = L.B * L.heads * ((L.n_tiles + 3) / 4);
     hipLaunchKernelGGL((dq_kernel<C, D, F32IN, 4>), dim3(n_grp), dim3(8 * C), 0, s, L, a, n_grp);
   }
-  hipLaunchKernelGGL((dkv_kernel<C, D, F32IN>), dim3(n_work), dim3(2 * C), 0, s, L, a, n_work);
+  hipLaunchKernelGGL((dkv16_kernel<C, D, F32IN>), dim3(n_work), dim3(4 * C), 0, s, L, a, n_work);
   return hipGetLastError();
 }
 
