@@ -606,7 +606,23 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   };
   const int tro = tr16_lane_offset<RSE>(lane);
 
-  auto step = [&](int s, const uint4* qs, const uint4* gs, const float4* st) __attribute__((always_inline)) {
+  // dV^T += dO^T . P and dK^T += Q^T . dS over 16-channel tiles
+  auto accumulate = [&](const uint4* qs, const uint4* gs, const uint4& pp, const uint4& dsp)
+      __attribute__((always_inline)) {
+    const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro;
+    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint2 glo = lds_tr(gt + 16 * dt), ghi = lds_tr(gt + 16 * RSE + 16 * dt);
+      const uint2 qlo = lds_tr(qt_ + 16 * dt), qhi = lds_tr(qt_ + 16 * RSE + 16 * dt);
+      dv[dt] = mfma16(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pp, dv[dt]);
+      dk[dt] = mfma16(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsp, dk[dt]);
+    }
+  };
+  // block s's scores and packed P, dS; block s-1's dV / dK products (its
+  // slot is not refilled before the next barrier)
+  auto step = [&](int s, const uint4* qs, const uint4* gs, const float4* st, const uint4* qp,
+                  const uint4* gp, uint4& pp_prev, uint4& ds_prev) __attribute__((always_inline)) {
     // S and dP: two 16-query tiles
     f32x4_t sc[2], dp[2];
 #pragma unroll
@@ -637,23 +653,22 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     }
     const uint4 pp = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
     const uint4 dsp = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-    // dV^T += dO^T . P and dK^T += Q^T . dS over 16-channel tiles
-    const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro;
-    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const uint2 glo = lds_tr(gt + 16 * dt), ghi = lds_tr(gt + 16 * RSE + 16 * dt);
-      const uint2 qlo = lds_tr(qt_ + 16 * dt), qhi = lds_tr(qt_ + 16 * RSE + 16 * dt);
-      dv[dt] = mfma16(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pp, dv[dt]);
-      dk[dt] = mfma16(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsp, dk[dt]);
-    }
+    accumulate(qp, gp, pp_prev, ds_prev);
+    pp_prev = pp;
+    ds_prev = dsp;
     (void)s;
   };
 
   using C1 = std::integral_constant<int, 1>;
   using C0 = std::integral_constant<int, 0>;
   constexpr int AHEAD = DMA ? 2 : 1;
+  // "block -1": zero slot 3 and zero operands, so step 0 adds nothing
+  uint4 pp_prev = make_uint4(0u, 0u, 0u, 0u), ds_prev = make_uint4(0u, 0u, 0u, 0u);
   if (nblk > 0) {
+    for (int i = tid; i < RB::LDS; i += THREADS) {
+      q_s3[i] = make_uint4(0u, 0u, 0u, 0u);
+      g_s3[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     copy_blk(0, q_s0, g_s0, st_s0);
     store_regs(q_s0, g_s0, st_s0);
     if constexpr (DMA) {
@@ -663,13 +678,14 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     __syncthreads();
   }
   for (int s = 0; s < nblk; ++s) {
-    const int in = (s + AHEAD) % NBUF, cur = s % NBUF;
+    const int in = (s + AHEAD) % NBUF, cur = s % NBUF, prv = (s + NBUF - 1) % NBUF;
     copy_blk(s + AHEAD, qbuf(in), gbuf(in), sbuf(in));
-    step(s, qbuf(cur), gbuf(cur), sbuf(cur));
+    step(s, qbuf(cur), gbuf(cur), sbuf(cur), qbuf(prv), gbuf(prv), pp_prev, ds_prev);
     store_regs(qbuf(in), gbuf(in), sbuf(in));
     wait_copies(C1{});
     __syncthreads();
   }
+  if (nblk > 0) accumulate(qbuf((nblk - 1) % NBUF), gbuf((nblk - 1) % NBUF), pp_prev, ds_prev);
   wait_copies(C0{});                      // no copy into LDS outlives the workgroup
 
   const bool real = row_is_real(L, tile_valid(L, kt), krow);
