@@ -126,14 +126,19 @@ def build_workload(name, torch, np, vsa):
                 timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(
                     lay, nat[0], tk, tv, kv_idx, kv_cnt, per_tile_walk=cfg.mask == "window"))
             return
-        tq, tk, tv = (timer.run("permute", lambda x=x: vsa.tile_permute(lay, x)) for x in nat)
+        # routed lists: Q and K are permuted with the routing's tile means pooled on
+        # the way, so the routing reads only the means
+        (tq, qp), (tk, kp) = (timer.run("permute_pool", lambda x=x: vsa.tile_permute_pool(lay, x))
+                              for x in nat[:2])
+        tv = timer.run("permute", lambda: vsa.tile_permute(lay, nat[2]))
         if cfg.mask == "topk":
-            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(lay, tq, tk, top_k=cfg.top_k))
+            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
+                lay, qp, kp, top_k=cfg.top_k))
             state["cnt"] = cnt
             out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv, idx, cnt))
         else:   # top-p routing on bf16, then fp8 attention
-            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk(
-                lay, tq, tk, top_p=cfg.top_p, k_floor=cfg.k_floor))
+            idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
+                lay, qp, kp, top_p=cfg.top_p, k_floor=cfg.k_floor))
             state["cnt"] = cnt
             # V quantised straight into the fp8 P.V operand layout
             (qc, qs), (kc, ks), (vc, vs) = (timer.run("quant", lambda x=x, vop=vop: vsa.quant_fp8_tiles(

@@ -24,7 +24,8 @@ from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, 
                    VSA_TILE3D, VsaError, VsaLayout, VsaLayoutInfo, check, lib)
 
 __all__ = [
-    "Layout", "layout_info", "tile_permute", "build_mask_window", "build_mask_topk",
+    "Layout", "layout_info", "tile_permute", "tile_permute_pool", "build_mask_window",
+    "build_mask_topk", "build_mask_topk_pooled",
     "quant_fp8_tiles", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat", "build_mask_window_grouped",
     "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
     "block_sparse_attn_bwd", "VsaError", "EXPORTED",
@@ -88,6 +89,25 @@ def tile_permute(lay: Layout, src: torch.Tensor, inverse: bool = False,
     check(lib().vsa_tile_permute(ctypes.byref(c), _DT.get(src.dtype, -1), _ptr(src), _ptr(out),
                                  1 if inverse else 0, _stream(stream)))
     return out
+
+
+def tile_permute_pool(lay: Layout, src: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      pooled: Optional[torch.Tensor] = None, stream=None):
+    """bf16 natural -> tiled permute that also returns the fp32 tile means
+    [B, heads, n_tiles, d] (vsa_tile_permute_pool): (tiled, pooled)."""
+    if src.dtype != torch.bfloat16:
+        raise ValueError("tile_permute_pool takes bf16 input")
+    info = layout_info(lay)
+    if out is None:
+        out = torch.empty((lay.batch, lay.heads, info.n_padded, lay.head_dim), dtype=src.dtype,
+                          device=src.device)
+    if pooled is None:
+        pooled = torch.empty((lay.batch, lay.heads, info.n_tiles, lay.head_dim),
+                             dtype=torch.float32, device=src.device)
+    c = lay.c()
+    check(lib().vsa_tile_permute_pool(ctypes.byref(c), _ptr(src), _ptr(out), _ptr(pooled),
+                                      _stream(stream)))
+    return out, pooled
 
 
 def build_mask_window(lay: Layout, radius: Tuple[int, int, int], max_kv: Optional[int] = None,
@@ -170,6 +190,39 @@ def build_mask_topk(lay: Layout, q_tiled: torch.Tensor, k_tiled: torch.Tensor,
                                     float(coarse_scale), int(top_k), float(top_p), int(k_floor),
                                     int(max_kv), _ptr(kv_idx), _ptr(kv_cnt), _ptr(scores),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+    return kv_idx, kv_cnt, scores
+
+
+def build_mask_topk_pooled(lay: Layout, q_pooled: torch.Tensor, k_pooled: torch.Tensor,
+                           coarse_scale: Optional[float] = None, top_k: int = 0,
+                           top_p: float = 0.0, k_floor: int = 0, max_kv: Optional[int] = None,
+                           want_scores: bool = False, workspace: Optional[torch.Tensor] = None,
+                           stream=None):
+    """Routed lists from pooled tile means (vsa_build_mask_topk_pooled):
+    (kv_idx, kv_cnt, scores or None), as build_mask_topk."""
+    info = layout_info(lay)
+    n = info.n_tiles
+    if coarse_scale is None:
+        coarse_scale = 1.0 / math.sqrt(lay.head_dim)
+    if max_kv is None:
+        max_kv = n if top_p > 0 else min(top_k, n)
+    dev = q_pooled.device
+    for t in (q_pooled, k_pooled):
+        if t.dtype != torch.float32 or tuple(t.shape) != (lay.batch, lay.heads, n, lay.head_dim):
+            raise ValueError("pooled means must be float32 [B, heads, n_tiles, d]")
+    kv_idx = torch.empty((lay.batch, lay.heads, n, max_kv), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty((lay.batch, lay.heads, n), dtype=torch.int32, device=dev)
+    scores = torch.empty((lay.batch, lay.heads, n, n), dtype=torch.float32, device=dev) \
+        if want_scores else None
+    need = topk_workspace_bytes(lay)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    c = lay.c()
+    check(lib().vsa_build_mask_topk_pooled(ctypes.byref(c), _ptr(q_pooled), _ptr(k_pooled),
+                                           float(coarse_scale), int(top_k), float(top_p),
+                                           int(k_floor), int(max_kv), _ptr(kv_idx), _ptr(kv_cnt),
+                                           _ptr(scores), _ptr(workspace), workspace.numel(),
+                                           _stream(stream)))
     return kv_idx, kv_cnt, scores
 
 

@@ -31,7 +31,7 @@ EXPORTED = (
     "vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window", "vsa_build_mask_topk",
     "vsa_build_mask_topk_workspace", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
     "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat", "vsa_build_mask_window_grouped",
-    "vsa_quant_fp8_tiles_grouped",
+    "vsa_quant_fp8_tiles_grouped", "vsa_tile_permute_pool", "vsa_build_mask_topk_pooled",
     "vsa_build_transposed_lists", "vsa_block_sparse_attn_bwd_workspace",
     "vsa_block_sparse_attn_bwd", "vsa_status_string", "vsa_last_error", "vsa_version",
 )
@@ -89,12 +89,14 @@ def lib() -> ctypes.CDLL:
     L.vsa_block_sparse_attn_bwd_workspace.restype = SZ
     L.vsa_block_sparse_attn_bwd.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, P, P, I32, F32,
                                             P, P, P, P, SZ, P]
+    L.vsa_tile_permute_pool.argtypes = [LP, P, P, P, P]
+    L.vsa_build_mask_topk_pooled.argtypes = [LP, P, P, F32, I32, F32, I32, I32, P, P, P, P, SZ, P]
     for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window",
                  "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
-                 "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat", "vsa_build_mask_window_grouped",
-    "vsa_quant_fp8_tiles_grouped",
-    "vsa_build_transposed_lists",
-                 "vsa_block_sparse_attn_bwd"):
+                 "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat",
+                 "vsa_build_mask_window_grouped", "vsa_quant_fp8_tiles_grouped",
+                 "vsa_tile_permute_pool", "vsa_build_mask_topk_pooled",
+                 "vsa_build_transposed_lists", "vsa_block_sparse_attn_bwd"):
         getattr(L, name).restype = I32
     L.vsa_status_string.argtypes = [I32]
     L.vsa_status_string.restype = ctypes.c_char_p

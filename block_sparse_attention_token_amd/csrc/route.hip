@@ -4,7 +4,9 @@
 // floor, per head, over video-aware blocks.
 //
 // Three kernels, all deterministic (fixed reduction orders, no float atomics):
-//   pool   : per (tensor, b, head, tile) mean over real rows, fp32;
+//   pool   : per (tensor, b, head, tile) mean over real rows, fp32; a second
+//            form reads the natural order and writes the tiled copy on the
+//            way (the tile permute with the pool folded in);
 //   score  : s_ij = coarse_scale * <qbar_i, kbar_j>, fp32, one 64x64 block of
 //            (i, j) per workgroup through LDS;
 //   select : per (b, head, i) row, bitonic sort of 64-bit keys
@@ -21,15 +23,23 @@ constexpr int kThreads = 256;
 constexpr int kMaxTiles = 4096;
 
 // ---------------------------------------------------------------- pool
-// grid (n_tiles, heads, B * 2); z selects Q (even) or K (odd).
+// MOVE = false: grid (n_tiles, heads, B * 2); z selects tiled Q (even) or K
+// (odd); pooled is [2][B][heads][n_tiles][d], counts gets the real rows per tile.
+// MOVE = true: the tile permute with the pool folded in. grid (n_tiles, heads,
+// B); q is the natural-order tensor [B, n_tokens, heads, d]; every row read is
+// also written to its tiled position in `tiled` (pad rows as zeros), pooled is
+// [B][heads][n_tiles][d]. Both forms give each thread the same rows and
+// chunks and sum them in the same order, so their means are bit-identical.
+template <bool MOVE>
 __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4* __restrict__ q,
                                                         const uint4* __restrict__ k,
+                                                        uint4* __restrict__ tiled,
                                                         float* __restrict__ pooled,
                                                         int* __restrict__ counts) {
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
-  const int b = blockIdx.z >> 1;
-  const int which = blockIdx.z & 1;
+  const int b = MOVE ? (int)blockIdx.z : (int)(blockIdx.z >> 1);
+  const int which = MOVE ? 0 : (int)(blockIdx.z & 1);
   const uint4* x = which ? k : q;
   const int chunks = L.d >> 3;                       // 8 bf16 per chunk
   const int groups = kThreads / chunks;              // row groups summed in parallel
@@ -43,8 +53,20 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   if (rg < groups) {
     for (int r = rg; r < L.C; r += groups) {
-      if (!row_is_real(L, tv, r)) continue;
-      const uint4 w = x[(row0 + r) * chunks + ch];
+      const long long t_off = (row0 + r) * chunks + ch;
+      uint4 w;
+      if (MOVE) {
+        const int nat = natural_index(L, tile, r);
+        if (nat < 0) {
+          tiled[t_off] = make_uint4(0u, 0u, 0u, 0u);
+          continue;
+        }
+        w = x[(((long long)b * L.n_tokens + nat) * L.heads + head) * chunks + ch];
+        tiled[t_off] = w;
+      } else {
+        if (!row_is_real(L, tv, r)) continue;
+        w = x[t_off];
+      }
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -65,13 +87,20 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
     for (int g = 0; g < groups; ++g) s += part[(g * chunks + cch) * 8 + ce];
     pooled[out0 * L.d + c] = n > 0 ? s / (float)n : 0.0f;
   }
-  if (threadIdx.x == 0 && which == 0 && b == 0 && head == 0) counts[tile] = n;
+  if (!MOVE && threadIdx.x == 0 && which == 0 && b == 0 && head == 0) counts[tile] = n;
+}
+
+// Real rows per tile, for routing from means pooled elsewhere.
+__global__ __launch_bounds__(kThreads) void counts_kernel(DevLayout L, int* __restrict__ counts) {
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t < L.n_tiles) counts[t] = real_rows(L, tile_valid(L, t));
 }
 
 // ---------------------------------------------------------------- score
 // grid (ceil(n/64) key blocks, ceil(n/64) query blocks, B * heads)
 constexpr int kSB = 64;
-__global__ __launch_bounds__(kThreads) void score_kernel(DevLayout L, const float* __restrict__ pooled,
+__global__ __launch_bounds__(kThreads) void score_kernel(DevLayout L, const float* __restrict__ q_pooled,
+                                                         const float* __restrict__ k_pooled,
                                                          const int* __restrict__ counts,
                                                          float coarse_scale,
                                                          float* __restrict__ scores) {
@@ -79,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(DevLayout L, const floa
   const int i0 = blockIdx.y * kSB;
   const int bh = blockIdx.z;
   const int n = L.n_tiles;
-  const float* qb = pooled + (long long)bh * n * L.d;
-  const float* kb = pooled + ((long long)L.B * L.heads + bh) * n * L.d;
+  const float* qb = q_pooled + (long long)bh * n * L.d;
+  const float* kb = k_pooled + (long long)bh * n * L.d;
   __shared__ float qs[kSB][33];
   __shared__ float ks[kSB][33];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 16 threads, 4 x 4 outputs each
@@ -280,31 +309,74 @@ size_t route_workspace_bytes(const DevLayout& L) {
   return ((pooled + 255) / 256) * 256 + counts + scores;
 }
 
-hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float coarse_scale,
-                        int top_k, float top_p, int k_floor, int max_kv, int32_t* kv_idx,
-                        int32_t* kv_cnt, float* scores, void* ws, hipStream_t s) {
-  const size_t n = (size_t)L.n_tiles;
-  char* base = static_cast<char*>(ws);
-  float* pooled = reinterpret_cast<float*>(base);
-  const size_t pooled_b = ((2ull * L.B * L.heads * n * L.d * sizeof(float) + 255) / 256) * 256;
-  int* counts = reinterpret_cast<int*>(base + pooled_b);
-  const size_t counts_b = ((n * sizeof(int) + 255) / 256) * 256;
-  float* sc = scores ? scores : reinterpret_cast<float*>(base + pooled_b + counts_b);
-
-  hipLaunchKernelGGL(pool_kernel, dim3(L.n_tiles, L.heads, L.B * 2), dim3(kThreads), 0, s, L,
-                     static_cast<const uint4*>(q), static_cast<const uint4*>(k), pooled, counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+// Score and select from pooled means; counts already hold the real rows per tile.
+static hipError_t route_from_pooled(const DevLayout& L, const float* q_pooled, const float* k_pooled,
+                                    const int* counts, float coarse_scale, int top_k, float top_p,
+                                    int k_floor, int max_kv, int32_t* kv_idx, int32_t* kv_cnt,
+                                    float* sc, hipStream_t s) {
   const int nb = (L.n_tiles + kSB - 1) / kSB;
-  hipLaunchKernelGGL(score_kernel, dim3(nb, nb, L.B * L.heads), dim3(kThreads), 0, s, L, pooled,
-                     counts, coarse_scale, sc);
-  e = hipGetLastError();
+  hipLaunchKernelGGL(score_kernel, dim3(nb, nb, L.B * L.heads), dim3(kThreads), 0, s, L, q_pooled,
+                     k_pooled, counts, coarse_scale, sc);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int npow2 = 256;
   while (npow2 < L.n_tiles) npow2 <<= 1;
-  const size_t lds = (size_t)npow2 * 8 + ((n + 15) / 16) * 16;
+  const size_t lds = (size_t)npow2 * 8 + ((L.n_tiles + 15) / 16) * 16;
   hipLaunchKernelGGL(select_kernel, dim3(L.n_tiles, L.heads, L.B), dim3(kThreads), lds, s, L, sc,
                      counts, npow2, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt);
+  return hipGetLastError();
+}
+
+struct RouteScratch {
+  float* pooled;
+  int* counts;
+  float* scores;
+};
+
+static RouteScratch carve(const DevLayout& L, void* ws, float* scores) {
+  const size_t n = (size_t)L.n_tiles;
+  char* base = static_cast<char*>(ws);
+  const size_t pooled_b = ((2ull * L.B * L.heads * n * L.d * sizeof(float) + 255) / 256) * 256;
+  const size_t counts_b = ((n * sizeof(int) + 255) / 256) * 256;
+  RouteScratch r;
+  r.pooled = reinterpret_cast<float*>(base);
+  r.counts = reinterpret_cast<int*>(base + pooled_b);
+  r.scores = scores ? scores : reinterpret_cast<float*>(base + pooled_b + counts_b);
+  return r;
+}
+
+hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float coarse_scale,
+                        int top_k, float top_p, int k_floor, int max_kv, int32_t* kv_idx,
+                        int32_t* kv_cnt, float* scores, void* ws, hipStream_t s) {
+  const RouteScratch r = carve(L, ws, scores);
+  hipLaunchKernelGGL(pool_kernel<false>, dim3(L.n_tiles, L.heads, L.B * 2), dim3(kThreads), 0, s,
+                     L, static_cast<const uint4*>(q), static_cast<const uint4*>(k), nullptr,
+                     r.pooled, r.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t per = (size_t)L.B * L.heads * L.n_tiles * L.d;
+  return route_from_pooled(L, r.pooled, r.pooled + per, r.counts, coarse_scale, top_k, top_p,
+                           k_floor, max_kv, kv_idx, kv_cnt, r.scores, s);
+}
+
+hipError_t launch_route_pooled(const DevLayout& L, const float* q_pooled, const float* k_pooled,
+                               float coarse_scale, int top_k, float top_p, int k_floor, int max_kv,
+                               int32_t* kv_idx, int32_t* kv_cnt, float* scores, void* ws,
+                               hipStream_t s) {
+  const RouteScratch r = carve(L, ws, scores);
+  hipLaunchKernelGGL(counts_kernel, dim3((L.n_tiles + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     s, L, r.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return route_from_pooled(L, q_pooled, k_pooled, r.counts, coarse_scale, top_k, top_p, k_floor,
+                           max_kv, kv_idx, kv_cnt, r.scores, s);
+}
+
+hipError_t launch_permute_pool(const DevLayout& L, const void* src, void* dst, float* pooled,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(pool_kernel<true>, dim3(L.n_tiles, L.heads, L.B), dim3(kThreads), 0, s, L,
+                     static_cast<const uint4*>(src), nullptr, static_cast<uint4*>(dst), pooled,
+                     nullptr);
   return hipGetLastError();
 }
 

@@ -146,6 +146,29 @@ vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void*
                                         static_cast<hipStream_t>(stream)), "vsa_tile_permute");
 }
 
+vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void* dst,
+                                 float* pooled, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!src || !dst || !pooled) return fail(VSA_ERR_INVALID, "src, dst and pooled must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst) || ((uintptr_t)pooled & 3u))
+    return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be <= 256 and a multiple of 8");
+  if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large for one launch");
+  const size_t bytes = (size_t)L.B * L.heads * L.d * 2;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  const char* p0 = reinterpret_cast<const char*>(pooled);
+  const size_t nat_b = bytes * L.n_tokens, til_b = bytes * L.n_padded;
+  const size_t pool_b = (size_t)L.B * L.heads * L.n_tiles * L.d * sizeof(float);
+  auto overlap = [](const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(s0, nat_b, d0, til_b) || overlap(s0, nat_b, p0, pool_b) || overlap(d0, til_b, p0, pool_b))
+    return fail(VSA_ERR_INVALID, "src, dst and pooled must not overlap");
+  return hip_status(vsa::launch_permute_pool(L, src, dst, pooled, static_cast<hipStream_t>(stream)),
+                    "vsa_tile_permute_pool");
+}
+
 vsa_status vsa_build_mask_window(const vsa_layout* layout, int32_t rt, int32_t rh, int32_t rw,
                                  int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
   vsa::DevLayout L;
@@ -199,16 +222,10 @@ size_t vsa_build_mask_topk_workspace(const vsa_layout* layout) {
   return vsa::route_workspace_bytes(L);
 }
 
-vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, const void* k_tiled,
-                               float coarse_scale, int32_t top_k, float top_p, int32_t k_floor,
-                               int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  vsa::DevLayout L;
-  vsa_status st = derive(layout, &L, nullptr);
-  if (st != VSA_OK) return st;
-  if (!q_tiled || !k_tiled || !kv_idx || !kv_cnt)
-    return fail(VSA_ERR_INVALID, "q_tiled, k_tiled, kv_idx and kv_cnt must be non-NULL");
-  if (!aligned16(q_tiled) || !aligned16(k_tiled)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+// Checks shared by both routing entry points (after the input pointers).
+static vsa_status check_route(const vsa::DevLayout& L, float coarse_scale, int32_t top_k,
+                              float top_p, int32_t k_floor, int32_t max_kv, const void* workspace,
+                              size_t workspace_bytes) {
   if (L.n_tiles > 4096) return fail(VSA_ERR_UNSUPPORTED, "routing supports at most 4096 tiles");
   if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "routing needs head_dim <= 256, multiple of 8");
   if (!isfinite(coarse_scale)) return fail(VSA_ERR_INVALID, "coarse_scale must be finite");
@@ -225,10 +242,45 @@ vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, co
   const size_t need_ws = vsa::route_workspace_bytes(L);
   if (!workspace || workspace_bytes < need_ws)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need_ws);
+  return VSA_OK;
+}
+
+vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, const void* k_tiled,
+                               float coarse_scale, int32_t top_k, float top_p, int32_t k_floor,
+                               int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!q_tiled || !k_tiled || !kv_idx || !kv_cnt)
+    return fail(VSA_ERR_INVALID, "q_tiled, k_tiled, kv_idx and kv_cnt must be non-NULL");
+  if (!aligned16(q_tiled) || !aligned16(k_tiled)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes);
+  if (st != VSA_OK) return st;
   return hip_status(vsa::launch_route(L, q_tiled, k_tiled, coarse_scale, top_k, top_p, k_floor,
                                       max_kv, kv_idx, kv_cnt, scores, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "vsa_build_mask_topk");
+}
+
+vsa_status vsa_build_mask_topk_pooled(const vsa_layout* layout, const float* q_pooled,
+                                      const float* k_pooled, float coarse_scale, int32_t top_k,
+                                      float top_p, int32_t k_floor, int32_t max_kv,
+                                      int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!q_pooled || !k_pooled || !kv_idx || !kv_cnt)
+    return fail(VSA_ERR_INVALID, "q_pooled, k_pooled, kv_idx and kv_cnt must be non-NULL");
+  if (((uintptr_t)q_pooled | (uintptr_t)k_pooled) & 3u)
+    return fail(VSA_ERR_INVALID, "pooled means must be 4-byte aligned");
+  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes);
+  if (st != VSA_OK) return st;
+  return hip_status(vsa::launch_route_pooled(L, q_pooled, k_pooled, coarse_scale, top_k, top_p,
+                                             k_floor, max_kv, kv_idx, kv_cnt, scores, workspace,
+                                             static_cast<hipStream_t>(stream)),
+                    "vsa_build_mask_topk_pooled");
 }
 
 static vsa_status quant_fp8(const vsa_layout* layout, const void* x_tiled, uint8_t* codes,

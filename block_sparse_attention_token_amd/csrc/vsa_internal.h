@@ -128,6 +128,12 @@ hipError_t launch_mask_window(const DevLayout& L, int rt, int rh, int rw, int ma
 hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float coarse_scale,
                         int top_k, float top_p, int k_floor, int max_kv, int32_t* kv_idx,
                         int32_t* kv_cnt, float* scores, void* ws, hipStream_t s);
+hipError_t launch_route_pooled(const DevLayout& L, const float* q_pooled, const float* k_pooled,
+                               float coarse_scale, int top_k, float top_p, int k_floor, int max_kv,
+                               int32_t* kv_idx, int32_t* kv_cnt, float* scores, void* ws,
+                               hipStream_t s);
+hipError_t launch_permute_pool(const DevLayout& L, const void* src, void* dst, float* pooled,
+                               hipStream_t s);
 size_t route_workspace_bytes(const DevLayout& L);
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
                             bool v_operand, hipStream_t s);

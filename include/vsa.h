@@ -181,6 +181,32 @@ vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, co
 /* Workspace bytes vsa_build_mask_topk needs for this layout (0 on a bad layout). */
 size_t vsa_build_mask_topk_workspace(const vsa_layout* layout);
 
+/* S1 with S3 folded in: FVAttn summary (video-aware block organisation: the
+ * pooling is a by-product of the regrouping pass); VSA page, Research Type row
+ * (the coarse stage works on pooled blocks).
+ *   src bf16 [B, T*H*W, heads, d] natural order -> dst bf16 [B, heads,
+ *   n_padded, d] tiled (bit-identical to vsa_tile_permute, pads zero) and
+ *   pooled float [B, heads, n_tiles, d]: each tile's mean over its real
+ *   tokens, the same fp32 values, bit for bit, as the pooling step inside
+ *   vsa_build_mask_topk (0 for a tile without real tokens).
+ * One pass over the tensor instead of the permute's pass plus the pool's.
+ * src, dst 16-byte aligned, pooled 4-byte aligned; buffers must not overlap.
+ * VSA_ERR_UNSUPPORTED unless head_dim <= 256 and a multiple of 8. */
+vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void* dst,
+                                 float* pooled, void* stream);
+
+/* S4 from pooled means: vsa_build_mask_topk's scoring and selection (same
+ * rules, limits and outputs) on q_pooled and k_pooled, float [B, heads,
+ * n_tiles, d] as written by vsa_tile_permute_pool. Given the means that
+ * vsa_build_mask_topk would pool from the same Q and K, the lists and scores
+ * are bit-identical to its. workspace: at least vsa_build_mask_topk_workspace()
+ * bytes. */
+vsa_status vsa_build_mask_topk_pooled(const vsa_layout* layout, const float* q_pooled,
+                                      const float* k_pooled, float coarse_scale, int32_t top_k,
+                                      float top_p, int32_t k_floor, int32_t max_kv,
+                                      int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----- S5: per-tile fp8 quantiser ---------------------------------------------
  * FPSAttention, Approach (FP8 on the same 3D tiles as the sparsity).
  *   x_tiled bf16 [B, heads, n_padded, d] -> codes uint8 [B, heads, n_padded, d]

@@ -193,3 +193,26 @@ def test_natural_forward_argument_errors_before_launch():
     big = vsa.Layout(T=30, H=64, W=64, heads=40, head_dim=128).c()
     assert _status(f, ctypes.byref(big), B.VSA_F32, q, k, v, None, None, 0, 0, ctypes.c_float(0.1), o,
                    None, None) == B.VSA_ERR_UNSUPPORTED
+
+
+def test_permute_pool_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    f = "vsa_tile_permute_pool"
+    src, dst, pooled = (ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(3))
+    assert _status(f, L, src, dst, None, None) == B.VSA_ERR_INVALID
+    assert _status(f, L, src, ctypes.c_void_p(0x20000008), pooled, None) == B.VSA_ERR_INVALID
+    assert _status(f, L, src, ctypes.c_void_p(0x10001000), pooled, None) == B.VSA_ERR_INVALID   # overlap
+    assert _status(f, L, src, dst, ctypes.c_void_p(0x20000100), None) == B.VSA_ERR_INVALID      # overlap
+    lay12 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=12).c()
+    assert _status(f, ctypes.byref(lay12), src, dst, pooled, None) == B.VSA_ERR_UNSUPPORTED
+    g = "vsa_build_mask_topk_pooled"
+    qp, kp = _fake(1), _fake(2)
+    assert _status(g, L, None, kp, ctypes.c_float(0.1), 32, ctypes.c_float(0.0), 0, 32, FAKE, FAKE,
+                   None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
+    assert _status(g, L, ctypes.c_void_p(0x100002), kp, ctypes.c_float(0.1), 32, ctypes.c_float(0.0),
+                   0, 32, FAKE, FAKE, None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
+    assert _status(g, L, qp, kp, ctypes.c_float(0.1), 32, ctypes.c_float(0.0), 0, 32, FAKE, FAKE,
+                   None, None, 0, None) == B.VSA_ERR_WORKSPACE
+    assert _status(g, L, qp, kp, ctypes.c_float(0.1), 0, ctypes.c_float(0.9), 16, 600, FAKE, FAKE,
+                   None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID

@@ -174,3 +174,81 @@ def test_topp_routing_workload():
     assert not bad, f"{len(bad)} rows differ beyond near-ties, e.g. {bad[:5]}"
     assert n_same >= 0.99 * gc.size
     assert int(gc.min()) >= cfg.k_floor
+
+
+# ---- tile permute with the pool folded in (FVAttn summary: video-aware block
+# organisation; VSA page, Research Type row: the coarse stage on pooled blocks)
+
+def _pool_bound(x_tiled, olay):
+    """Worst-case fp32 error of a tile mean of n <= 64 values summed in any
+    order: (n - 1) u sum|x| / n < 64 u mean|x|, plus the final division's u |mean|."""
+    return 64 * 2.0 ** -24 * OR.pool_tiles(np.abs(x_tiled), olay)
+
+
+def _check_permute_pool(olay, blay, x, route):
+    """x natural-order float32 (bf16 values). Tiled copy bit-identical to the
+    plain permute, means against the oracle, routing from the means
+    bit-identical to routing from the tiled tensors."""
+    xd = [to_device(a, "bf16") for a in x]
+    outs = [vsa.tile_permute_pool(blay, a) for a in xd]
+    plain = [vsa.tile_permute(blay, a) for a in xd]
+    torch.cuda.synchronize()
+    for (t, p), ref_t, a in zip(outs, plain, x):
+        assert torch.equal(t.view(torch.int16), ref_t.view(torch.int16))
+        xt = OL.permute(a, olay)
+        ref = OR.pool_tiles(xt, olay)
+        got = p.cpu().numpy()
+        fin = np.isfinite(ref)
+        assert np.all(got[~fin] == 0.0)
+        bound = _pool_bound(xt, olay) + 2.0 ** -24 * np.abs(np.nan_to_num(ref))
+        assert np.all(np.abs(got[fin] - ref[fin]) <= bound[fin] + 1e-30)
+    (qt, qp), (kt, kp) = outs
+    a = vsa.build_mask_topk(blay, qt, kt, want_scores=True, **route)
+    b = vsa.build_mask_topk_pooled(blay, qp, kp, want_scores=True, **route)
+    torch.cuda.synchronize()
+    # slots past a row's count are not written: compare the counts and the lists
+    assert torch.equal(a[1], b[1])
+    valid = torch.arange(a[0].shape[-1], device=a[0].device) < a[1].unsqueeze(-1)
+    assert torch.equal(a[0][valid], b[0][valid])
+    assert torch.equal(a[2].view(torch.int32), b[2].view(torch.int32))
+    return b
+
+
+@pytest.mark.parametrize("shape,tile,kind,stride,batch,d", [
+    ((5, 9, 13), (2, 4, 4), "tile3d", (2, 2), 2, 64),
+    ((3, 4, 6), (1, 4, 4), "skiparse2d", (2, 2), 1, 128),
+    ((2, 6, 9), (1, 4, 8), "skiparse2d", (3, 3), 2, 96),
+])
+def test_permute_pool_ragged(shape, tile, kind, stride, batch, d):
+    T, H, W = shape
+    heads = 3
+    olay = OLayout(T=T, H=H, W=W, heads=heads, head_dim=d, kind=kind, tile=tile, stride=stride)
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, kind=kind, tile=tile, stride=stride,
+                      batch=batch)
+    rng = np.random.default_rng(3301 + d)
+    x = [round_to_bf16((rng.standard_normal((batch, T * H * W, heads, d)) * 2.0 + 0.5)
+                       .astype(np.float32)) for _ in range(2)]
+    announce(f"permute+pool {shape} tile={tile} {kind} B={batch} d={d}")
+    top_k = min(3, olay.n_tiles)
+    kv_idx, kv_cnt, scores = _check_permute_pool(olay, blay, x, dict(top_k=top_k))
+    s = OR.coarse_scores(OR.pool_tiles(OL.permute(x[0], olay), olay),
+                         OR.pool_tiles(OL.permute(x[1], olay), olay), 1.0 / math.sqrt(d))
+    ridx, rcnt = OR.select_lists_vectorized(s, top_k=top_k)
+    gi, gc = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    assert np.array_equal(gc, rcnt)
+    for b in range(batch):
+        for h in range(heads):
+            for i in range(olay.n_tiles):
+                g = gi[b, h, i, :gc[b, h, i]].tolist()
+                r = ridx[b, h, i, :rcnt[b, h, i]].tolist()
+                assert _accept_topk(g, r, s[b, h, i], top_k), (b, h, i)
+
+
+@pytest.mark.parametrize("name", ["topk32_16x32x32", "fp8_topp_720p"])
+def test_permute_pool_workloads(name):
+    cfg = CONFIGS[name]
+    olay, blay = layouts(cfg)
+    q, k, _ = inputs(cfg.name)
+    announce(f"permute+pool {cfg.name}")
+    route = dict(top_k=cfg.top_k) if cfg.top_p <= 0 else dict(top_p=cfg.top_p, k_floor=cfg.k_floor)
+    _check_permute_pool(olay, blay, (q, k), route)
