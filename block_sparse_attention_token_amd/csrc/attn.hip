@@ -38,6 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // two floats -> two bf16 (round to nearest even) in one dword, lo first
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -905,6 +906,47 @@ struct F8Tile {
   }
 };
 
+// Direct copies (buffer_load ... lds, 16 bytes a lane) of one fp8 tile into
+// the padded LDS rows, for one-tile workgroups (two waves) with V in the
+// P.V operand layout, where K and V^T are both plain row copies. Copy j of
+// wave w fills the 1 KB of LDS chunks 64 * (w + 2 j) .. +63; chunk p is row
+// p / RS, chunk p % RS of the tile (the pad chunk takes a copy of the row's
+// last chunk and is never read). K: 64 rows of 8 chunks (9 copies), V^T: 128
+// rows of 4 chunks (10 copies). Source offsets are per lane, kept in
+// registers for the whole walk.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+// s_waitcnt with vmcnt 0 (expcnt and lgkmcnt at their maxima)
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+struct F8Dma {
+  static constexpr int KN = 64 * kK8Stride / 64, VN = 128 * kV8Stride / 64;   // 9, 10 copies
+  static_assert(KN == 9 && VN == 10, "copy counts of the padded rows");
+  uint32_t kvo[5], vvo[5];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int p = 64 * (wave + 2 * j) + lane;
+      kvo[j] = (uint32_t)((p / kK8Stride) * 128 + min(p % kK8Stride, kK8Stride - 2) * 16);
+      vvo[j] = (uint32_t)((p / kV8Stride) * 64 + min(p % kV8Stride, kV8Stride - 2) * 16);
+    }
+  }
+  // the tile at byte offset soff (wave-uniform) of rk / rv
+  __device__ __forceinline__ void issue_k(rsrc_t rk, uint4* lds, uint32_t soff, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+      if (wave + 2 * j < KN) dma16(rk, reinterpret_cast<char*>(lds) + 1024 * (wave + 2 * j), kvo[j], soff);
+  }
+  __device__ __forceinline__ void issue_v(rsrc_t rv, uint4* lds, uint32_t soff, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+      dma16(rv, reinterpret_cast<char*>(lds) + 1024 * (wave + 2 * j), vvo[j], soff);
+  }
+};
+
 // S^T (64 kv tokens x 32 query rows, raw code products) from one K buffer
 // (kb = buffer + lane base)
 __device__ __forceinline__ void f8_scores(const uint4* kb, const i32x8_t (&qf)[2], f32x16_t (&sacc)[2]) {
@@ -919,7 +961,10 @@ __device__ __forceinline__ void f8_scores(const uint4* kb, const i32x8_t (&qf)[2
 }
 
 // P8^T = e4m3(exp2(S * cs + e0)) for the tile's 32 scores of this lane (e0 =
-// log2 ps - m_run); returns the sum of the unrounded p * ps
+// log2 ps - m_run). VSUM: also returns the sum of the unrounded p * ps (the
+// one-tile walk; the four-tile walk sums the rounded values on the matrix
+// core, f8_rowsum).
+template <bool VSUM>
 __device__ __forceinline__ float f8_exp_pack(const f32x16_t (&s)[2], float cs, float e0, i32x8_t& pk) {
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
@@ -929,12 +974,32 @@ __device__ __forceinline__ float f8_exp_pack(const f32x16_t (&s)[2], float cs, f
     const float p1 = fast_exp2(fmaf(s[mb][r0 + 1], cs, e0));
     const float p2 = fast_exp2(fmaf(s[mb][r0 + 2], cs, e0));
     const float p3 = fast_exp2(fmaf(s[mb][r0 + 3], cs, e0));
-    acc0 += p0 + p1;
-    acc1 += p2 + p3;
+    if constexpr (VSUM) {
+      acc0 += p0 + p1;
+      acc1 += p2 + p3;
+    }
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
     pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
   }
   return acc0 + acc1;
+}
+
+// Row sums of the packed P8 on the matrix core. Read as the B operand of a
+// 16x16x128 product, lane l of pk is column l % 16 and k-group l / 16, and
+// holds query (l % 16) + 16 * ((l / 16) % 2), key half l / 32. The A operand
+// (sel) is 1.0 (e4m3 0x38) where the k-group's parity equals bit 2 of the
+// row, so output row m, column n sums both key halves of query
+// n + 16 * ((m / 4) % 2); lane l receives rows 4 * (l / 16) .. +3 of column
+// l % 16, which are the full 64-key sum of its own query l % 32 (in both
+// half-waves). In the one-tile walk the extra product and its operands cost
+// more registers than the wave has, so that walk keeps the VALU sum.
+__device__ __forceinline__ i32x8_t f8_rowsum_selector(int lane) {
+  const int v = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
+  return i32x8_t{v, v, v, v, v, v, v, v};
+}
+__device__ __forceinline__ float f8_rowsum(const i32x8_t& sel, const i32x8_t& pk) {
+  const f32x4_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pk, f32x4_t{}, 0, 0, 0, 127, 0, 127);
+  return r[0];
 }
 
 // O^T += Vc^T . P8^T (vb = V^T buffer + lane base)
@@ -953,8 +1018,14 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int THREADS = 64 * QPW * WPQ;
   using IO = F8Tile<THREADS, VOP>;
 
-  __shared__ uint4 k_lds[2][IO::K_LDS];               // 64 rows x (128 + 16) B
-  __shared__ uint4 v_lds[2][IO::V_LDS];               // V^T: 128 rows x (64 + 16) B
+  // one-tile walks with V in the operand layout copy K and V straight into LDS
+  constexpr bool DMA = VOP && QPW == 1;
+  // separate arrays per buffer, so that reads of one buffer need not wait for
+  // copies still in flight into the other
+  __shared__ uint4 k_lds0[IO::K_LDS], k_lds1[IO::K_LDS];   // 64 rows x (128 + 16) B
+  __shared__ uint4 v_lds0[IO::V_LDS], v_lds1[IO::V_LDS];   // V^T: 128 rows x (64 + 16) B
+  auto k_buf = [&](int p) -> uint4* { return p ? k_lds1 : k_lds0; };
+  auto v_buf = [&](int p) -> uint4* { return p ? v_lds1 : v_lds0; };
   extern __shared__ int sched[];
   static_assert(THREADS * 4 <= IO::K_LDS * 16, "scan scratch fits one K buffer");
   static_assert(4096 <= IO::V_LDS * 16, "marks of 4096 tiles fit one V buffer");
@@ -970,8 +1041,8 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   int len;
   bool shared = true;
   if constexpr (QPW > 1)
-    len = build_schedule<QPW, WPQ>(L, ww, reinterpret_cast<uint32_t*>(v_lds[1]),
-                                   reinterpret_cast<int*>(k_lds[1]), sched, tid, lane, shared);
+    len = build_schedule<QPW, WPQ>(L, ww, reinterpret_cast<uint32_t*>(v_buf(1)),
+                                   reinterpret_cast<int*>(k_buf(1)), sched, tid, lane, shared);
   else len = ww.cnt;
 
   const long long head_bytes = L.n_padded * D;
@@ -1037,6 +1108,9 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
   const int k_lane = l32 * kK8Stride + 2 * half;
   const int v_lane = l32 * kV8Stride + 2 * half;
+  // row sums on the matrix core for the four-tile walk (full sums in both half-waves)
+  constexpr bool MSUM = QPW > 1;
+  const i32x8_t rsel = f8_rowsum_selector(lane);
   // pad mask, running-max update (rare rescale of O) and exp2/pack of block
   // s; returns the packed P8^T operand
   auto softmax = [&](int s, f32x16_t (&sc)[MB], float hi) __attribute__((always_inline)) {
@@ -1053,8 +1127,8 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
       for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
     }
     i32x8_t pk;
-    const float psum = f8_exp_pack(sc, cs, rd(lps_v, s) - m_run, pk);
-    l_run = fmaf(psum, rd(ips_v, s), l_run);
+    const float psum = f8_exp_pack<!MSUM>(sc, cs, rd(lps_v, s) - m_run, pk);
+    l_run = fmaf(MSUM ? f8_rowsum(rsel, pk) : psum, rd(ips_v, s), l_run);
     return pk;
   };
   // pad mask of block s applied to its scores; returns their row maximum
@@ -1073,15 +1147,25 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     // V(s+1) are staged into K buffer P and V buffer P^1).
     f32x16_t s_a[MB], s_b[MB];
     float hi = 0.0f;
+    F8Dma dma;
+    const int w2 = wave & 1;                 // a one-tile workgroup has two waves
+    if constexpr (DMA) dma.init(w2, lane);
     if (steps > 0) {
-      io.load_k(rk, tile_off(0), tid);
-      io.load_v(rv, tile_off(0), tid);
-      io.store_k(k_lds[0], tid);
-      io.store_v(v_lds[0], tid);
-      io.load_k(rk, tile_off(1), tid);
-      io.store_k(k_lds[1], tid);
+      if constexpr (DMA) {
+        dma.issue_k(rk, k_buf(0), tile_off(0), w2);
+        dma.issue_v(rv, v_buf(0), tile_off(0), w2);
+        dma.issue_k(rk, k_buf(1), tile_off(1), w2);
+        wait_vmcnt0();
+      } else {
+        io.load_k(rk, tile_off(0), tid);
+        io.load_v(rv, tile_off(0), tid);
+        io.store_k(k_buf(0), tid);
+        io.store_v(v_buf(0), tid);
+        io.load_k(rk, tile_off(1), tid);
+        io.store_k(k_buf(1), tid);
+      }
       __syncthreads();
-      f8_scores(k_lds[0] + k_lane, qf, s_a);
+      f8_scores(k_buf(0) + k_lane, qf, s_a);
       hi = bf_row_max<MB>(s_a);
       __syncthreads();                   // K buffer 0 is refilled during step 0
     }
@@ -1089,17 +1173,26 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
                     f32x16_t (&snext)[MB]) __attribute__((always_inline)) {
       constexpr int P = decltype(parity)::value;
       cover(s);
-      io.load_k(rk, tile_off(s + 2), tid);
-      io.load_v(rv, tile_off(s + 1), tid);
+      if constexpr (DMA) {
+        dma.issue_k(rk, k_buf(P), tile_off(s + 2), w2);
+        dma.issue_v(rv, v_buf(P ^ 1), tile_off(s + 1), w2);
+      } else {
+        io.load_k(rk, tile_off(s + 2), tid);
+        io.load_v(rv, tile_off(s + 1), tid);
+      }
       hi = mask_max(s, scur, hi);
-      f8_scores(k_lds[P ^ 1] + k_lane, qf, snext);
+      f8_scores(k_buf(P ^ 1) + k_lane, qf, snext);
       const i32x8_t pk = softmax(s, scur, hi);
-      f8_pv(v_lds[P] + v_lane, pk, oacc);
+      f8_pv(v_buf(P) + v_lane, pk, oacc);
       hi = bf_row_max<MB>(snext);
       interleave_hint<8, 2, 8>();
-      __builtin_amdgcn_sched_barrier(0);  // the staging stores wait for their loads here
-      io.store_k(k_lds[P], tid);
-      io.store_v(v_lds[P ^ 1], tid);
+      __builtin_amdgcn_sched_barrier(0);  // the staging stores (copies) wait for their loads here
+      if constexpr (DMA) {
+        wait_vmcnt0();                    // this wave's copies have landed
+      } else {
+        io.store_k(k_buf(P), tid);
+        io.store_v(v_buf(P ^ 1), tid);
+      }
       __syncthreads();
     };
     for (int s = 0; s < steps; s += 2) {
@@ -1111,8 +1204,8 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     if (steps > 0) {
       io.load_k(rk, tile_off(0), tid);
       io.load_v(rv, tile_off(0), tid);
-      io.store_k(k_lds[0], tid);
-      io.store_v(v_lds[0], tid);
+      io.store_k(k_buf(0), tid);
+      io.store_v(v_buf(0), tid);
       __syncthreads();
     }
     for (int s = 0; s < steps; ++s) {
@@ -1125,14 +1218,14 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
       }
       if ((win.flags(s) >> (8 + ww.slot)) & 1) {
         f32x16_t sc[MB];
-        f8_scores(k_lds[P] + k_lane, qf, sc);
+        f8_scores(k_buf(P) + k_lane, qf, sc);
         const float hi = mask_max(s, sc, bf_row_max<MB>(sc));
         const i32x8_t pk = softmax(s, sc, hi);
-        f8_pv(v_lds[P] + v_lane, pk, oacc);
+        f8_pv(v_buf(P) + v_lane, pk, oacc);
       }
       if (has_next) {
-        io.store_k(k_lds[P ^ 1], tid);
-        io.store_v(v_lds[P ^ 1], tid);
+        io.store_k(k_buf(P ^ 1), tid);
+        io.store_v(v_buf(P ^ 1), tid);
       }
       __syncthreads();
     }
@@ -1141,7 +1234,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   if (!ww.active) return;
   const TileValid tq = tile_valid(L, ww.qt);
   const int qrow = 32 * rg + l32;
-  const float lt = halves_sum(l_run);
+  const float lt = MSUM ? l_run : halves_sum(l_run);
   const bool real = row_is_real(L, tq, qrow);
   const float inv = (real && lt > 0.0f) ? wmax / (kP8Scale * lt) : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
