@@ -311,3 +311,26 @@ def test_more_than_4096_tiles():
                                            0, 0, kt, query_tiles=qts)
         _check("dk sampled", _np(c.grads[1][0, 0, kt * C:(kt + 1) * C]), dk_r, "bf16")
         _check("dv sampled", _np(c.grads[2][0, 0, kt * C:(kt + 1) * C]), dv_r, "bf16")
+
+
+def test_workgroup_shapes_bit_identical():
+    """LDS race check: one Skiparse table passed once (the dQ kernel runs four
+    query tiles per workgroup, eight waves sharing staged K/V blocks) and
+    repeated per head (one query tile per workgroup, two waves). Tiles of a
+    residue group share their list, so every wave does the same products in
+    the same order either way: dQ, dK and dV must be bit-identical."""
+    T, H, W, heads, d = 5, 12, 20, 3, 128
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, kind="skiparse2d", stride=(2, 2))
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, kind="skiparse2d", stride=(2, 2))
+    rng = np.random.default_rng(2701)
+    q, k, v, g = _small_inputs(olay, 1, "bf16", rng)
+    idx, cnt = table_from_lists(OM.skiparse_lists(olay))
+    announce("bwd workgroup shapes bit-identical")
+    c = Case(olay, blay, q, k, v, g, "bf16", None, idx, cnt)
+    di4 = c.di[None, None].expand(1, heads, *c.di.shape).contiguous()
+    dc4 = c.dc[None, None].expand(1, heads, *c.dc.shape).contiguous()
+    per_head = vsa.block_sparse_attn_bwd(blay, c.qd, c.kd, c.vd, c.out, c.gd, c.lse, di4, dc4,
+                                         softmax_scale=c.sigma)
+    torch.cuda.synchronize()
+    for nm, a, b in zip(("dq", "dk", "dv"), c.grads, per_head):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
