@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -414,24 +415,36 @@ def cpu_baseline(name, np, seconds=12.0, bwd_seconds=0.0):
     return fwd, bwd
 
 
+def code_hash(path):
+    """sha256 of a source file's code: comments, trailing blanks and empty
+    lines removed, so that a comment edit does not invalidate counters taken
+    on the same code."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
 def traffic_from_profiles(kernel_src_hash):
     """HBM bytes per attention launch from the committed counter summary.
 
-    The summary records the sha256 of the attention source it was measured
-    on; if the kernel has changed since, the figure is stale and None is
-    returned.
+    The summary records the code hash (code_hash) of the attention source it
+    was measured on; if the kernel's code has changed since, the figure is
+    stale and None is returned.
     """
     path = os.path.join(ROOT, "profiles", "attn_skiparse_768p_pmc.md")
     rec = {}
     try:
         with open(path) as f:
             for line in f:
-                if ":" in line and line.split(":", 1)[0] in ("attn_source_sha256", "bytes_per_launch"):
+                if ":" in line and line.split(":", 1)[0] in ("attn_code_sha256", "bytes_per_launch"):
                     k, v = line.split(":", 1)
                     rec[k] = v.strip()
     except OSError:
         return None
-    if rec.get("attn_source_sha256") != kernel_src_hash or "bytes_per_launch" not in rec:
+    if rec.get("attn_code_sha256") != kernel_src_hash or "bytes_per_launch" not in rec:
         return None
     return int(rec["bytes_per_launch"])
 
@@ -440,18 +453,17 @@ def bwd_traffic_from_profiles():
     """HBM bytes per backward call (row statistics, dQ and dK/dV kernels) from
     the committed counter summary, or None if the backward source changed."""
     path = os.path.join(ROOT, "profiles", "attn_bwd_skiparse_768p_pmc.md")
-    with open(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn_bwd.hip"), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = code_hash(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn_bwd.hip"))
     rec = {}
     try:
         with open(path) as f:
             for line in f:
-                if ":" in line and line.split(":", 1)[0] in ("bwd_source_sha256", "bytes_per_call"):
+                if ":" in line and line.split(":", 1)[0] in ("bwd_code_sha256", "bytes_per_call"):
                     k, v = line.split(":", 1)
                     rec[k] = v.strip()
     except OSError:
         return None
-    if rec.get("bwd_source_sha256") != sha or "bytes_per_call" not in rec:
+    if rec.get("bwd_code_sha256") != sha or "bytes_per_call" not in rec:
         return None
     return int(rec["bytes_per_call"])
 
@@ -503,8 +515,7 @@ def main():
     attn_flops = sum(per_launch[k] * timer.count.get(k, 0) for k in per_launch)
     peak = FP8_PEAK_TFLOPS if cfg.fp8 else BF16_PEAK_TFLOPS
     achieved = (attn_flops / attn_n) / (attn_ms / attn_n * 1e-3) / 1e12
-    with open(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn.hip"), "rb") as f:
-        src_hash = hashlib.sha256(f.read()).hexdigest()
+    src_hash = code_hash(os.path.join(ROOT, "block_sparse_attention_token_amd", "csrc", "attn.hip"))
     kernels = {k: {"ms_avg": timer.total[k] / timer.count[k], "launches_per_step": timer.count[k] // args.steps}
                for k in timer.total}
     for k, f in per_launch.items():

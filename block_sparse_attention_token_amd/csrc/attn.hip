@@ -804,14 +804,18 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
 //                     max_t v_scale (112 for an all-zero V tile, whose codes
 //                     are all zero).
 // ps is folded into the exponent (p * ps = exp2(S * cs - m + log2 ps)) and
-// the running sum adds the tile's sum of p * ps times 1/ps. The lazy-rescale
+// the running sum adds the tile's sum of p * ps times 1/ps (the four-tile
+// walk sums the rounded P8 on the matrix core, the one-tile walk the
+// unrounded values on the VALU). The lazy-rescale
 // threshold is 2 (p <= 4), so p * ps <= 448 fits e4m3, and one O accumulator
 // scale serves the whole walk: O = acc * max v_scale / 112 / l.
 // The two half-waves each hold 32 of a tile's 64 kv tokens (element e of a
 // lane in half-wave h is token 32*(e/16) + 8*((e%16)/4) + 4*h + e%4), so one
 // K=64 MFMA covers the whole tile in the PV product. The walks are those of
 // the bf16 kernel: pipelined when every wave owns every tile, a plain
-// double-buffered union walk otherwise; LDS rows are padded by 16 bytes.
+// double-buffered union walk otherwise; LDS rows are padded by 16 bytes. The
+// one-tile walk over V in the operand layout copies K and V^T straight into
+// LDS (F8Dma); the others stage them through registers (F8Tile).
 constexpr float kP8Scale = 112.0f;          // 448 / 2^2
 constexpr float kLazyFp8 = 2.0f;
 
