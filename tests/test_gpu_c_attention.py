@@ -351,8 +351,12 @@ def test_tile_and_head_dim_shapes(tile, d, dtype, mode):
     kd, ko = (vsa.tile_permute(blay, to_device(k, dtype)), OL.permute(k, olay).astype(np.float64))
     vd, vo = (vsa.tile_permute(blay, to_device(v, dtype)), OL.permute(v, olay).astype(np.float64))
     n = olay.n_tiles
-    if mode == "shared":
-        lists = OM.window_lists(olay, 1, 1, 1)
+    if mode == "shared":     # one list per group of four query tiles: the pipelined walk
+        lists = []
+        for g in range((n + 3) // 4):
+            row = sorted(set(rng.choice(n, 8, replace=False).tolist()) | {0, 3, 5})
+            lists += [row] * 4
+        lists = lists[:n]
         idx, cnt = table_from_lists(lists)
         lists_fn = OA.shared_lists(lists)
     else:
@@ -555,3 +559,59 @@ def test_natural_io_skiparse_768p_identical():
     torch.cuda.synchronize()
     assert torch.equal(out_n.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(dense_n.view(torch.int16), dense_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", ["shared", "routed"])
+@pytest.mark.parametrize("vop", [False, True])
+def test_fp8_zero_tiles(mode, vop):
+    """Tiles whose absmax is 0 (scale 0, all codes 0) in Q, K and V: a zero K
+    tile scores 0, a zero Q tile gives uniform weights over its key set, a
+    zero V tile keeps its softmax weight but adds nothing to O; both walks
+    (the four-tile walk sums P on the matrix core) and both V layouts, gated
+    against the oracle of the fp8 method."""
+    T, H, W, heads, d = 6, 10, 14, 2, 128
+    olay = OL.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4))
+    blay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, tile=(4, 4, 4))
+    rng = np.random.default_rng(1401 + 2 * vop + (mode == "routed"))
+    from synth import round_to_bf16
+    x = [round_to_bf16(rng.standard_normal((1, olay.n_tokens, heads, d)).astype(np.float32))
+         for _ in range(3)]
+    order = OL.token_order(olay)
+    C, n = olay.tile_tokens, olay.n_tiles
+    for which, tiles in ((0, (1, n - 2)), (1, (0, 3, n - 1)), (2, (2, 5, n - 3))):
+        for t in tiles:
+            nat = order[t * C:(t + 1) * C]
+            x[which][0, nat[nat >= 0], t % heads, :] = 0.0
+    announce(f"attn fp8 zero tiles {mode} v_operand={vop}")
+    if mode == "shared":
+        lists = OM.window_lists(olay, 1, 1, 1)
+        idx, cnt = table_from_lists(lists)
+        lists_fn = OA.shared_lists(lists)
+    else:
+        width = n // 2
+        idx = np.full((1, heads, n, width), -1, dtype=np.int32)
+        cnt = np.zeros((1, heads, n), dtype=np.int32)
+        for h in range(heads):
+            for t in range(n):
+                row = sorted(set(rng.choice(n, width - 1, replace=False).tolist()) | {0, 3, 5})[:width]
+                idx[0, h, t, :len(row)] = row
+                cnt[0, h, t] = len(row)
+        lists_fn = lambda b, h, t: idx[b, h, t, :cnt[b, h, t]].tolist()
+    tiled = [vsa.tile_permute(blay, to_device(a, "bf16")) for a in x]
+    (qc, qs), (kc, ks) = (vsa.quant_fp8_tiles(blay, t) for t in tiled[:2])
+    vc, vs = vsa.quant_fp8_tiles(blay, tiled[2], v_operand=vop)
+    di, dc = lists_to_device(idx, cnt)
+    out, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs), v_operand=vop)
+    torch.cuda.synchronize()
+    assert int((qs == 0).sum()) == 2 and int((ks == 0).sum()) == 3 and int((vs == 0).sum()) == 3
+    xo = [OL.permute(a, olay).astype(np.float32) for a in x]
+    deq = [OF.dequantize_tiles(*OF.quantize_tiles(a, olay), olay) for a in xo]
+    O, _ = OA.attention(*deq, olay, lists_fn, 1.0 / math.sqrt(d))
+    og = out.float().cpu().numpy()
+    assert np.all(np.isfinite(og))
+    items = [(0, h, t) for h in range(heads) for t in range(n)]
+    g = np.concatenate([og[0, h, t * C:(t + 1) * C] for _, h, t in items])
+    r = np.concatenate([O[0, h, t * C:(t + 1) * C] for _, h, t in items])
+    mae, rl2 = errors(g, r)
+    print(f"fp8 zero tiles {mode} vop={vop}: max_abs={mae:.3e} rel_l2={rl2:.3e}")
+    assert rl2 <= REL_L2_FP8
