@@ -330,6 +330,15 @@ vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int
                     "vsa_quant_fp8_tiles_grouped");
 }
 
+// The attention kernels address one (batch, head) slice of a tiled tensor
+// through a buffer resource with 32-bit offsets.
+static vsa_status check_slice(const vsa::DevLayout& L, int32_t dtype) {
+  const long long es = dtype == VSA_F32 ? 4 : (dtype == VSA_BF16 ? 2 : 1);
+  if ((long long)L.n_padded * L.d * es > 0x7FFFFFFFll)
+    return fail(VSA_ERR_UNSUPPORTED, "one (batch, head) slice of a tiled tensor must stay below 2 GiB");
+  return VSA_OK;
+}
+
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,
@@ -358,6 +367,8 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
   }
   const long long work = (long long)L.B * L.heads * L.n_tiles;
   if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  st = check_slice(L, dtype);
+  if (st != VSA_OK) return st;
   vsa::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -430,6 +441,8 @@ vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, co
   if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
   const long long work = (long long)L.B * L.heads * L.n_tiles;
   if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  st = check_slice(L, dtype);
+  if (st != VSA_OK) return st;
   const size_t need = vsa::attn_bwd_workspace_bytes(L);
   if (!workspace || workspace_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
@@ -482,6 +495,8 @@ vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype
   if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
   const long long work = (long long)L.B * L.heads * L.n_tiles;
   if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  st = check_slice(L, dtype);
+  if (st != VSA_OK) return st;
   vsa::AttnArgs a{};
   a.q = q;
   a.k = k;

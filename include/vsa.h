@@ -268,7 +268,10 @@ vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int
  *   lse (optional, may be NULL): float [B, heads, n_padded], natural-log
  *     sum_{j in A(i)} exp(sigma q_i.k_j); -inf for pad rows and empty lists.
  * Supported: tile_tokens in {32, 64}; head_dim in {64, 128}; the fp8 dtypes
- * need tile_tokens 64 and head_dim 128. */
+ * need tile_tokens 64 and head_dim 128; one (batch, head) slice of q, k or v
+ * (n_padded * d elements) must stay below 2 GiB, as the kernels address it
+ * with 32-bit offsets (VSA_ERR_UNSUPPORTED otherwise; the same holds for the
+ * natural-order forward and the backward). */
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,

@@ -216,3 +216,21 @@ def test_permute_pool_argument_errors_before_launch():
                    None, None, 0, None) == B.VSA_ERR_WORKSPACE
     assert _status(g, L, qp, kp, ctypes.c_float(0.1), 0, ctypes.c_float(0.9), 16, 600, FAKE, FAKE,
                    None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
+
+
+def test_slice_over_2gib_rejected_before_launch():
+    """One (batch, head) slice of tiled f32 Q/K/V past 2 GiB (64 x 256 x 256
+    tokens, d = 128: exactly 2^31 bytes) cannot be addressed with 32-bit
+    buffer offsets: UNSUPPORTED from the forward and the backward."""
+    lay = vsa.Layout(T=64, H=256, W=256, heads=1, head_dim=128).c()
+    L = ctypes.byref(lay)
+    far = [ctypes.c_void_p((i + 1) << 33) for i in range(12)]    # 8 GiB apart: no overlaps
+    q, k, v, o = far[:4]
+    assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_F32, q, k, v, None, None, None, None, None,
+                   0, 0, ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+    assert b"2 GiB" in B.lib().vsa_last_error()
+    ws = B.lib().vsa_block_sparse_attn_bwd_workspace(L)
+    assert _status("vsa_block_sparse_attn_bwd", L, B.VSA_F32, q, k, v, o, far[4], far[5], None, None,
+                   0, None, None, 0, ctypes.c_float(0.1), far[6], far[7], far[8], far[9], ws,
+                   None) == B.VSA_ERR_UNSUPPORTED
+    assert b"2 GiB" in B.lib().vsa_last_error()
