@@ -368,6 +368,10 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
   }
   const float2 st = a.rowstat[row0 + min(qt, L.n_tiles - 1) * C + qrow];
   const float nl = -st.x, dd = st.y;
+  // dP^T accumulators start at -D, so they end as dP - D
+  f32x16_t neg_dd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_dd[r] = -dd;
   const float sl2 = a.scale_log2;
 
   f32x16_t acc[D / 32];
@@ -406,24 +410,30 @@ void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
       const uint32_t kbits = block_real_bits(L, ent & 0xFFFFFF, 32 * (b % SUB), lane, half);
       const uint4* kb = k_lds[buf] + l32 * RB::RS + half;
       const uint4* vb = v_lds[buf] + l32 * RB::RS + half;
-      f32x16_t s = {}, dp = {};
+      f32x16_t s = {}, dp = neg_dd;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         s = mfma(kb[2 * ks], qf[ks], s);
         dp = mfma(vb[2 * ks], gf[ks], dp);
       }
+      // dS^T operands; pad keys (only in tiles with pads) get p = 0
       uint4 dsp[2];
+      auto ds_pack = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float x[8];
+        for (int c = 0; c < 2; ++c) {
+          float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * c + i;
-          const float p = ((kbits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) : 0.0f;
-          x[i] = p * (dp[r] - dd);
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * c + i;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
+            if constexpr (decltype(masked)::value) p = ((kbits >> r) & 1u) ? p : 0.0f;
+            x[i] = p * dp[r];
+          }
+          dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
         }
-        dsp[c] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-      }
+      };
+      if (kbits == 0xFFFFu) ds_pack(std::false_type{});    // full tiles: uniform across the wave
+      else ds_pack(std::true_type{});
       const uint16_t* kt = reinterpret_cast<const uint16_t*>(k_lds[buf]) + tro;
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt)
