@@ -509,9 +509,14 @@ struct BlockCopy {
 // column l%16. The 32 queries of P and dS (C rows 4g + i of the two query
 // tiles, g = l/16) are the contraction slots: slot s of lane group g is query
 // 4g + s (s < 4) or 16 + 4g + s - 4, and the transposed LDS reads of dO and
-// Q gather the same queries. Q and dO blocks are copied into a four-slot LDS
-// ring two blocks ahead (bf16) or staged through registers one block ahead
-// (fp32 inputs).
+// Q gather the same queries. For the dV/dK products the waves split the
+// channels instead of the keys: each wave publishes its packed P and dS (the
+// B operands of its 16 keys, 1 KB each) in LDS, and wave w accumulates
+// channels D/WAVES*w .. for all C keys from every wave's operands, so each
+// wave reads only its own channels of dO^T and Q^T (the half-rate transposed
+// reads) instead of all of them. Q and dO blocks are copied into a
+// three-slot LDS ring one block ahead (bf16) or staged through registers
+// (fp32 inputs); the P/dS exchange has two slots.
 template <int RSE>
 __device__ __forceinline__ int tr16_lane_offset(int lane) {
   const int g = lane >> 4, i = lane & 15;
@@ -525,18 +530,23 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 template <int C, int D, bool F32IN>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
-  constexpr int WAVES = C / 16, THREADS = 64 * WAVES, SUB = C / 32, NBUF = 4;
+  constexpr int WAVES = C / 16, THREADS = 64 * WAVES, SUB = C / 32, NBUF = 3;
+  constexpr int NCT = D / WAVES / 16, NKT = WAVES;    // channel and key tiles of a wave's dK/dV
   constexpr int ES = F32IN ? 4 : 2;
   constexpr bool DMA = !F32IN;
   using RB = RowBlock<D, THREADS, F32IN>;
   using BC = BlockCopy<D, WAVES>;
   constexpr int RSE = RB::RSE;
-  __shared__ uint4 q_s0[RB::LDS], q_s1[RB::LDS], q_s2[RB::LDS], q_s3[RB::LDS];
-  __shared__ uint4 g_s0[RB::LDS], g_s1[RB::LDS], g_s2[RB::LDS], g_s3[RB::LDS];
-  __shared__ float4 st_s0[16], st_s1[16], st_s2[16], st_s3[16];   // 32 rows of {lse2, D}
-  auto qbuf = [&](int i) -> uint4* { return i == 0 ? q_s0 : i == 1 ? q_s1 : i == 2 ? q_s2 : q_s3; };
-  auto gbuf = [&](int i) -> uint4* { return i == 0 ? g_s0 : i == 1 ? g_s1 : i == 2 ? g_s2 : g_s3; };
-  auto sbuf = [&](int i) -> float4* { return i == 0 ? st_s0 : i == 1 ? st_s1 : i == 2 ? st_s2 : st_s3; };
+  __shared__ uint4 q_s0[RB::LDS], q_s1[RB::LDS], q_s2[RB::LDS];
+  __shared__ uint4 g_s0[RB::LDS], g_s1[RB::LDS], g_s2[RB::LDS];
+  __shared__ float4 st_s0[16], st_s1[16], st_s2[16];   // 32 rows of {lse2, D}
+  __shared__ uint4 xp0[THREADS], xp1[THREADS], xp2[THREADS];   // P / dS exchange, slot = block % 3
+  __shared__ uint4 xd0[THREADS], xd1[THREADS], xd2[THREADS];
+  auto qbuf = [&](int i) -> uint4* { return i == 0 ? q_s0 : i == 1 ? q_s1 : q_s2; };
+  auto gbuf = [&](int i) -> uint4* { return i == 0 ? g_s0 : i == 1 ? g_s1 : g_s2; };
+  auto sbuf = [&](int i) -> float4* { return i == 0 ? st_s0 : i == 1 ? st_s1 : st_s2; };
+  auto xpbuf = [&](int i) -> uint4* { return i == 0 ? xp0 : i == 1 ? xp1 : xp2; };
+  auto xdbuf = [&](int i) -> uint4* { return i == 0 ? xd0 : i == 1 ? xd1 : xd2; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -571,15 +581,26 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     vf[kc] = bload8<F32IN>(rv, koff + (32 * kc + 8 * g) * ES, 0);
   }
   const float sl2 = a.scale_log2;
-  f32x4_t dk[D / 16], dv[D / 16];
+  // dK^T / dV^T of channel tile ct (channels D/WAVES*wave + 16 ct ..) and key tile j (keys 16 j ..)
+  f32x4_t dk[NCT][NKT], dv[NCT][NKT];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) dk[dt] = dv[dt] = f32x4_t{};
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int j = 0; j < NKT; ++j) dk[ct][j] = dv[ct][j] = f32x4_t{};
 
   const int nblk = cnt * SUB;
+  // list entries come from a 64-entry register window (lane i holds entry
+  // base + i), refilled once per 64 entries: no per-block memory load whose
+  // wait would also wait for the copies in flight
+  int lwin = 0, lbase = -64;
   auto first_row = [&](int b) -> int {
     b = min(b, nblk - 1);
     const int e = b / SUB;
-    const int t = list ? min(max(list[e], 0), L.n_tiles - 1) : e;
+    if (e - lbase >= 64) {
+      lbase = e & ~63;
+      lwin = list ? list[min(lbase + lane, cnt - 1)] : lbase + lane;
+    }
+    const int t = min(max(__builtin_amdgcn_readlane(lwin, e - lbase), 0), L.n_tiles - 1);
     return __builtin_amdgcn_readfirstlane(t * C + 32 * (b % SUB));
   };
   BC cp;
@@ -587,8 +608,7 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   RB qio, gio;
   float2 streg = make_float2(0.0f, 0.0f);
   constexpr int VM0 = 2 * BC::NIW0 + 1, VM1 = 2 * BC::NIW1;
-  auto copy_blk = [&](int b, uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
-    const int r = first_row(b);
+  auto copy_blk = [&](int r, uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
     if constexpr (DMA) {
       const uint32_t soff = (uint32_t)(r * D * ES);
       cp.issue(rq, qd, soff, wave);
@@ -616,23 +636,31 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   };
   const int tro = tr16_lane_offset<RSE>(lane);
 
-  // dV^T += dO^T . P and dK^T += Q^T . dS over 16-channel tiles
-  auto accumulate = [&](const uint4* qs, const uint4* gs, const uint4& pp, const uint4& dsp)
+  // dV^T += dO^T . P and dK^T += Q^T . dS for this wave's channel tiles and
+  // every wave's keys (xp / xd: the published B operands of one block)
+  const int ch0 = (D / WAVES) * wave;
+  auto accumulate = [&](const uint4* qs, const uint4* gs, const uint4* xp, const uint4* xd)
       __attribute__((always_inline)) {
-    const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro;
-    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro;
+    const uint16_t* gt = reinterpret_cast<const uint16_t*>(gs) + tro + ch0;
+    const uint16_t* qt_ = reinterpret_cast<const uint16_t*>(qs) + tro + ch0;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const uint2 glo = lds_tr(gt + 16 * dt), ghi = lds_tr(gt + 16 * RSE + 16 * dt);
-      const uint2 qlo = lds_tr(qt_ + 16 * dt), qhi = lds_tr(qt_ + 16 * RSE + 16 * dt);
-      dv[dt] = mfma16(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pp, dv[dt]);
-      dk[dt] = mfma16(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsp, dk[dt]);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint2 glo = lds_tr(gt + 16 * ct), ghi = lds_tr(gt + 16 * RSE + 16 * ct);
+      const uint2 qlo = lds_tr(qt_ + 16 * ct), qhi = lds_tr(qt_ + 16 * RSE + 16 * ct);
+      const uint4 ga = make_uint4(glo.x, glo.y, ghi.x, ghi.y), qa = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) {
+        dv[ct][j] = mfma16(ga, xp[64 * j + lane], dv[ct][j]);
+        dk[ct][j] = mfma16(qa, xd[64 * j + lane], dk[ct][j]);
+      }
     }
   };
-  // block s's scores and packed P, dS; block s-1's dV / dK products (its
-  // slot is not refilled before the next barrier)
-  auto step = [&](int s, const uint4* qs, const uint4* gs, const float4* st, const uint4* qp,
-                  const uint4* gp, uint4& pp_prev, uint4& ds_prev) __attribute__((always_inline)) {
+  // block s's scores and packed P, dS (published in exchange slot s % 3);
+  // block s-1's dV / dK products from its Q / dO slot and exchange slot (not
+  // refilled before the next barrier)
+  auto step = [&](const uint4* qs, const uint4* gs, const float4* st, const uint4* qp,
+                  const uint4* gp, const uint4* xpr, const uint4* xdr, uint4* xpw, uint4* xdw)
+      __attribute__((always_inline)) {
     // S and dP: two 16-query tiles
     f32x4_t sc[2], dp[2];
 #pragma unroll
@@ -663,51 +691,67 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     }
     const uint4 pp = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
     const uint4 dsp = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-    accumulate(qp, gp, pp_prev, ds_prev);
-    pp_prev = pp;
-    ds_prev = dsp;
-    (void)s;
+    accumulate(qp, gp, xpr, xdr);
+    xpw[tid] = pp;
+    xdw[tid] = dsp;
   };
 
   using C1 = std::integral_constant<int, 1>;
   using C0 = std::integral_constant<int, 0>;
-  constexpr int AHEAD = DMA ? 2 : 1;
-  // "block -1": zero slot 3 and zero operands, so step 0 adds nothing
-  uint4 pp_prev = make_uint4(0u, 0u, 0u, 0u), ds_prev = make_uint4(0u, 0u, 0u, 0u);
+  // "block -1": zero Q / dO slot 2 and exchange slot 2, so step 0 adds nothing.
+  // The walk is unrolled by three so that every slot is a compile-time array:
+  // reads of one slot then need not wait for the copy in flight into another.
+  int nrow = 0;                           // first row of the next block to copy
   if (nblk > 0) {
     for (int i = tid; i < RB::LDS; i += THREADS) {
-      q_s3[i] = make_uint4(0u, 0u, 0u, 0u);
-      g_s3[i] = make_uint4(0u, 0u, 0u, 0u);
+      q_s2[i] = make_uint4(0u, 0u, 0u, 0u);
+      g_s2[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    copy_blk(0, q_s0, g_s0, st_s0);
+    xp2[tid] = make_uint4(0u, 0u, 0u, 0u);
+    xd2[tid] = make_uint4(0u, 0u, 0u, 0u);
+    copy_blk(first_row(0), q_s0, g_s0, st_s0);
     store_regs(q_s0, g_s0, st_s0);
-    if constexpr (DMA) {
-      copy_blk(1, q_s1, g_s1, st_s1);
-      wait_copies(C1{});
-    }
+    nrow = first_row(1);
+    wait_copies(C0{});
     __syncthreads();
   }
-  for (int s = 0; s < nblk; ++s) {
-    const int in = (s + AHEAD) % NBUF, cur = s % NBUF, prv = (s + NBUF - 1) % NBUF;
-    copy_blk(s + AHEAD, qbuf(in), gbuf(in), sbuf(in));
-    step(s, qbuf(cur), gbuf(cur), sbuf(cur), qbuf(prv), gbuf(prv), pp_prev, ds_prev);
+  wait_vmcnt<0>();                        // K / V operands in registers (also when the list is empty)
+  auto body = [&](auto phase, int s) __attribute__((always_inline)) {
+    constexpr int cur = decltype(phase)::value, in = (cur + 1) % NBUF, prv = (cur + NBUF - 1) % NBUF;
+    const int r2 = first_row(s + 2);      // before the copies: a window refill waits for nothing else
+    copy_blk(nrow, qbuf(in), gbuf(in), sbuf(in));
+    nrow = r2;
+    step(qbuf(cur), gbuf(cur), sbuf(cur), qbuf(prv), gbuf(prv), xpbuf(prv), xdbuf(prv), xpbuf(cur),
+         xdbuf(cur));
     store_regs(qbuf(in), gbuf(in), sbuf(in));
-    wait_copies(C1{});
+    wait_copies(C0{});                    // block s+1 has landed
     __syncthreads();
+  };
+  using C2 = std::integral_constant<int, 2>;
+  for (int s = 0; s < nblk; s += 3) {
+    body(C0{}, s);
+    if (s + 1 >= nblk) break;
+    body(C1{}, s + 1);
+    if (s + 2 >= nblk) break;
+    body(C2{}, s + 2);
   }
-  if (nblk > 0) accumulate(qbuf((nblk - 1) % NBUF), gbuf((nblk - 1) % NBUF), pp_prev, ds_prev);
+  if (nblk > 0)
+    accumulate(qbuf((nblk - 1) % NBUF), gbuf((nblk - 1) % NBUF), xpbuf((nblk - 1) % NBUF),
+               xdbuf((nblk - 1) % NBUF));
   wait_copies(C0{});                      // no copy into LDS outlives the workgroup
 
-  const bool real = row_is_real(L, tile_valid(L, kt), krow);
-  const long long orow = row0 + kt * C + krow;
+  const TileValid tvk = tile_valid(L, kt);
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    const int c0 = 16 * dt + 4 * g;
+  for (int t = 0; t < NCT * NKT; ++t) {
+    const int ct = t / NKT, j = t % NKT;
+    const bool real = row_is_real(L, tvk, 16 * j + l16);
+    const long long orow = row0 + kt * C + 16 * j + l16;
+    const int c0 = ch0 + 16 * ct + 4 * g;
     const float f = a.scale;
-    const float k0 = real ? dk[dt][0] * f : 0.0f, k1 = real ? dk[dt][1] * f : 0.0f;
-    const float k2 = real ? dk[dt][2] * f : 0.0f, k3 = real ? dk[dt][3] * f : 0.0f;
-    const float v0 = real ? dv[dt][0] : 0.0f, v1 = real ? dv[dt][1] : 0.0f;
-    const float v2 = real ? dv[dt][2] : 0.0f, v3 = real ? dv[dt][3] : 0.0f;
+    const float k0 = real ? dk[ct][j][0] * f : 0.0f, k1 = real ? dk[ct][j][1] * f : 0.0f;
+    const float k2 = real ? dk[ct][j][2] * f : 0.0f, k3 = real ? dk[ct][j][3] * f : 0.0f;
+    const float v0 = real ? dv[ct][j][0] : 0.0f, v1 = real ? dv[ct][j][1] : 0.0f;
+    const float v2 = real ? dv[ct][j][2] : 0.0f, v3 = real ? dv[ct][j][3] : 0.0f;
     if constexpr (F32IN) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.dk) + orow * D + c0) = make_float4(k0, k1, k2, k3);
       *reinterpret_cast<float4*>(static_cast<float*>(a.dv) + orow * D + c0) = make_float4(v0, v1, v2, v3);
