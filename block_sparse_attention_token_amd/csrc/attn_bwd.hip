@@ -496,14 +496,16 @@ struct BlockCopy {
 };
 
 // dK and dV: one workgroup per (b, head, key tile), 16 key rows per wave
-// (v_mfma_f32_16x16x32_bf16, C/16 waves per tile). A wave holds its K and V
-// operands and both accumulators in about 150 registers, so two waves share
-// each SIMD and cover each other's latencies (owning 32 keys with 32x32
-// products needs more than 256 registers, one wave per SIMD). Per 32-query
-// block a wave computes
-//   S = Q . K^T, dP = dO . V^T          (2 query tiles x 4 channel chunks each)
-//   dV^T += dO^T . P, dK^T += Q^T . dS  (8 channel tiles each, the 32 queries
-//                                        as one contraction chunk)
+// for the scores (v_mfma_f32_16x16x32_bf16, C/16 waves per tile). A wave
+// holds its K and V operands and the accumulators of its share of dK/dV in
+// about 210 registers, so two waves share each SIMD and cover each other's
+// latencies (owning 32 keys with 32x32 products needs more than 256
+// registers, one wave per SIMD). Per 32-query block a wave computes
+//   S = Q . K^T, dP = dO . V^T          (its 16 keys; 2 query tiles x 4
+//                                        channel chunks each)
+//   dV^T += dO^T . P, dK^T += Q^T . dS  (its D/WAVES channels x all C keys,
+//                                        the 32 queries as one contraction
+//                                        chunk)
 // 16x16x32 operand layouts: A lane l holds row l%16, k = 8*(l/16) .. +7; B
 // lane l holds column l%16, the same k; C lane l holds rows 4*(l/16) + i,
 // column l%16. The 32 queries of P and dS (C rows 4g + i of the two query
@@ -516,7 +518,7 @@ struct BlockCopy {
 // wave reads only its own channels of dO^T and Q^T (the half-rate transposed
 // reads) instead of all of them. Q and dO blocks are copied into a
 // three-slot LDS ring one block ahead (bf16) or staged through registers
-// (fp32 inputs); the P/dS exchange has two slots.
+// (fp32 inputs); the P/dS exchange has three slots as well.
 template <int RSE>
 __device__ __forceinline__ int tr16_lane_offset(int lane) {
   const int g = lane >> 4, i = lane & 15;
@@ -607,7 +609,6 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   if constexpr (DMA) cp.init(wave, lane);
   RB qio, gio;
   float2 streg = make_float2(0.0f, 0.0f);
-  constexpr int VM0 = 2 * BC::NIW0 + 1, VM1 = 2 * BC::NIW1;
   auto copy_blk = [&](int r, uint4* qd, uint4* gd, float4* sd) __attribute__((always_inline)) {
     if constexpr (DMA) {
       const uint32_t soff = (uint32_t)(r * D * ES);
@@ -627,12 +628,9 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
       if (tid < 32) reinterpret_cast<float2*>(sd)[tid] = streg;
     }
   };
-  auto wait_copies = [&](auto batches) __attribute__((always_inline)) {
-    if constexpr (DMA) {
-      constexpr int NB = decltype(batches)::value;
-      if (wave == 0) wait_vmcnt<NB * VM0>();
-      else wait_vmcnt<NB * VM1>();
-    }
+  // every copy this wave has issued has landed in LDS
+  auto wait_copies = [&]() __attribute__((always_inline)) {
+    if constexpr (DMA) wait_vmcnt<0>();
   };
   const int tro = tr16_lane_offset<RSE>(lane);
 
@@ -712,7 +710,7 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     copy_blk(first_row(0), q_s0, g_s0, st_s0);
     store_regs(q_s0, g_s0, st_s0);
     nrow = first_row(1);
-    wait_copies(C0{});
+    wait_copies();
     __syncthreads();
   }
   wait_vmcnt<0>();                        // K / V operands in registers (also when the list is empty)
@@ -724,7 +722,7 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
     step(qbuf(cur), gbuf(cur), sbuf(cur), qbuf(prv), gbuf(prv), xpbuf(prv), xdbuf(prv), xpbuf(cur),
          xdbuf(cur));
     store_regs(qbuf(in), gbuf(in), sbuf(in));
-    wait_copies(C0{});                    // block s+1 has landed
+    wait_copies();                    // block s+1 has landed
     __syncthreads();
   };
   using C2 = std::integral_constant<int, 2>;
@@ -738,7 +736,7 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   if (nblk > 0)
     accumulate(qbuf((nblk - 1) % NBUF), gbuf((nblk - 1) % NBUF), xpbuf((nblk - 1) % NBUF),
                xdbuf((nblk - 1) % NBUF));
-  wait_copies(C0{});                      // no copy into LDS outlives the workgroup
+  wait_copies();                      // no copy into LDS outlives the workgroup
 
   const TileValid tvk = tile_valid(L, kt);
 #pragma unroll
