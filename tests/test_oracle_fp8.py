@@ -144,3 +144,47 @@ def test_v_operand_layout_is_a_per_tile_transpose():
     a = np.sort(codes.reshape(1, 2, lay.n_tiles, -1), axis=-1)
     b = np.sort(out.reshape(1, 2, lay.n_tiles, -1), axis=-1)
     assert np.array_equal(a, b)
+
+
+def _golden_quant_cases():
+    rows = []
+    for line in read_golden("quant_cases.txt"):
+        a_s, x_s, c_s = line.split()
+        rows.append((float(a_s), float(x_s), int(c_s, 16)))
+    return rows
+
+
+def _one_tile(a, x):
+    """A one-tile layout (one token, d = 8) whose tile holds a (its absmax) and x."""
+    lay = Layout(T=1, H=1, W=1, heads=1, head_dim=8, tile=(1, 1, 1))
+    t = np.zeros((1, 1, lay.n_padded, 8), dtype=np.float32)
+    t[0, 0, 0, 0] = a
+    t[0, 0, 0, 1] = x
+    return lay, t
+
+
+@pytest.mark.parametrize("a,x,code", _golden_quant_cases())
+def test_quantiser_operation_order_golden(a, x, code):
+    """Hand-derived codes at exact rounding midpoints (tests/golden/quant_cases.txt):
+    the codes follow inv = fl32(448 / a), y = fl32(x * inv), RNE."""
+    assert np.float32(x) == x and (np.float32(x).view(np.uint32) & 0xFFFF) == 0   # x is a bf16 value
+    lay, t = _one_tile(a, x)
+    codes, scales = F.quantize_tiles(t, lay)
+    assert int(codes[0, 0, 0, 1]) == code
+    assert int(codes[0, 0, 0, 0]) == 0x7E                  # the absmax itself maps to 448
+    assert scales[0, 0, 0] == np.float32(np.float32(a) / np.float32(448.0))
+
+
+def test_golden_quant_cases_separate_the_operation_orders():
+    """The golden rows reject the two nearby readings: dividing by fl32(a / 448),
+    and forming x * 448 / a in float64 before the e4m3 rounding. (Each row's
+    float64 product is the exact midpoint, so float64 rounds to the even code.)"""
+    by_div = by_f64 = 0
+    for a, x, code in _golden_quant_cases():
+        s = np.float32(np.float32(a) / np.float32(448.0))
+        y_div = np.float32(np.float32(x) / s)
+        by_div += F.e4m3_encode(y_div) != code
+        exact = x * 448.0 / a                       # exact in float64 for these rows
+        assert exact == np.float32(exact)
+        by_f64 += F.e4m3_encode(np.float32(exact)) != code
+    assert by_div >= 1 and by_f64 >= 1
