@@ -77,14 +77,65 @@ def _stream(stream) -> ctypes.c_void_p:
 _DT = {torch.float32: VSA_F32, torch.bfloat16: VSA_BF16}
 
 
+# Argument checks against the layout. The C ABI takes plain pointers and has no
+# way to see a tensor's dtype or size, so a wrong one here would be read or
+# written as if it were right; every check below runs before the call.
+def _want(t: Optional[torch.Tensor], name: str, dtypes, shape=None) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+
+
+def _tiled_shape(lay: "Layout", info) -> tuple:
+    return (lay.batch, lay.heads, int(info.n_padded), lay.head_dim)
+
+
+def _natural_shape(lay: "Layout", info) -> tuple:
+    return (lay.batch, int(info.n_tokens), lay.heads, lay.head_dim)
+
+
+def _check_lists(lay: "Layout", info, kv_idx, kv_cnt, per_head_only=False) -> None:
+    """Forward lists: int32, [n_tiles, max_kv] + [n_tiles] (one shared table) or
+    [B, heads, n_tiles, max_kv] + [B, heads, n_tiles] (per (b, head)); both or neither."""
+    if (kv_idx is None) != (kv_cnt is None):
+        raise ValueError("kv_idx and kv_cnt must be given together")
+    if kv_idx is None:
+        return
+    n = int(info.n_tiles)
+    if kv_idx.dim() == 2 and not per_head_only:
+        lead = (n,)
+    elif kv_idx.dim() == 4:
+        lead = (lay.batch, lay.heads, n)
+    else:
+        raise ValueError("kv_idx must be [n_tiles, max_kv] or [B, heads, n_tiles, max_kv]")
+    if kv_idx.shape[-1] < 1:
+        raise ValueError("kv_idx needs max_kv >= 1 columns")
+    _want(kv_idx, "kv_idx", torch.int32, lead + (kv_idx.shape[-1],))
+    _want(kv_cnt, "kv_cnt", torch.int32, lead)
+
+
+def _ws_bytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
 def tile_permute(lay: Layout, src: torch.Tensor, inverse: bool = False,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Natural [B, T*H*W, heads, d] <-> tiled [B, heads, n_padded, d] (vsa_tile_permute)."""
     info = layout_info(lay)
+    src_shape, dst_shape = _natural_shape(lay, info), _tiled_shape(lay, info)
+    if inverse:
+        src_shape, dst_shape = dst_shape, src_shape
+    _want(src, "src", (torch.float32, torch.bfloat16), src_shape)
     if out is None:
-        shape = ((lay.batch, info.n_tokens, lay.heads, lay.head_dim) if inverse
-                 else (lay.batch, lay.heads, info.n_padded, lay.head_dim))
-        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+        out = torch.empty(dst_shape, dtype=src.dtype, device=src.device)
+    _want(out, "out", src.dtype, dst_shape)
     c = lay.c()
     check(lib().vsa_tile_permute(ctypes.byref(c), _DT.get(src.dtype, -1), _ptr(src), _ptr(out),
                                  1 if inverse else 0, _stream(stream)))
@@ -95,15 +146,15 @@ def tile_permute_pool(lay: Layout, src: torch.Tensor, out: Optional[torch.Tensor
                       pooled: Optional[torch.Tensor] = None, stream=None):
     """bf16 natural -> tiled permute that also returns the fp32 tile means
     [B, heads, n_tiles, d] (vsa_tile_permute_pool): (tiled, pooled)."""
-    if src.dtype != torch.bfloat16:
-        raise ValueError("tile_permute_pool takes bf16 input")
     info = layout_info(lay)
+    _want(src, "src", torch.bfloat16, _natural_shape(lay, info))
     if out is None:
-        out = torch.empty((lay.batch, lay.heads, info.n_padded, lay.head_dim), dtype=src.dtype,
-                          device=src.device)
+        out = torch.empty(_tiled_shape(lay, info), dtype=src.dtype, device=src.device)
     if pooled is None:
         pooled = torch.empty((lay.batch, lay.heads, info.n_tiles, lay.head_dim),
                              dtype=torch.float32, device=src.device)
+    _want(out, "out", torch.bfloat16, _tiled_shape(lay, info))
+    _want(pooled, "pooled", torch.float32, (lay.batch, lay.heads, info.n_tiles, lay.head_dim))
     c = lay.c()
     check(lib().vsa_tile_permute_pool(ctypes.byref(c), _ptr(src), _ptr(out), _ptr(pooled),
                                       _stream(stream)))
@@ -151,6 +202,7 @@ def quant_fp8_tiles_grouped(lay: Layout, x_tiled: torch.Tensor, group: Tuple[int
     """e4m3 codes with one scale per group of tiles (vsa_quant_fp8_tiles_grouped);
     the group's scale is stored for each of its tiles."""
     info = layout_info(lay)
+    _want(x_tiled, "x_tiled", torch.bfloat16, _tiled_shape(lay, info))
     codes = torch.empty(x_tiled.shape, dtype=torch.uint8, device=x_tiled.device)
     scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32,
                          device=x_tiled.device)
@@ -178,6 +230,8 @@ def build_mask_topk(lay: Layout, q_tiled: torch.Tensor, k_tiled: torch.Tensor,
     if max_kv is None:
         max_kv = n if top_p > 0 else min(top_k, n)
     dev = q_tiled.device
+    _want(q_tiled, "q_tiled", torch.bfloat16, _tiled_shape(lay, info))
+    _want(k_tiled, "k_tiled", torch.bfloat16, _tiled_shape(lay, info))
     kv_idx = torch.empty((lay.batch, lay.heads, n, max_kv), dtype=torch.int32, device=dev)
     kv_cnt = torch.empty((lay.batch, lay.heads, n), dtype=torch.int32, device=dev)
     scores = torch.empty((lay.batch, lay.heads, n, n), dtype=torch.float32, device=dev) \
@@ -189,7 +243,7 @@ def build_mask_topk(lay: Layout, q_tiled: torch.Tensor, k_tiled: torch.Tensor,
     check(lib().vsa_build_mask_topk(ctypes.byref(c), _ptr(q_tiled), _ptr(k_tiled),
                                     float(coarse_scale), int(top_k), float(top_p), int(k_floor),
                                     int(max_kv), _ptr(kv_idx), _ptr(kv_cnt), _ptr(scores),
-                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+                                    _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return kv_idx, kv_cnt, scores
 
 
@@ -221,7 +275,7 @@ def build_mask_topk_pooled(lay: Layout, q_pooled: torch.Tensor, k_pooled: torch.
     check(lib().vsa_build_mask_topk_pooled(ctypes.byref(c), _ptr(q_pooled), _ptr(k_pooled),
                                            float(coarse_scale), int(top_k), float(top_p),
                                            int(k_floor), int(max_kv), _ptr(kv_idx), _ptr(kv_cnt),
-                                           _ptr(scores), _ptr(workspace), workspace.numel(),
+                                           _ptr(scores), _ptr(workspace), _ws_bytes(workspace),
                                            _stream(stream)))
     return kv_idx, kv_cnt, scores
 
@@ -233,6 +287,7 @@ def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None, v_operand: 
     tile's codes channel-major in the fp8 P.V operand order, for V).
     """
     info = layout_info(lay)
+    _want(x_tiled, "x_tiled", torch.bfloat16, _tiled_shape(lay, info))
     codes = torch.empty(x_tiled.shape, dtype=torch.uint8, device=x_tiled.device)
     scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32,
                          device=x_tiled.device)
@@ -263,22 +318,35 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     info = layout_info(lay)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    tiled = _tiled_shape(lay, info)
+    _want(q, "q", (torch.float32, torch.bfloat16, torch.uint8), tiled)
+    _want(k, "k", q.dtype, tiled)
+    _want(v, "v", q.dtype, tiled)
+    _check_lists(lay, info, kv_idx, kv_cnt)
+    if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
+        raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
     if q.dtype == torch.uint8:
         dtype, odt = VSA_FP8_E4M3, torch.bfloat16
         if scales is None:
             raise ValueError("fp8 codes need (q_scale, k_scale, v_scale)")
+        for nm, t in zip(("q_scale", "k_scale", "v_scale"), scales):
+            _want(t, nm, torch.float32, (lay.batch, lay.heads, info.n_tiles))
         if v_operand:
             dtype = VSA_FP8_E4M3_VOP
     elif v_operand:
         raise ValueError("v_operand applies to fp8 codes only")
+    elif scales is not None:
+        raise ValueError("scales apply to fp8 codes only")
     else:
         dtype, odt = _DT.get(q.dtype, -1), q.dtype
     if out is None:
-        out = torch.empty((lay.batch, lay.heads, info.n_padded, lay.head_dim), dtype=odt,
-                          device=q.device)
+        out = torch.empty(tiled, dtype=odt, device=q.device)
     if want_lse and lse is None:
         lse = torch.empty((lay.batch, lay.heads, info.n_padded), dtype=torch.float32,
                           device=q.device)
+    _want(out, "out", odt, tiled)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, (lay.batch, lay.heads, info.n_padded))
     if kv_idx is not None:
         max_kv = kv_idx.shape[-1]
         list_mode = (2 if per_tile_walk else 0) if kv_idx.dim() == 2 else 1
@@ -299,6 +367,7 @@ def build_transposed_lists(lay: Layout, kv_idx: torch.Tensor, kv_cnt: torch.Tens
     4-D / 3-D for per-(b, head) lists."""
     info = layout_info(lay)
     n = info.n_tiles
+    _check_lists(lay, info, kv_idx, kv_cnt)
     list_mode = 0 if kv_idx.dim() == 2 else 1
     lead = () if list_mode == 0 else (lay.batch, lay.heads)
     q_idx = torch.empty(lead + (n, n), dtype=torch.int32, device=kv_idx.device)
@@ -332,6 +401,20 @@ def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     """
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    info = layout_info(lay)
+    tiled = _tiled_shape(lay, info)
+    _want(q, "q", (torch.float32, torch.bfloat16), tiled)
+    for nm, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _want(t, nm, q.dtype, tiled)
+    _want(lse, "lse", torch.float32, (lay.batch, lay.heads, info.n_padded))
+    _check_lists(lay, info, kv_idx, kv_cnt)
+    if q_idx is not None or q_cnt is not None:
+        if kv_idx is None:
+            raise ValueError("q_idx / q_cnt need the forward lists kv_idx / kv_cnt")
+        n = int(info.n_tiles)
+        lead = (n,) if kv_idx.dim() == 2 else (lay.batch, lay.heads, n)
+        _want(q_idx, "q_idx", torch.int32, lead + (n,))
+        _want(q_cnt, "q_cnt", torch.int32, lead)
     dtype = _DT.get(q.dtype, -1)
     if kv_idx is not None and q_idx is None:
         q_idx, q_cnt = build_transposed_lists(lay, kv_idx, kv_cnt, stream=stream)
@@ -343,6 +426,8 @@ def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     if grads is None:
         grads = tuple(torch.empty_like(x) for x in (q, k, v))
     dq, dk, dv = grads
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, nm, q.dtype, tiled)
     need = bwd_workspace_bytes(lay)
     if workspace is None:
         workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=q.device)
@@ -350,7 +435,7 @@ def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     check(lib().vsa_block_sparse_attn_bwd(
         ctypes.byref(c), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
         _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), _ptr(q_idx), _ptr(q_cnt), list_mode,
-        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _ws_bytes(workspace),
         _stream(stream)))
     return dq, dk, dv
 
@@ -367,12 +452,22 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
     info = layout_info(lay)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    nat, tiled = _natural_shape(lay, info), _tiled_shape(lay, info)
+    _want(q_nat, "q_nat", (torch.float32, torch.bfloat16), nat)
+    _want(k, "k", q_nat.dtype, tiled)
+    _want(v, "v", q_nat.dtype, tiled)
+    _check_lists(lay, info, kv_idx, kv_cnt)
+    if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
+        raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
     dtype = _DT.get(q_nat.dtype, -1)
     if out is None:
         out = torch.empty_like(q_nat)
     if want_lse and lse is None:
         lse = torch.empty((lay.batch, lay.heads, info.n_padded), dtype=torch.float32,
                           device=q_nat.device)
+    _want(out, "out", q_nat.dtype, nat)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, (lay.batch, lay.heads, info.n_padded))
     if kv_idx is not None:
         max_kv = kv_idx.shape[-1]
         list_mode = (2 if per_tile_walk else 0) if kv_idx.dim() == 2 else 1
