@@ -253,7 +253,8 @@ def build_mask_topk_pooled(lay: Layout, q_pooled: torch.Tensor, k_pooled: torch.
                            want_scores: bool = False, workspace: Optional[torch.Tensor] = None,
                            stream=None):
     """Routed lists from pooled tile means (vsa_build_mask_topk_pooled):
-    (kv_idx, kv_cnt, scores or None), as build_mask_topk."""
+    (kv_idx, kv_cnt, scores or None), as build_mask_topk. Needs no workspace
+    (``workspace`` is accepted and ignored)."""
     info = layout_info(lay)
     n = info.n_tiles
     if coarse_scale is None:
@@ -268,14 +269,12 @@ def build_mask_topk_pooled(lay: Layout, q_pooled: torch.Tensor, k_pooled: torch.
     kv_cnt = torch.empty((lay.batch, lay.heads, n), dtype=torch.int32, device=dev)
     scores = torch.empty((lay.batch, lay.heads, n, n), dtype=torch.float32, device=dev) \
         if want_scores else None
-    need = topk_workspace_bytes(lay)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     c = lay.c()
     check(lib().vsa_build_mask_topk_pooled(ctypes.byref(c), _ptr(q_pooled), _ptr(k_pooled),
                                            float(coarse_scale), int(top_k), float(top_p),
                                            int(k_floor), int(max_kv), _ptr(kv_idx), _ptr(kv_cnt),
-                                           _ptr(scores), _ptr(workspace), _ws_bytes(workspace),
+                                           _ptr(scores), _ptr(workspace),
+                                           0 if workspace is None else _ws_bytes(workspace),
                                            _stream(stream)))
     return kv_idx, kv_cnt, scores
 

@@ -223,9 +223,11 @@ size_t vsa_build_mask_topk_workspace(const vsa_layout* layout) {
 }
 
 // Checks shared by both routing entry points (after the input pointers).
+// need_ws: the call pools Q and K into the workspace (vsa_build_mask_topk);
+// the call from pooled means needs none.
 static vsa_status check_route(const vsa::DevLayout& L, float coarse_scale, int32_t top_k,
                               float top_p, int32_t k_floor, int32_t max_kv, const void* workspace,
-                              size_t workspace_bytes) {
+                              size_t workspace_bytes, bool need_ws) {
   if (L.n_tiles > 4096) return fail(VSA_ERR_UNSUPPORTED, "routing supports at most 4096 tiles");
   if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "routing needs head_dim <= 256, multiple of 8");
   if (!isfinite(coarse_scale)) return fail(VSA_ERR_INVALID, "coarse_scale must be finite");
@@ -239,9 +241,12 @@ static vsa_status check_route(const vsa::DevLayout& L, float coarse_scale, int32
     if (max_kv < need) return fail(VSA_ERR_INVALID, "max_kv %d < %d", max_kv, need);
   }
   if (L.B * L.heads > 65535) return fail(VSA_ERR_UNSUPPORTED, "batch * heads too large");
-  const size_t need_ws = vsa::route_workspace_bytes(L);
-  if (!workspace || workspace_bytes < need_ws)
-    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need_ws);
+  if (need_ws) {
+    const size_t bytes = vsa::route_workspace_bytes(L);
+    if (!workspace || workspace_bytes < bytes)
+      return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", bytes);
+    if (!aligned16(workspace)) return fail(VSA_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
   return VSA_OK;
 }
 
@@ -255,7 +260,7 @@ vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, co
   if (!q_tiled || !k_tiled || !kv_idx || !kv_cnt)
     return fail(VSA_ERR_INVALID, "q_tiled, k_tiled, kv_idx and kv_cnt must be non-NULL");
   if (!aligned16(q_tiled) || !aligned16(k_tiled)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
-  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes);
+  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes, true);
   if (st != VSA_OK) return st;
   return hip_status(vsa::launch_route(L, q_tiled, k_tiled, coarse_scale, top_k, top_p, k_floor,
                                       max_kv, kv_idx, kv_cnt, scores, workspace,
@@ -273,12 +278,14 @@ vsa_status vsa_build_mask_topk_pooled(const vsa_layout* layout, const float* q_p
   if (st != VSA_OK) return st;
   if (!q_pooled || !k_pooled || !kv_idx || !kv_cnt)
     return fail(VSA_ERR_INVALID, "q_pooled, k_pooled, kv_idx and kv_cnt must be non-NULL");
-  if (((uintptr_t)q_pooled | (uintptr_t)k_pooled) & 3u)
-    return fail(VSA_ERR_INVALID, "pooled means must be 4-byte aligned");
-  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes);
+  if (!aligned16(q_pooled) || !aligned16(k_pooled))
+    return fail(VSA_ERR_INVALID, "pooled means must be 16-byte aligned");
+  st = check_route(L, coarse_scale, top_k, top_p, k_floor, max_kv, workspace, workspace_bytes, false);
   if (st != VSA_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;
   return hip_status(vsa::launch_route_pooled(L, q_pooled, k_pooled, coarse_scale, top_k, top_p,
-                                             k_floor, max_kv, kv_idx, kv_cnt, scores, workspace,
+                                             k_floor, max_kv, kv_idx, kv_cnt, scores,
                                              static_cast<hipStream_t>(stream)),
                     "vsa_build_mask_topk_pooled");
 }

@@ -161,16 +161,24 @@ vsa_status vsa_build_mask_window_grouped(const vsa_layout* layout, int32_t gt, i
  *   q_tiled, k_tiled: bf16 [B, heads, n_padded, d] (output of vsa_tile_permute).
  * Steps, per (b, head):
  *   pooled tile means over real (non-pad) tokens, in fp32;
- *   s_ij = coarse_scale * <qbar_i, kbar_j>;
+ *   s_ij = coarse_scale * <qbar_i, kbar_j> (fp32, the products accumulated
+ *   in increasing channel order);
  *   top_p <= 0: keep the top_k highest-scoring key tiles (ties: lower index);
  *   top_p  > 0: p_ij = softmax_j(s_ij); keep the shortest prefix of the
  *               descending order whose mass reaches top_p, then at least
- *               k_floor tiles (capped at n_tiles); top_k is unused.
+ *               k_floor tiles (capped at n_tiles); top_k is unused. The mass
+ *               of a prefix is an fp32 sum in a fixed order, so where the
+ *               exact mass at the cut lies within rounding of top_p the count
+ *               may differ by one from an exact evaluation.
+ * Scores and selection run in one pass: no n_tiles x n_tiles buffer is
+ * formed unless `scores` is requested.
  * Outputs: kv_idx int32 [B, heads, n_tiles, max_kv] ascending, kv_cnt int32
  *   [B, heads, n_tiles]; scores (optional, may be NULL) float [B, heads,
  *   n_tiles, n_tiles] holding s_ij.
- * workspace: device memory of at least vsa_build_mask_topk_workspace() bytes.
+ * workspace: device memory of at least vsa_build_mask_topk_workspace() bytes
+ *   (the pooled means of Q and K), 16-byte aligned.
  * Limits: n_tiles <= 4096, head_dim <= 256 and a multiple of 8.
+ * Deterministic: repeated calls give identical lists.
  * VSA_ERR_INVALID if max_kv < the largest possible count (top_k, or n_tiles
  * for top-p). */
 vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, const void* k_tiled,
@@ -178,7 +186,8 @@ vsa_status vsa_build_mask_topk(const vsa_layout* layout, const void* q_tiled, co
                                int32_t max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes vsa_build_mask_topk needs for this layout (0 on a bad layout). */
+/* Workspace bytes vsa_build_mask_topk needs for this layout: 2 * B * heads *
+ * n_tiles * head_dim * 4 (0 on a bad layout). */
 size_t vsa_build_mask_topk_workspace(const vsa_layout* layout);
 
 /* S1 with S3 folded in: FVAttn summary (video-aware block organisation: the
@@ -197,10 +206,10 @@ vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void
 
 /* S4 from pooled means: vsa_build_mask_topk's scoring and selection (same
  * rules, limits and outputs) on q_pooled and k_pooled, float [B, heads,
- * n_tiles, d] as written by vsa_tile_permute_pool. Given the means that
- * vsa_build_mask_topk would pool from the same Q and K, the lists and scores
- * are bit-identical to its. workspace: at least vsa_build_mask_topk_workspace()
- * bytes. */
+ * n_tiles, d] as written by vsa_tile_permute_pool (16-byte aligned). Given
+ * the means that vsa_build_mask_topk would pool from the same Q and K, the
+ * lists and scores are bit-identical to its. Needs no workspace: workspace
+ * and workspace_bytes are ignored (NULL and 0 are fine). */
 vsa_status vsa_build_mask_topk_pooled(const vsa_layout* layout, const float* q_pooled,
                                       const float* k_pooled, float coarse_scale, int32_t top_k,
                                       float top_p, int32_t k_floor, int32_t max_kv,

@@ -104,7 +104,8 @@ def test_argument_errors_before_launch():
 def test_workspace_query():
     lay = vsa.Layout(T=21, H=45, W=80, heads=40, head_dim=128).c()
     n = B.lib().vsa_build_mask_topk_workspace(ctypes.byref(lay))
-    assert n >= 40 * 1440 * 1440 * 4
+    # the pooled means of Q and K only: no n_tiles x n_tiles score buffer
+    assert n == 2 * 40 * 1440 * 128 * 4
     bad = vsa.Layout(T=0, H=45, W=80, heads=40, head_dim=128).c()
     assert B.lib().vsa_build_mask_topk_workspace(ctypes.byref(bad)) == 0
 
@@ -212,8 +213,9 @@ def test_permute_pool_argument_errors_before_launch():
                    None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
     assert _status(g, L, ctypes.c_void_p(0x100002), kp, ctypes.c_float(0.1), 32, ctypes.c_float(0.0),
                    0, 32, FAKE, FAKE, None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
-    assert _status(g, L, qp, kp, ctypes.c_float(0.1), 32, ctypes.c_float(0.0), 0, 32, FAKE, FAKE,
-                   None, None, 0, None) == B.VSA_ERR_WORKSPACE
+    # routing from pooled means needs no workspace; a misaligned mean is still rejected
+    assert _status(g, L, qp, ctypes.c_void_p(0x200008), ctypes.c_float(0.1), 32, ctypes.c_float(0.0),
+                   0, 32, FAKE, FAKE, None, None, 0, None) == B.VSA_ERR_INVALID
     assert _status(g, L, qp, kp, ctypes.c_float(0.1), 0, ctypes.c_float(0.9), 16, 600, FAKE, FAKE,
                    None, FAKE, 1 << 40, None) == B.VSA_ERR_INVALID
 

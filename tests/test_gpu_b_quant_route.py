@@ -1,5 +1,6 @@
 """GPU parity: fp8 quantiser (bit-exact) and adaptive routing (exact up to near-ties)."""
 import math
+import sys
 
 import numpy as np
 import pytest
@@ -96,7 +97,12 @@ def _accept_topk(gpu_row, ref_row, s, k):
 
 
 def _accept_topp(gpu_row, s, p, floor):
-    """GPU row acceptable under the top-p rule given oracle scores s (fp64)."""
+    """GPU row acceptable under the top-p rule given oracle scores s (fp64).
+
+    Returns False, "count" (the row keeps the oracle's count and differs only
+    by swaps between tiles whose oracle scores lie within TIE of the cut) or
+    "mass" (the count differs by one, admitted because the oracle's cumulative
+    mass at the cut lies within TIE of p: the mass-tie reading)."""
     order = sorted([j for j in range(len(s)) if np.isfinite(s[j])], key=lambda j: (-s[j], j))
     vals = np.array([s[j] for j in order])
     w = np.exp(vals - vals.max())
@@ -115,7 +121,9 @@ def _accept_topp(gpu_row, s, p, floor):
         return False
     ref = set(order[:m])
     cut = s[order[m - 1]]
-    return all(abs(s[j] - cut) <= TIE for j in set(gpu_row) ^ ref)
+    if not all(abs(s[j] - cut) <= TIE for j in set(gpu_row) ^ ref):
+        return False
+    return "count" if m == c else "mass"
 
 
 def _oracle_scores(cfg, olay, q, k):
@@ -162,17 +170,25 @@ def test_topp_routing_workload():
     s = _oracle_scores(cfg, olay, q, k)
     gi, gc = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
     ridx, rcnt = OR.select_lists_vectorized(s, top_p=cfg.top_p, k_floor=cfg.k_floor)
-    n_same = int((gc == rcnt).sum())
     bad = []
+    admitted = {"count": 0, "mass": 0}
     for h in range(cfg.heads):
         for i in range(olay.n_tiles):
             g = gi[0, h, i, :gc[0, h, i]].tolist()
             if gc[0, h, i] == rcnt[0, h, i] and g == ridx[0, h, i, :rcnt[0, h, i]].tolist():
                 continue
-            if not _accept_topp(g, s[0, h, i], cfg.top_p, cfg.k_floor):
+            why = _accept_topp(g, s[0, h, i], cfg.top_p, cfg.k_floor)
+            if not why:
                 bad.append((h, i))
+            else:
+                admitted[why] += 1
     assert not bad, f"{len(bad)} rows differ beyond near-ties, e.g. {bad[:5]}"
-    assert n_same >= 0.99 * gc.size
+    # the mass-tie reading may not widen silently: at this workload it admits
+    # a few tens of the 57,600 rows (measured: 0 to 30); at most 0.1% pass
+    print(f"[route topp] rows admitted by score near-ties: {admitted['count']}, "
+          f"by mass near-ties (count +-1): {admitted['mass']}", file=sys.stderr)
+    assert admitted["mass"] <= gc.size // 1000
+    assert admitted["count"] <= gc.size // 1000
     assert int(gc.min()) >= cfg.k_floor
 
 
