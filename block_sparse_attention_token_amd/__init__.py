@@ -28,7 +28,7 @@ __all__ = [
     "build_mask_topk", "build_mask_topk_pooled",
     "quant_fp8_tiles", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat", "build_mask_window_grouped",
     "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
-    "block_sparse_attn_bwd", "VsaError", "EXPORTED",
+    "block_sparse_attn_bwd", "block_sparse_attn_bwd_noalloc", "VsaError", "EXPORTED",
     "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
 ]
 
@@ -436,6 +436,51 @@ def block_sparse_attn_bwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
         _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), _ptr(q_idx), _ptr(q_cnt), list_mode,
         float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _ws_bytes(workspace),
         _stream(stream)))
+    return dq, dk, dv
+
+
+def block_sparse_attn_bwd_noalloc(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                                  kv_idx: Optional[torch.Tensor] = None,
+                                  kv_cnt: Optional[torch.Tensor] = None,
+                                  q_idx: Optional[torch.Tensor] = None,
+                                  q_cnt: Optional[torch.Tensor] = None,
+                                  softmax_scale: Optional[float] = None,
+                                  grads: Tuple[torch.Tensor, torch.Tensor, torch.Tensor] = None,
+                                  stream=None):
+    """block_sparse_attn_bwd without a workspace (vsa_block_sparse_attn_bwd_noalloc):
+    the library's built-in scratch holds the row statistics. ``grads`` (dq, dk,
+    dv) and, for listed attention, the transposed lists must be passed in, so
+    the call allocates nothing."""
+    if grads is None:
+        raise ValueError("grads (dq, dk, dv) must be given: this call allocates nothing")
+    if kv_idx is not None and q_idx is None:
+        raise ValueError("q_idx / q_cnt must be given: this call allocates nothing")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    info = layout_info(lay)
+    tiled = _tiled_shape(lay, info)
+    _want(q, "q", (torch.float32, torch.bfloat16), tiled)
+    for nm, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _want(t, nm, q.dtype, tiled)
+    _want(lse, "lse", torch.float32, (lay.batch, lay.heads, info.n_padded))
+    _check_lists(lay, info, kv_idx, kv_cnt)
+    if kv_idx is not None:
+        n = int(info.n_tiles)
+        lead = (n,) if kv_idx.dim() == 2 else (lay.batch, lay.heads, n)
+        _want(q_idx, "q_idx", torch.int32, lead + (n,))
+        _want(q_cnt, "q_cnt", torch.int32, lead)
+        max_kv, list_mode = kv_idx.shape[-1], (0 if kv_idx.dim() == 2 else 1)
+    else:
+        max_kv, list_mode = 0, 0
+    dq, dk, dv = grads
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, nm, q.dtype, tiled)
+    c = lay.c()
+    check(lib().vsa_block_sparse_attn_bwd_noalloc(
+        ctypes.byref(c), _DT.get(q.dtype, -1), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+        _ptr(lse), _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), _ptr(q_idx), _ptr(q_cnt), list_mode,
+        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
     return dq, dk, dv
 
 

@@ -35,6 +35,8 @@
 
 #include <type_traits>
 
+#include <mutex>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -799,6 +801,30 @@ hipError_t launch_transpose_lists(const DevLayout& L, const int32_t* kv_idx, con
 
 size_t attn_bwd_workspace_bytes(const DevLayout& L) {
   return (size_t)L.B * L.heads * L.n_padded * sizeof(float2);
+}
+
+// Row statistics of the allocation-free backward: a file-scope device array,
+// one copy per GPU (at its own address), held until the process ends. Every
+// call rewrites the rows it uses before reading them, so nothing needs
+// clearing; calls that overlap on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+hipError_t attn_bwd_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_bwd(const DevLayout& L, int dtype, const BwdArgs& a, hipStream_t s) {

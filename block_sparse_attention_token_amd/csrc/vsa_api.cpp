@@ -417,15 +417,15 @@ size_t vsa_block_sparse_attn_bwd_workspace(const vsa_layout* layout) {
   return vsa::attn_bwd_workspace_bytes(L);
 }
 
-vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, const void* q,
-                                     const void* k, const void* v, const void* out,
-                                     const void* dout, const float* lse, const int32_t* kv_idx,
-                                     const int32_t* kv_cnt, int32_t max_kv, const int32_t* q_idx,
-                                     const int32_t* q_cnt, int32_t list_mode, float softmax_scale,
-                                     void* dq, void* dk, void* dv, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
-  vsa::DevLayout L;
-  vsa_status st = derive(layout, &L, nullptr);
+// Argument checks and argument block shared by both backward entry points
+// (everything but the workspace).
+static vsa_status bwd_args(const vsa_layout* layout, int32_t dtype, const void* q, const void* k,
+                           const void* v, const void* out, const void* dout, const float* lse,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_kv,
+                           const int32_t* q_idx, const int32_t* q_cnt, int32_t list_mode,
+                           float softmax_scale, void* dq, void* dk, void* dv, vsa::DevLayout* L,
+                           vsa::BwdArgs* a) {
+  vsa_status st = derive(layout, L, nullptr);
   if (st != VSA_OK) return st;
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
     return fail(VSA_ERR_INVALID, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
@@ -444,38 +444,80 @@ vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, co
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
   if (dtype != VSA_F32 && dtype != VSA_BF16)
     return fail(VSA_ERR_UNSUPPORTED, "the backward pass takes VSA_F32 or VSA_BF16");
-  if (L.C != 32 && L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
-  if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
-  const long long work = (long long)L.B * L.heads * L.n_tiles;
+  if (L->C != 32 && L->C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
+  if (L->d != 64 && L->d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
+  const long long work = (long long)L->B * L->heads * L->n_tiles;
   if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many tiles for one launch");
-  st = check_slice(L, dtype);
+  st = check_slice(*L, dtype);
+  if (st != VSA_OK) return st;
+  *a = vsa::BwdArgs{};
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->out = out;
+  a->dout = dout;
+  a->lse = lse;
+  a->kv_idx = kv_idx;
+  a->kv_cnt = kv_cnt;
+  a->max_kv = lists ? max_kv : L->n_tiles;
+  a->q_idx = q_idx;
+  a->q_cnt = q_cnt;
+  a->list_mode = list_mode;
+  a->scale = softmax_scale;
+  a->scale_log2 = softmax_scale * 1.4426950408889634f;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  return VSA_OK;
+}
+
+vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, const void* q,
+                                     const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, const int32_t* kv_idx,
+                                     const int32_t* kv_cnt, int32_t max_kv, const int32_t* q_idx,
+                                     const int32_t* q_cnt, int32_t list_mode, float softmax_scale,
+                                     void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  vsa::DevLayout L;
+  vsa::BwdArgs a;
+  vsa_status st = bwd_args(layout, dtype, q, k, v, out, dout, lse, kv_idx, kv_cnt, max_kv, q_idx,
+                           q_cnt, list_mode, softmax_scale, dq, dk, dv, &L, &a);
   if (st != VSA_OK) return st;
   const size_t need = vsa::attn_bwd_workspace_bytes(L);
   if (!workspace || workspace_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
     return fail(VSA_ERR_INVALID, "workspace must be 8-byte aligned");
-  vsa::BwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.dout = dout;
-  a.lse = lse;
-  a.kv_idx = kv_idx;
-  a.kv_cnt = kv_cnt;
-  a.max_kv = lists ? max_kv : L.n_tiles;
-  a.q_idx = q_idx;
-  a.q_cnt = q_cnt;
-  a.list_mode = list_mode;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
   a.rowstat = static_cast<float2*>(workspace);
   return hip_status(vsa::launch_attn_bwd(L, dtype, a, static_cast<hipStream_t>(stream)),
                     "vsa_block_sparse_attn_bwd");
+}
+
+vsa_status vsa_block_sparse_attn_bwd_noalloc(const vsa_layout* layout, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const void* out,
+                                             const void* dout, const float* lse,
+                                             const int32_t* kv_idx, const int32_t* kv_cnt,
+                                             int32_t max_kv, const int32_t* q_idx,
+                                             const int32_t* q_cnt, int32_t list_mode,
+                                             float softmax_scale, void* dq, void* dk, void* dv,
+                                             void* stream) {
+  vsa::DevLayout L;
+  vsa::BwdArgs a;
+  vsa_status st = bwd_args(layout, dtype, q, k, v, out, dout, lse, kv_idx, kv_cnt, max_kv, q_idx,
+                           q_cnt, list_mode, softmax_scale, dq, dk, dv, &L, &a);
+  if (st != VSA_OK) return st;
+  const size_t need = vsa::attn_bwd_workspace_bytes(L);
+  if (need > vsa::kBwdScratchBytes)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "the row statistics need %zu bytes; the built-in scratch holds %zu "
+                "(B * heads * n_padded <= %zu rows): call vsa_block_sparse_attn_bwd with a workspace",
+                need, vsa::kBwdScratchBytes, vsa::kBwdScratchBytes / 8);
+  void* ptr = nullptr;
+  const hipError_t e = vsa::attn_bwd_scratch(&ptr);
+  if (e != hipSuccess) return hip_status(e, "vsa_block_sparse_attn_bwd_noalloc: scratch address");
+  a.rowstat = static_cast<float2*>(ptr);
+  return hip_status(vsa::launch_attn_bwd(L, dtype, a, static_cast<hipStream_t>(stream)),
+                    "vsa_block_sparse_attn_bwd_noalloc");
 }
 
 vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,

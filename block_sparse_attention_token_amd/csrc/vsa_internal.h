@@ -188,6 +188,12 @@ struct BwdArgs {
   float2* rowstat;         // workspace: per row {lse * log2(e) (+inf: no weight), dO . O}
 };
 size_t attn_bwd_workspace_bytes(const DevLayout& L);
+// Built-in scratch of the allocation-free backward (row statistics): its
+// size, and its device address on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+constexpr size_t kBwdScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t attn_bwd_scratch(void** ptr);
 hipError_t launch_attn_bwd(const DevLayout& L, int dtype, const BwdArgs& a, hipStream_t s);
 
 }  // namespace vsa

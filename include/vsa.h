@@ -355,6 +355,25 @@ vsa_status vsa_block_sparse_attn_bwd(const vsa_layout* layout, int32_t dtype, co
                                      void* dq, void* dk, void* dv, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* vsa_block_sparse_attn_bwd_noalloc: vsa_block_sparse_attn_bwd (same
+ * arguments, checks and results, bit for bit) without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight training or serving loops, harnesses that forbid allocation. The row
+ * statistics live in a 32 MiB scratch array built into the library, one copy
+ * on every GPU it runs on, held until the process ends; the call allocates
+ * nothing. Limit: B * heads * n_padded <= 4,194,304 rows (8 bytes each; the
+ * 768p Skiparse layer with 40 heads needs 3,225,600), VSA_ERR_UNSUPPORTED
+ * beyond it. Calls on one GPU share that scratch: calls that overlap in time
+ * on one GPU (different streams, or threads) race and must not be issued. */
+vsa_status vsa_block_sparse_attn_bwd_noalloc(const vsa_layout* layout, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const void* out,
+                                             const void* dout, const float* lse,
+                                             const int32_t* kv_idx, const int32_t* kv_cnt,
+                                             int32_t max_kv, const int32_t* q_idx,
+                                             const int32_t* q_cnt, int32_t list_mode,
+                                             float softmax_scale, void* dq, void* dk, void* dv,
+                                             void* stream);
+
 /* ----- diagnostics --------------------------------------------------------- */
 const char* vsa_status_string(int32_t status);
 /* Message for the last failing call on this thread ("" if none). */

@@ -236,3 +236,20 @@ def test_slice_over_2gib_rejected_before_launch():
                    0, None, None, 0, ctypes.c_float(0.1), far[6], far[7], far[8], far[9], ws,
                    None) == B.VSA_ERR_UNSUPPORTED
     assert b"2 GiB" in B.lib().vsa_last_error()
+
+
+def test_noalloc_backward_rejects_layouts_past_its_scratch():
+    """The allocation-free backward checks the row count against its built-in
+    32 MiB scratch before anything else touches the GPU (64 heads of the 768p
+    Skiparse grid are 5,160,960 rows, past the 4,194,304 it holds)."""
+    lay = vsa.Layout(T=21, H=48, W=80, heads=64, head_dim=128, kind="skiparse2d").c()
+    L = ctypes.byref(lay)
+    p = [_fake(i) for i in range(8)]
+    st = _status("vsa_block_sparse_attn_bwd_noalloc", L, B.VSA_BF16, p[0], p[1], p[2], p[3], p[4],
+                 p[5], None, None, 0, None, None, 0, ctypes.c_float(0.1), p[6], p[7], _fake(9), None)
+    assert st == B.VSA_ERR_UNSUPPORTED
+    assert b"scratch" in B.lib().vsa_last_error()
+    # the shared argument checks run first: a null gradient is rejected the same way
+    st = _status("vsa_block_sparse_attn_bwd_noalloc", L, B.VSA_BF16, p[0], p[1], p[2], p[3], p[4],
+                 p[5], None, None, 0, None, None, 0, ctypes.c_float(0.1), None, p[7], _fake(9), None)
+    assert st == B.VSA_ERR_INVALID
