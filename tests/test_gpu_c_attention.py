@@ -29,6 +29,14 @@ from tests.gpu_util import (announce, errors, inputs, layouts, lists_to_device, 
 pytestmark = pytest.mark.gpu
 
 MAX_ABS, REL_L2, REL_L2_FP8 = 2e-2, 1e-2, 5e-2
+# fp8 lse gates. One-tile (routed) walk: the row sum adds the unrounded
+# weights in fp32, so lse follows the dequantised oracle up to fp32 rounding
+# of scores and exp2. Four-tile walks sum the e4m3-rounded weights on the
+# matrix core: each weight in the e4m3 normal range is off by at most 2^-4
+# relatively (half an e4m3 step), so the row sum is off by at most 2^-4 and
+# lse by at most ln(1 + 2^-4) = 0.061 (measured: up to 3.5e-2 on rows whose
+# list is one or two tiles, where a few weights dominate); gate 6.5e-2.
+FP8_LSE_GATE = {"routed": 2e-3, "window_union": 6.5e-2, "shared_lengths": 6.5e-2}
 
 
 def _tiled(cfg, olay, blay, x):
@@ -419,19 +427,25 @@ def test_fp8_walks(mode):
     tiled = [vsa.tile_permute(blay, to_device(a, "bf16")) for a in x]
     (qc, qs), (kc, ks), (vc, vs) = (vsa.quant_fp8_tiles(blay, t) for t in tiled)
     di, dc = lists_to_device(idx, cnt)
-    out, _ = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs))
+    out, lse = vsa.block_sparse_attn_fwd(blay, qc, kc, vc, di, dc, scales=(qs, ks, vs), want_lse=True)
     torch.cuda.synchronize()
     xo = [OL.permute(a, olay).astype(np.float32) for a in x]
     deq = [OF.dequantize_tiles(*OF.quantize_tiles(a, olay), olay) for a in xo]
-    O, _ = OA.attention(*deq, olay, lists_fn, 1.0 / math.sqrt(d))
+    O, Lr = OA.attention(*deq, olay, lists_fn, 1.0 / math.sqrt(d))
     og = out.float().cpu().numpy()
     C = olay.tile_tokens
     items = [(0, h, t) for h in range(heads) for t in range(n)]
     g = np.concatenate([og[0, h, t * C:(t + 1) * C] for _, h, t in items])
     r = np.concatenate([O[0, h, t * C:(t + 1) * C] for _, h, t in items])
     mae, rl2 = errors(g, r)
-    print(f"fp8 {mode}: max_abs={mae:.3e} rel_l2={rl2:.3e}")
+    # lse against the oracle's on the dequantised inputs (natural log)
+    lg, lr = lse.cpu().numpy(), Lr
+    fin = np.isfinite(lr)
+    assert np.array_equal(np.isfinite(lg), fin)
+    lerr = float(np.abs(lg[fin] - lr[fin]).max())
+    print(f"fp8 {mode}: max_abs={mae:.3e} rel_l2={rl2:.3e} lse_max_abs={lerr:.3e}")
     assert rl2 <= REL_L2_FP8
+    assert lerr <= FP8_LSE_GATE[mode]
     empty = [(h, t) for h in range(heads) for t in range(n) if not lists_fn(0, h, t)]
     for h, t in empty:
         assert np.all(og[0, h, t * C:(t + 1) * C] == 0)
