@@ -7,10 +7,16 @@ natural-order Q, K, V to natural-order O: tile permute of K and V, attention
 over the cached fixed lists (built once per shape, as a Skiparse pattern is
 head- and data-invariant) with the permute of Q and the inverse permute of
 O fused into the kernel. The other four workloads are measured after it and
-reported under "per_workload" (one layer per step each).
+reported under "per_workload" (one layer per step each); the routed ones
+also from natural-order inputs to natural-order O: the 720p fp8 top-p layer
+quantises each tensor straight from the natural order (Q and K with the
+routing's tile means), routes from the means and writes O in the natural
+order; the top-32 layer pools Q without a tiled copy, permutes K (with its
+means) and V, and reads Q / writes O in the natural order.
 
 Printed: ONE JSON line. value = executed TFLOP/s of the attention over the
-whole timed step (permutes included in the time); roofline = the attention
+whole timed step (permutes included in the time; ms_per_step is the median
+of the per-step times, the mean is also given); roofline = the attention
 kernel's executed FLOP per launch / its average launch time (HIP events on
 the launch stream) against the 2.5 PFLOP/s dense bf16 peak; cpu_baseline =
 the fp64 oracle timed on this host on a seeded sample of (head, query tile)
@@ -60,6 +66,7 @@ class Timer:
         self.pending = {}
         self.total = {}
         self.count = {}
+        self.times = {}
 
     def run(self, name, fn):
         t = self.torch
@@ -74,14 +81,23 @@ class Timer:
         self.torch.cuda.synchronize()
         for name, evs in self.pending.items():
             for e0, e1 in evs:
-                self.total[name] = self.total.get(name, 0.0) + e0.elapsed_time(e1)
+                t = e0.elapsed_time(e1)
+                self.total[name] = self.total.get(name, 0.0) + t
                 self.count[name] = self.count.get(name, 0) + 1
+                self.times.setdefault(name, []).append(t)
         self.pending.clear()
+
+    def median(self, name):
+        """Median launch time of one kernel kind (ms); robust to a stray slow launch."""
+        t = sorted(self.times[name])
+        m = len(t)
+        return t[m // 2] if m % 2 else 0.5 * (t[m // 2 - 1] + t[m // 2])
 
     def reset(self):
         self.pending.clear()
         self.total.clear()
         self.count.clear()
+        self.times.clear()
 
 
 def to_dev(x, dtype, torch, np):
@@ -127,26 +143,31 @@ def build_workload(name, torch, np, vsa):
                 timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(
                     lay, nat[0], tk, tv, kv_idx, kv_cnt, per_tile_walk=cfg.mask == "window"))
             return
-        # routed lists: Q and K are permuted with the routing's tile means pooled on
-        # the way, so the routing reads only the means
-        (tq, qp), (tk, kp) = (timer.run("permute_pool", lambda x=x: vsa.tile_permute_pool(lay, x))
-                              for x in nat[:2])
-        tv = timer.run("permute", lambda: vsa.tile_permute(lay, nat[2]))
         if cfg.mask == "topk":
+            # routed bf16 layer: the tile means of Q come from a pass that writes no
+            # tiled copy (the attention reads Q in the natural order), K is permuted
+            # with its means pooled on the way, V permuted; O is written in the
+            # natural order by the attention kernel
+            _, qp = timer.run("pool", lambda: vsa.tile_permute_pool(lay, nat[0], means_only=True))
+            tk, kp = timer.run("permute_pool", lambda: vsa.tile_permute_pool(lay, nat[1]))
+            tv = timer.run("permute", lambda: vsa.tile_permute(lay, nat[2]))
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
                 lay, qp, kp, top_k=cfg.top_k))
             state["cnt"] = cnt
-            out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(lay, tq, tk, tv, idx, cnt))
-        else:   # top-p routing on bf16, then fp8 attention
+            timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv, idx, cnt))
+        else:
+            # fp8 top-p layer: each tensor goes from the natural order to tiled e4m3
+            # codes in one pass (Q and K with the routing's tile means, V in the P.V
+            # operand layout); routing on the bf16 means; the fp8 attention writes O
+            # in the natural order
+            (qc, qs, qp), (kc, ks, kp) = (timer.run("quant", lambda x=x: vsa.quant_fp8_tiles_nat(
+                lay, x, want_pooled=True)) for x in nat[:2])
+            vc, vs, _ = timer.run("quant", lambda: vsa.quant_fp8_tiles_nat(lay, nat[2], v_operand=True))
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
                 lay, qp, kp, top_p=cfg.top_p, k_floor=cfg.k_floor))
             state["cnt"] = cnt
-            # V quantised straight into the fp8 P.V operand layout
-            (qc, qs), (kc, ks), (vc, vs) = (timer.run("quant", lambda x=x, vop=vop: vsa.quant_fp8_tiles(
-                lay, x, v_operand=vop)) for x, vop in ((tq, False), (tk, False), (tv, True)))
-            out, _ = timer.run("attn", lambda: vsa.block_sparse_attn_fwd(
-                lay, qc, kc, vc, idx, cnt, scales=(qs, ks, vs), v_operand=True))
-        timer.run("unpermute", lambda: vsa.tile_permute(lay, out, inverse=True))
+            timer.run("attn", lambda: vsa.block_sparse_attn_fwd_fp8_nat(
+                lay, qc, kc, vc, (qs, ks, vs), idx, cnt, v_operand=True))
 
     def step(timer):
         if cfg.dense_every:
@@ -198,8 +219,24 @@ def build_workload(name, torch, np, vsa):
         del scratch, tk, tv
         return total / reps
 
+    def hbm_bytes():
+        """Algorithmic HBM bytes per launch of each data-movement kernel: every
+        input byte read once and every output byte written once (pad rows of a
+        tiled tensor count as written)."""
+        es = 2 if cfg.dtype == "bf16" else 4
+        row = cfg.heads * d
+        nat_b, til_b = info.n_tokens * row * es, info.n_padded * row * es
+        means = n * row * 4
+        out = {"permute": nat_b + til_b, "unpermute": nat_b + til_b,
+               "permute_pool": nat_b + til_b + means, "pool": nat_b + means}
+        if cfg.fp8:
+            codes, scales = info.n_padded * row, n * cfg.heads * 4
+            # quantiser launches per layer: Q and K with their means, V without
+            out["quant"] = nat_b + codes + scales + (2 * means) / 3
+        return out
+
     state.update(step=step, flops=flops, dense_equiv=dense_equiv, nat=nat, head_spread=head_spread,
-                 cold_attn=cold_attn)
+                 cold_attn=cold_attn, hbm_bytes=hbm_bytes)
     return state
 
 
@@ -324,23 +361,29 @@ def measure_big_tiles(torch, np, vsa, reps=5):
 
 
 def measure(state, torch, steps, warmup):
+    """Warm-up steps, then `steps` timed steps with a HIP event before each step
+    and after the last (all on the launch stream). Returns the median step time
+    (ms), the mean step time, the wall time of the timed region and the timer of
+    the individual launches."""
     timer = Timer(torch)
     for _ in range(warmup):
         state["step"](timer)
     timer.collect()
     timer.reset()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t_wall = time.time()
-    e0.record()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         state["step"](timer)
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.time() - t_wall
-    ms_step = e0.elapsed_time(e1) / steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    median = per_step[steps // 2] if steps % 2 else 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
+    mean = evs[0].elapsed_time(evs[-1]) / steps
     timer.collect()
-    return ms_step, wall, timer
+    return median, mean, wall, timer
 
 
 def cpu_baseline(name, np, seconds=12.0, bwd_seconds=0.0):
@@ -379,13 +422,17 @@ def cpu_baseline(name, np, seconds=12.0, bwd_seconds=0.0):
     el = time.time() - t0
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in blas] + [1])
+        blas_name = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads, blas_name = len(os.sched_getaffinity(0)), "unknown"
     fwd = {
         "value": exec_flops(done_pairs, cfg.head_dim, lay.tile_tokens) / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "blas": blas_name,
+        "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{n_items} seeded (head, query-tile) items of the {name} sparse layer, "
                   f"fp64 numpy, {el:.1f}s wall",
@@ -408,6 +455,7 @@ def cpu_baseline(name, np, seconds=12.0, bwd_seconds=0.0):
         "value": 2.5 * exec_flops(done_pairs, cfg.head_dim, lay.tile_tokens) / el / 1e12,
         "unit": "TFLOP/s (algorithmic: 2.5x the forward's FLOP)",
         "cores": int(threads),
+        "blas": blas_name,
         "kind": "oracle",
         "sample": f"{n_items} seeded (head, query-tile) items of the {name} sparse layer backward, "
                   f"fp64 numpy, {el:.1f}s wall",
@@ -505,7 +553,7 @@ def main():
 
     head = build_workload(args.workload, torch, np, vsa)
     cfg = head["cfg"]
-    ms_step, wall, timer = measure(head, torch, args.steps, args.warmup)
+    ms_step, ms_mean, wall, timer = measure(head, torch, args.steps, args.warmup)
     step_flops, per_launch = head["flops"]()
     value = step_flops / (ms_step * 1e-3) / 1e12
     layers = cfg.dense_every or 1
@@ -529,10 +577,25 @@ def main():
             "tflops": per_launch["attn"] / (cold_ms * 1e-3) / 1e12,
             "frac_of_peak": per_launch["attn"] / (cold_ms * 1e-3) / 1e12 / peak}
     info = head["info"]
-    perm_bytes = 2 * info.n_tokens * cfg.heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
-    if "permute" in kernels:
-        kernels["permute"]["gbs"] = perm_bytes / (kernels["permute"]["ms_avg"] * 1e-3) / 1e9
-        kernels["permute"]["frac_of_hbm_peak"] = kernels["permute"]["gbs"] / HBM_PEAK_GBS
+    hbm = head["hbm_bytes"]()
+    for k in hbm:
+        if k in kernels:
+            kernels[k]["gbs"] = hbm[k] / (kernels[k]["ms_avg"] * 1e-3) / 1e9
+            kernels[k]["frac_of_hbm_peak"] = kernels[k]["gbs"] / HBM_PEAK_GBS
+    # plain device-to-device copy of 1 GiB on the same device: the HBM rate a
+    # pure read + write stream reaches here (reference for the permute's rate)
+    src_c = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst_c = torch.empty_like(src_c)
+    dst_c.copy_(src_c)
+    torch.cuda.synchronize()
+    ec0, ec1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ec0.record()
+    for _ in range(5):
+        dst_c.copy_(src_c)
+    ec1.record()
+    torch.cuda.synchronize()
+    kernels["copy_1GiB_reference"] = {"gbs": 2 * (1 << 30) * 5 / (ec0.elapsed_time(ec1) * 1e-3) / 1e9}
+    del src_c, dst_c
 
     out = {
         "metric": METRIC,
@@ -542,6 +605,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
+        "ms_per_step_mean": round(ms_mean, 3),
+        "timing": "median of the per-step HIP-event times (mean also given)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -585,10 +650,10 @@ def main():
             if name == args.workload:
                 continue
             st = build_workload(name, torch, np, vsa)
-            ms, _, tm = measure(st, torch, 20, 3)
+            ms, _, _, tm = measure(st, torch, 20, 3)
             f, pl = st["flops"]()
             pk = FP8_PEAK_TFLOPS if st["cfg"].fp8 else BF16_PEAK_TFLOPS
-            a_ms = tm.total["attn"] / tm.count["attn"]
+            a_ms = tm.median("attn")
             per[name] = {
                 "ms_per_layer": round(ms / (st["cfg"].dense_every or 1), 4),
                 "exec_tflops_step": round(f / (ms * 1e-3) / 1e12, 2),
@@ -596,8 +661,15 @@ def main():
                 "attn_tflops": round(pl["attn"] / (a_ms * 1e-3) / 1e12, 2),
                 "attn_frac_of_peak": round(pl["attn"] / (a_ms * 1e-3) / 1e12 / pk, 4),
                 "peak_tflops": pk,
-                "kernels_ms": {k: round(tm.total[k] / tm.count[k], 4) for k in tm.total},
+                "kernels_ms": {k: round(tm.median(k), 4) for k in tm.total},
+                "kernel_times": "median launch time per kernel kind",
             }
+            hbm = st["hbm_bytes"]()
+            per[name]["hbm"] = {k: {"gb_per_launch": round(hbm[k] / 1e9, 4),
+                                    "gbs": round(hbm[k] / (tm.median(k) * 1e-3) / 1e9, 1),
+                                    "frac_of_hbm_peak": round(hbm[k] / (tm.median(k) * 1e-3)
+                                                              / 1e9 / HBM_PEAK_GBS, 4)}
+                                for k in hbm if k in tm.total}
             if st["cfg"].fp8:
                 per[name]["attn_frac_of_bf16_peak"] = round(
                     pl["attn"] / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)

@@ -26,7 +26,8 @@ from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, 
 __all__ = [
     "Layout", "layout_info", "tile_permute", "tile_permute_pool", "build_mask_window",
     "build_mask_topk", "build_mask_topk_pooled",
-    "quant_fp8_tiles", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat", "build_mask_window_grouped",
+    "quant_fp8_tiles", "quant_fp8_tiles_nat", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat",
+    "block_sparse_attn_fwd_fp8_nat", "build_mask_window_grouped",
     "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
     "block_sparse_attn_bwd", "block_sparse_attn_bwd_noalloc", "VsaError", "EXPORTED",
     "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
@@ -143,17 +144,21 @@ def tile_permute(lay: Layout, src: torch.Tensor, inverse: bool = False,
 
 
 def tile_permute_pool(lay: Layout, src: torch.Tensor, out: Optional[torch.Tensor] = None,
-                      pooled: Optional[torch.Tensor] = None, stream=None):
+                      pooled: Optional[torch.Tensor] = None, stream=None, means_only: bool = False):
     """bf16 natural -> tiled permute that also returns the fp32 tile means
-    [B, heads, n_tiles, d] (vsa_tile_permute_pool): (tiled, pooled)."""
+    [B, heads, n_tiles, d] (vsa_tile_permute_pool): (tiled, pooled); with
+    ``means_only`` no tiled copy is written: (None, pooled)."""
     info = layout_info(lay)
     _want(src, "src", torch.bfloat16, _natural_shape(lay, info))
-    if out is None:
+    if out is None and not means_only:
         out = torch.empty(_tiled_shape(lay, info), dtype=src.dtype, device=src.device)
     if pooled is None:
         pooled = torch.empty((lay.batch, lay.heads, info.n_tiles, lay.head_dim),
                              dtype=torch.float32, device=src.device)
-    _want(out, "out", torch.bfloat16, _tiled_shape(lay, info))
+    if not means_only:
+        _want(out, "out", torch.bfloat16, _tiled_shape(lay, info))
+    else:
+        out = None
     _want(pooled, "pooled", torch.float32, (lay.batch, lay.heads, info.n_tiles, lay.head_dim))
     c = lay.c()
     check(lib().vsa_tile_permute_pool(ctypes.byref(c), _ptr(src), _ptr(out), _ptr(pooled),
@@ -294,6 +299,67 @@ def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None, v_operand: 
     fn = lib().vsa_quant_fp8_tiles_v if v_operand else lib().vsa_quant_fp8_tiles
     check(fn(ctypes.byref(c), _ptr(x_tiled), _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def quant_fp8_tiles_nat(lay: Layout, x_nat: torch.Tensor, v_operand: bool = False,
+                        want_pooled: bool = False, stream=None):
+    """Natural-order bf16 [B, T*H*W, heads, d] -> tiled e4m3 codes and scales in
+    one pass (vsa_quant_fp8_tiles_nat); the same bits as tile_permute then
+    quant_fp8_tiles. Returns (codes, scales, pooled means or None)."""
+    info = layout_info(lay)
+    _want(x_nat, "x_nat", torch.bfloat16, _natural_shape(lay, info))
+    dev = x_nat.device
+    codes = torch.empty(_tiled_shape(lay, info), dtype=torch.uint8, device=dev)
+    scales = torch.empty((lay.batch, lay.heads, info.n_tiles), dtype=torch.float32, device=dev)
+    pooled = torch.empty((lay.batch, lay.heads, info.n_tiles, lay.head_dim), dtype=torch.float32,
+                         device=dev) if want_pooled else None
+    c = lay.c()
+    check(lib().vsa_quant_fp8_tiles_nat(ctypes.byref(c), _ptr(x_nat), _ptr(codes), _ptr(scales),
+                                        _ptr(pooled), int(bool(v_operand)), _stream(stream)))
+    return codes, scales, pooled
+
+
+def block_sparse_attn_fwd_fp8_nat(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  scales: Tuple[torch.Tensor, torch.Tensor, torch.Tensor],
+                                  kv_idx: Optional[torch.Tensor] = None,
+                                  kv_cnt: Optional[torch.Tensor] = None,
+                                  softmax_scale: Optional[float] = None, want_lse: bool = False,
+                                  out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None, stream=None,
+                                  v_operand: bool = False, per_tile_walk: bool = False):
+    """fp8 forward with O written in the natural order [B, T*H*W, heads, d]
+    (vsa_block_sparse_attn_fwd_fp8_nat); q/k/v tiled e4m3 codes. Returns
+    (out, lse or None); lse tiled."""
+    info = layout_info(lay)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(lay.head_dim)
+    tiled = _tiled_shape(lay, info)
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _want(t, nm, torch.uint8, tiled)
+    for nm, t in zip(("q_scale", "k_scale", "v_scale"), scales):
+        _want(t, nm, torch.float32, (lay.batch, lay.heads, info.n_tiles))
+    _check_lists(lay, info, kv_idx, kv_cnt)
+    if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
+        raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
+    if out is None:
+        out = torch.empty(_natural_shape(lay, info), dtype=torch.bfloat16, device=q.device)
+    _want(out, "out", torch.bfloat16, _natural_shape(lay, info))
+    if want_lse and lse is None:
+        lse = torch.empty((lay.batch, lay.heads, info.n_padded), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, (lay.batch, lay.heads, info.n_padded))
+    if kv_idx is not None:
+        max_kv = kv_idx.shape[-1]
+        list_mode = (2 if per_tile_walk else 0) if kv_idx.dim() == 2 else 1
+    else:
+        max_kv, list_mode = 0, 0
+    qs, ks, vs = scales
+    c = lay.c()
+    check(lib().vsa_block_sparse_attn_fwd_fp8_nat(
+        ctypes.byref(c), VSA_FP8_E4M3_VOP if v_operand else VSA_FP8_E4M3, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(qs), _ptr(ks), _ptr(vs), _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode,
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -1015,7 +1015,10 @@ __device__ __forceinline__ void f8_pv(const uint4* vb, const i32x8_t& pk, f32x16
   }
 }
 
-template <int QPW, bool VOP = false>
+// NAT: O is written to the natural order [B, T*H*W, heads, d] (the inverse
+// tile permute folded into the last store; pad rows have no natural position
+// and are not written); Q, K, V codes and the lse stay tiled.
+template <int QPW, bool VOP = false, bool NAT = false>
 __global__ __launch_bounds__(128 * QPW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int TILE = 64, D = 128, WPQ = 2, MB = 2, CB = 4, SUB = 1, KVH = 64;
@@ -1242,12 +1245,21 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
   const bool real = row_is_real(L, tq, qrow);
   const float inv = (real && lt > 0.0f) ? wmax / (kP8Scale * lt) : 0.0f;
   const long long orow = ww.head_row0 + (long long)ww.qt * TILE + qrow;
+  long long obase = orow;
+  bool store = true;
+  if constexpr (NAT) {
+    const int n = natural_index(L, ww.qt, qrow);
+    const int b = ww.bh / L.heads, h = ww.bh - b * L.heads;
+    store = n >= 0;
+    obase = ((long long)b * L.n_tokens + max(n, 0)) * L.heads + h;
+  }
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      if (!store) break;
       const int c0 = 32 * cb + 8 * g + 4 * half;
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + c0) =
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase * D + c0) =
           make_uint2(pack2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv),
                      pack2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv));
     }
@@ -1274,7 +1286,10 @@ template <int QPW, bool VOP = false>
 hipError_t launch_fp8(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
-  hipLaunchKernelGGL((attn_fp8_kernel<QPW, VOP>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
+  if (a.natural_io)
+    hipLaunchKernelGGL((attn_fp8_kernel<QPW, VOP, true>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
+  else
+    hipLaunchKernelGGL((attn_fp8_kernel<QPW, VOP, false>), dim3(n_work), dim3(128 * QPW), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
 
@@ -1296,7 +1311,6 @@ hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStre
   // shared tables the caller marks as walked per tile (list_mode 2): one
   // query tile per workgroup.
   const bool grouped = (a.kv_idx == nullptr || a.list_mode == 0) && L.n_tiles <= 4096;
-  if (a.natural_io && dtype != 0 && dtype != 1) return hipErrorInvalidValue;
   if (dtype == 3) {   // e4m3 with V codes in the P.V operand layout
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
     return grouped ? launch_fp8<4, true>(L, a, s) : launch_fp8<1, true>(L, a, s);

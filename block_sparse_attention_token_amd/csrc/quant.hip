@@ -126,6 +126,130 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
   }
 }
 
+// The quantiser with the tile permute folded in (FVAttn summary: video-aware
+// block organisation; FPSAttention, Approach: FP8 on the shared tiles): one
+// workgroup per (batch, tile, head) gathers the tile's rows of one head from
+// the natural order [B, T*H*W, heads, d] into registers, takes their absmax,
+// and writes the codes to the tiled position (VOP: in the P.V operand
+// layout) and the scale, exactly as quant_kernel does from the tiled copy.
+// POOL: also the tile's fp32 mean over its real rows, with the rows of each
+// thread and the order of the sums of the routing's pool pass, so the means
+// are bit-identical to it. Thread t takes chunk t % chunks of rows
+// t / chunks + groups * m (groups = 256 / chunks), at most kNatRows rows.
+constexpr int kNatRows = 8;
+
+template <bool VOP, bool POOL>
+__global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const uint4* __restrict__ x,
+                                                             uint2* __restrict__ codes,
+                                                             float* __restrict__ scales,
+                                                             float* __restrict__ pooled) {
+  const int tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int b = blockIdx.z;
+  const int chunks = L.d >> 3;
+  const int groups = kThreads / chunks;
+  const int ch = threadIdx.x % chunks;
+  const int rg = threadIdx.x / chunks;
+  const long long bh = (long long)b * L.heads + head;
+  const long long row0 = bh * L.n_padded + (long long)tile * L.C;
+  // natural position of each row of the tile, found once per row
+  __shared__ int nat_of[kThreads * kNatRows];           // C <= 8 * groups <= 2048 rows
+  for (int r = threadIdx.x; r < L.C; r += kThreads) nat_of[r] = natural_index(L, tile, r);
+  __syncthreads();
+  uint4 xr[kNatRows];
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kNatRows; ++m) {
+    const int r = rg + groups * m;
+    xr[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (rg < groups && r < L.C) {
+      const int nat = nat_of[r];
+      if (nat >= 0) xr[m] = x[(((long long)b * L.n_tokens + nat) * L.heads + head) * chunks + ch];
+    }
+    const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(bf16_lo(ws[e])));
+      amax = fmaxf(amax, fabsf(bf16_hi(ws[e])));
+    }
+  }
+  __shared__ float red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  float a = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+  const float inv = (a > 0.0f) ? __fdiv_rn(448.0f, a) : 0.0f;
+  if (threadIdx.x == 0) scales[bh * L.n_tiles + tile] = (a > 0.0f) ? __fdiv_rn(a, 448.0f) : 0.0f;
+
+  __shared__ uint2 tl[VOP ? 64 * 128 / 8 : 1];       // VOP: the tile's codes, token-major
+#pragma unroll
+  for (int m = 0; m < kNatRows; ++m) {
+    const int r = rg + groups * m;
+    if (rg >= groups || r >= L.C) continue;
+    uint2 out = make_uint2(0u, 0u);
+    if (a != 0.0f) {
+      const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
+        const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
+        packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
+      }
+      out = make_uint2(packed[0], packed[1]);
+    }
+    if constexpr (VOP) tl[r * chunks + ch] = out;
+    else codes[(row0 + r) * chunks + ch] = out;
+  }
+  if constexpr (POOL) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < kNatRows; ++m) {
+      const int r = rg + groups * m;
+      if (rg >= groups || r >= L.C || nat_of[r] < 0) continue;
+      const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(ws[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(ws[e] & 0xFFFF0000u);
+      }
+    }
+    __shared__ float part[kThreads * 8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[threadIdx.x * 8 + e] = acc[e];
+    __syncthreads();
+    const int n = real_rows(L, tile_valid(L, tile));
+    for (int c = threadIdx.x; c < L.d; c += kThreads) {
+      const int cch = c >> 3, ce = c & 7;
+      float sum = 0.0f;
+      for (int g = 0; g < groups; ++g) sum += part[(g * chunks + cch) * 8 + ce];
+      pooled[(bh * L.n_tiles + tile) * L.d + c] = n > 0 ? sum / (float)n : 0.0f;
+    }
+  }
+  if constexpr (VOP) {
+    __syncthreads();
+    const uint8_t* tb = reinterpret_cast<const uint8_t*>(tl);
+    uint4* dst = reinterpret_cast<uint4*>(codes + row0 * chunks);
+    for (int q = threadIdx.x; q < 128 * 4; q += kThreads) {
+      const int c = q >> 2, p0 = 16 * (q & 3);
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int pp = p0 + e;
+        const int h = pp >> 5, A = (pp >> 4) & 1, B = (pp >> 2) & 3, rr = pp & 3;
+        const int t = 32 * A + 8 * B + 4 * h + rr;
+        w[e >> 2] |= (uint32_t)tb[t * 128 + c] << (8 * (e & 3));
+      }
+      dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 // One workgroup per (batch, head, group of gt x gh x gw tiles): the absmax
 // over the real rows of every tile of the group, written to scales[] for
 // each member tile (3D tiles only).
@@ -205,6 +329,22 @@ hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, f
   } else {
     hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(kThreads), 0, s, L,
                        static_cast<const uint4*>(x), reinterpret_cast<uint2*>(codes), scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_nat(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
+                                float* pooled, bool v_operand, hipStream_t s) {
+  dim3 grid(L.n_tiles, L.heads, L.B);
+  const uint4* xs = static_cast<const uint4*>(x);
+  uint2* cs = reinterpret_cast<uint2*>(codes);
+  if (v_operand) {
+    if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
+    if (pooled) hipLaunchKernelGGL((quant_nat_kernel<true, true>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+    else hipLaunchKernelGGL((quant_nat_kernel<true, false>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+  } else {
+    if (pooled) hipLaunchKernelGGL((quant_nat_kernel<false, true>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+    else hipLaunchKernelGGL((quant_nat_kernel<false, false>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
   }
   return hipGetLastError();
 }

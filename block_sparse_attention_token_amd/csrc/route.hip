@@ -27,8 +27,8 @@ constexpr int kRowBatch = 4;      // rows whose loads a pool thread issues toget
 // (odd); pooled is [2][B][heads][n_tiles][d], counts gets the real rows per tile.
 // MOVE = true: the tile permute with the pool folded in. grid (n_tiles, heads,
 // B); q is the natural-order tensor [B, n_tokens, heads, d]; every row read is
-// also written to its tiled position in `tiled` (pad rows as zeros), pooled is
-// [B][heads][n_tiles][d]. Both forms give each thread the same rows and
+// also written to its tiled position in `tiled` (pad rows as zeros; no copy
+// when tiled is null), pooled is [B][heads][n_tiles][d]. Both forms give each thread the same rows and
 // chunks and sum them in the same order, so their means are bit-identical.
 template <bool MOVE>
 __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4* __restrict__ q,
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
       for (int u = 0; u < kRowBatch; ++u) {
         const int r = r0 + u * groups;
         if (r >= L.C) break;
-        if (MOVE) tiled[(row0 + r) * chunks + ch] = real[u] ? w[u] : make_uint4(0u, 0u, 0u, 0u);
+        if (MOVE && tiled) tiled[(row0 + r) * chunks + ch] = real[u] ? w[u] : make_uint4(0u, 0u, 0u, 0u);
         if (!real[u]) continue;
         const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll

@@ -151,9 +151,9 @@ vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
   if (st != VSA_OK) return st;
-  if (!src || !dst || !pooled) return fail(VSA_ERR_INVALID, "src, dst and pooled must be non-NULL");
-  if (!aligned16(src) || !aligned16(dst) || ((uintptr_t)pooled & 3u))
-    return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (!src || !pooled) return fail(VSA_ERR_INVALID, "src and pooled must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst) || !aligned16(pooled))
+    return fail(VSA_ERR_INVALID, "src, dst and pooled must be 16-byte aligned");
   if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be <= 256 and a multiple of 8");
   if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large for one launch");
   const size_t bytes = (size_t)L.B * L.heads * L.d * 2;
@@ -163,7 +163,8 @@ vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void
   const size_t nat_b = bytes * L.n_tokens, til_b = bytes * L.n_padded;
   const size_t pool_b = (size_t)L.B * L.heads * L.n_tiles * L.d * sizeof(float);
   auto overlap = [](const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; };
-  if (overlap(s0, nat_b, d0, til_b) || overlap(s0, nat_b, p0, pool_b) || overlap(d0, til_b, p0, pool_b))
+  if ((dst && overlap(s0, nat_b, d0, til_b)) || overlap(s0, nat_b, p0, pool_b) ||
+      (dst && overlap(d0, til_b, p0, pool_b)))
     return fail(VSA_ERR_INVALID, "src, dst and pooled must not overlap");
   return hip_status(vsa::launch_permute_pool(L, src, dst, pooled, static_cast<hipStream_t>(stream)),
                     "vsa_tile_permute_pool");
@@ -335,6 +336,31 @@ vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int
   return hip_status(vsa::launch_quant_fp8_grouped(L, gt, gh, gw, x_tiled, codes, scales, v_operand != 0,
                                                   static_cast<hipStream_t>(stream)),
                     "vsa_quant_fp8_tiles_grouped");
+}
+
+vsa_status vsa_quant_fp8_tiles_nat(const vsa_layout* layout, const void* x_nat, uint8_t* codes,
+                                   float* scales, float* pooled, int32_t v_operand, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!x_nat || !codes || !scales) return fail(VSA_ERR_INVALID, "x_nat, codes and scales must be non-NULL");
+  if (!aligned16(x_nat) || ((uintptr_t)codes & (v_operand ? 15u : 7u)) || !aligned16(pooled))
+    return fail(VSA_ERR_INVALID, "misaligned pointer");
+  if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be <= 256 and a multiple of 8");
+  const int chunks = L.d / 8, groups = 256 / chunks;
+  if ((L.C + groups - 1) / groups > 8)
+    return fail(VSA_ERR_UNSUPPORTED, "tile_tokens * head_dim must be at most 16,384 (one tile in registers)");
+  if (v_operand && (L.C != 64 || L.d != 128))
+    return fail(VSA_ERR_UNSUPPORTED, "the P.V operand layout needs 64-token tiles and head_dim 128");
+  if (L.heads > 65535 || L.B > 65535) return fail(VSA_ERR_UNSUPPORTED, "grid too large");
+  const size_t nat_b = (size_t)L.B * L.n_tokens * L.heads * L.d * 2;
+  const size_t code_b = (size_t)L.B * L.heads * L.n_padded * L.d;
+  const char* x0 = static_cast<const char*>(x_nat);
+  const char* c0 = reinterpret_cast<const char*>(codes);
+  if (x0 < c0 + code_b && c0 < x0 + nat_b) return fail(VSA_ERR_INVALID, "x_nat and codes must not overlap");
+  return hip_status(vsa::launch_quant_fp8_nat(L, x_nat, codes, scales, pooled, v_operand != 0,
+                                              static_cast<hipStream_t>(stream)),
+                    "vsa_quant_fp8_tiles_nat");
 }
 
 // The attention kernels address one (batch, head) slice of a tiled tensor
@@ -518,6 +544,50 @@ vsa_status vsa_block_sparse_attn_bwd_noalloc(const vsa_layout* layout, int32_t d
   a.rowstat = static_cast<float2*>(ptr);
   return hip_status(vsa::launch_attn_bwd(L, dtype, a, static_cast<hipStream_t>(stream)),
                     "vsa_block_sparse_attn_bwd_noalloc");
+}
+
+vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const float* q_scale,
+                                             const float* k_scale, const float* v_scale,
+                                             const int32_t* kv_idx, const int32_t* kv_cnt,
+                                             int32_t max_kv, int32_t list_mode, float softmax_scale,
+                                             void* out, float* lse, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd_fp8_nat takes the fp8 dtypes");
+  if (!q || !k || !v || !out) return fail(VSA_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (!q_scale || !k_scale || !v_scale) return fail(VSA_ERR_INVALID, "fp8 needs q_scale, k_scale and v_scale");
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr))
+    return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
+  if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
+  if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
+  if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
+  if (L.C != 64 || L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "fp8 attention needs 64-token tiles and head_dim 128");
+  const long long work = (long long)L.B * L.heads * L.n_tiles;
+  if (work > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  st = check_slice(L, dtype);
+  if (st != VSA_OK) return st;
+  vsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = kv_idx ? max_kv : L.n_tiles;
+  a.list_mode = list_mode;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  a.natural_io = 1;
+  return hip_status(vsa::launch_attn(L, dtype, a, static_cast<hipStream_t>(stream)),
+                    "vsa_block_sparse_attn_fwd_fp8_nat");
 }
 
 vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,

@@ -137,6 +137,9 @@ hipError_t launch_permute_pool(const DevLayout& L, const void* src, void* dst, f
 size_t route_workspace_bytes(const DevLayout& L);
 hipError_t launch_quant_fp8(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
                             bool v_operand, hipStream_t s);
+// natural order -> tiled e4m3 codes (+ scales, + tile means when pooled != null)
+hipError_t launch_quant_fp8_nat(const DevLayout& L, const void* x, uint8_t* codes, float* scales,
+                                float* pooled, bool v_operand, hipStream_t s);
 hipError_t launch_mask_window_grouped(const DevLayout& L, int gt, int gh, int gw, int et, int eh,
                                       int ew, int max_kv, int32_t* kv_idx, int32_t* kv_cnt,
                                       hipStream_t s);
@@ -157,7 +160,7 @@ struct AttnArgs {
   float scale_log2;        // softmax scale * log2(e)
   void* out;
   float* lse;
-  int natural_io;          // q read from / out written to [B, T*H*W, heads, d]
+  int natural_io;          // out written to [B, T*H*W, heads, d]; bf16/f32 also read q from it
 };
 hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStream_t s);
 

@@ -198,8 +198,10 @@ size_t vsa_build_mask_topk_workspace(const vsa_layout* layout);
  *   pooled float [B, heads, n_tiles, d]: each tile's mean over its real
  *   tokens, the same fp32 values, bit for bit, as the pooling step inside
  *   vsa_build_mask_topk (0 for a tile without real tokens).
+ * dst may be NULL: the means only (for a Q read by the natural-order
+ * forward, which needs no tiled copy).
  * One pass over the tensor instead of the permute's pass plus the pool's.
- * src, dst 16-byte aligned, pooled 4-byte aligned; buffers must not overlap.
+ * src, dst and pooled 16-byte aligned; buffers must not overlap.
  * VSA_ERR_UNSUPPORTED unless head_dim <= 256 and a multiple of 8. */
 vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void* dst,
                                  float* pooled, void* stream);
@@ -249,6 +251,20 @@ vsa_status vsa_quant_fp8_tiles_v(const vsa_layout* layout, const void* x_tiled, 
 vsa_status vsa_quant_fp8_tiles_grouped(const vsa_layout* layout, int32_t gt, int32_t gh, int32_t gw,
                                        const void* x_tiled, uint8_t* codes, float* scales,
                                        int32_t v_operand, void* stream);
+
+/* vsa_quant_fp8_tiles_nat: S1 and S5 (and S3) in one pass (FVAttn summary:
+ * video-aware block organisation; FPSAttention, Approach: FP8 on the shared
+ * tiles). x_nat bf16 [B, T*H*W, heads, d] in the natural order -> codes and
+ * scales bit-identical to vsa_tile_permute followed by vsa_quant_fp8_tiles
+ * (v_operand 0) or vsa_quant_fp8_tiles_v (v_operand 1); no tiled bf16 copy
+ * is written. pooled (may be NULL) float [B, heads, n_tiles, d]: also the
+ * tile means, bit-identical to vsa_tile_permute_pool's, for routing.
+ * Needs head_dim <= 256 and a multiple of 8 and tile_tokens * head_dim <=
+ * 16,384 (the P.V operand layout: 64-token tiles and head_dim 128),
+ * VSA_ERR_UNSUPPORTED otherwise; x_nat and pooled 16-byte aligned, codes 8
+ * (16 for the operand layout). */
+vsa_status vsa_quant_fp8_tiles_nat(const vsa_layout* layout, const void* x_nat, uint8_t* codes,
+                                   float* scales, float* pooled, int32_t v_operand, void* stream);
 
 /* ----- S6: block-sparse attention forward --------------------------------------
  * The flash-style, FlashAttention-compatible sparse attention every page
@@ -302,6 +318,22 @@ vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype
                                          const void* k, const void* v, const int32_t* kv_idx,
                                          const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
                                          float softmax_scale, void* out, float* lse, void* stream);
+
+/* vsa_block_sparse_attn_fwd_fp8_nat: the fp8 forward (dtype VSA_FP8_E4M3 or
+ * VSA_FP8_E4M3_VOP; q, k, v tiled codes with their scales, lists, list_mode
+ * and scale as for vsa_block_sparse_attn_fwd) with the inverse tile permute
+ * of O folded into the kernel's last store: out is bf16 in the natural order
+ * [B, T*H*W, heads, d], every real token written (FVAttn summary:
+ * video-aware block organisation). lse, if given, is tiled as for the
+ * forward. The result equals vsa_block_sparse_attn_fwd followed by
+ * vsa_tile_permute(inverse), bit for bit. Needs 64-token tiles and head_dim
+ * 128 (VSA_ERR_UNSUPPORTED otherwise). */
+vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const float* q_scale,
+                                             const float* k_scale, const float* v_scale,
+                                             const int32_t* kv_idx, const int32_t* kv_cnt,
+                                             int32_t max_kv, int32_t list_mode, float softmax_scale,
+                                             void* out, float* lse, void* stream);
 
 /* ----- S6 backward: gradients of the block-sparse attention -------------------
  * The pages train through this attention: VSA ("Faster Video Diffusion with

@@ -253,3 +253,25 @@ def test_noalloc_backward_rejects_layouts_past_its_scratch():
     st = _status("vsa_block_sparse_attn_bwd_noalloc", L, B.VSA_BF16, p[0], p[1], p[2], p[3], p[4],
                  p[5], None, None, 0, None, None, 0, ctypes.c_float(0.1), None, p[7], _fake(9), None)
     assert st == B.VSA_ERR_INVALID
+
+
+def test_fused_natural_calls_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    x, c, s, p = _fake(1), _fake(2), _fake(3), _fake(4)
+    f = "vsa_quant_fp8_tiles_nat"
+    assert _status(f, L, None, c, s, p, 0, None) == B.VSA_ERR_INVALID
+    assert _status(f, L, x, c, s, ctypes.c_void_p(0x400004), 0, None) == B.VSA_ERR_INVALID   # pooled misaligned
+    assert _status(f, L, x, x, s, None, 0, None) == B.VSA_ERR_INVALID                          # overlap
+    lay48 = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=48, tile=(4, 4, 4)).c()
+    assert _status(f, ctypes.byref(lay48), x, c, s, None, 1, None) == B.VSA_ERR_UNSUPPORTED  # operand layout
+    big = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=256, tile=(4, 8, 8)).c()
+    assert _status(f, ctypes.byref(big), x, c, s, None, 0, None) == B.VSA_ERR_UNSUPPORTED    # tile too big
+    g = "vsa_block_sparse_attn_fwd_fp8_nat"
+    q, k, v, o = _fake(5), _fake(6), _fake(7), _fake(8)
+    args = lambda dt, sc: (L, dt, q, k, v, sc, sc, sc, None, None, 0, 0, ctypes.c_float(0.1), o, None, None)
+    assert _status(g, *args(B.VSA_BF16, s)) == B.VSA_ERR_UNSUPPORTED
+    assert _status(g, *args(B.VSA_FP8_E4M3, None)) == B.VSA_ERR_INVALID
+    lay64 = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=64).c()
+    assert _status(g, ctypes.byref(lay64), B.VSA_FP8_E4M3, q, k, v, s, s, s, None, None, 0, 0,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
