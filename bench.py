@@ -158,16 +158,18 @@ def build_workload(name, torch, np, vsa):
         else:
             # fp8 top-p layer: each tensor goes from the natural order to tiled e4m3
             # codes in one pass (Q and K with the routing's tile means, V in the P.V
-            # operand layout); routing on the bf16 means; the fp8 attention writes O
-            # in the natural order
+            # operand layout); routing on the bf16 means; the fp8 attention, dealt
+            # heavy-first, writes O in the natural order
             (qc, qs, qp), (kc, ks, kp) = (timer.run("quant", lambda x=x: vsa.quant_fp8_tiles_nat(
                 lay, x, want_pooled=True)) for x in nat[:2])
             vc, vs, _ = timer.run("quant", lambda: vsa.quant_fp8_tiles_nat(lay, nat[2], v_operand=True))
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
                 lay, qp, kp, top_p=cfg.top_p, k_floor=cfg.k_floor))
             state["cnt"] = cnt
+            # top-p lists differ in length: deal the walks heavy-first
+            order = timer.run("order", lambda: vsa.build_work_order(lay, cnt))
             timer.run("attn", lambda: vsa.block_sparse_attn_fwd_fp8_nat(
-                lay, qc, kc, vc, (qs, ks, vs), idx, cnt, v_operand=True))
+                lay, qc, kc, vc, (qs, ks, vs), idx, cnt, v_operand=True, work_order=order))
 
     def step(timer):
         if cfg.dense_every:

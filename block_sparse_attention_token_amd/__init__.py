@@ -284,6 +284,26 @@ def build_mask_topk_pooled(lay: Layout, q_pooled: torch.Tensor, k_pooled: torch.
     return kv_idx, kv_cnt, scores
 
 
+def build_work_order(lay: Layout, kv_cnt: torch.Tensor, stream=None) -> torch.Tensor:
+    """Heavy-first dealing order of the routed walks (vsa_build_work_order):
+    int32 [B * heads * n_tiles], heads by total pairs then query tiles by list
+    length, both descending, ties in index order."""
+    info = layout_info(lay)
+    _want(kv_cnt, "kv_cnt", torch.int32, (lay.batch, lay.heads, info.n_tiles))
+    order = torch.empty(lay.batch * lay.heads * info.n_tiles, dtype=torch.int32, device=kv_cnt.device)
+    c = lay.c()
+    check(lib().vsa_build_work_order(ctypes.byref(c), _ptr(kv_cnt), _ptr(order), _stream(stream)))
+    return order
+
+
+def _check_order(lay: Layout, info, kv_idx, work_order) -> None:
+    if work_order is None:
+        return
+    if kv_idx is None or kv_idx.dim() != 4:
+        raise ValueError("work_order applies to per-head [B, heads, n_tiles, max_kv] lists only")
+    _want(work_order, "work_order", torch.int32, (lay.batch * lay.heads * info.n_tiles,))
+
+
 def quant_fp8_tiles(lay: Layout, x_tiled: torch.Tensor, stream=None, v_operand: bool = False):
     """Per-tile e4m3 codes (uint8, same shape) and scales [B, heads, n_tiles].
 
@@ -326,10 +346,12 @@ def block_sparse_attn_fwd_fp8_nat(lay: Layout, q: torch.Tensor, k: torch.Tensor,
                                   softmax_scale: Optional[float] = None, want_lse: bool = False,
                                   out: Optional[torch.Tensor] = None,
                                   lse: Optional[torch.Tensor] = None, stream=None,
-                                  v_operand: bool = False, per_tile_walk: bool = False):
+                                  v_operand: bool = False, per_tile_walk: bool = False,
+                                  work_order: Optional[torch.Tensor] = None):
     """fp8 forward with O written in the natural order [B, T*H*W, heads, d]
     (vsa_block_sparse_attn_fwd_fp8_nat); q/k/v tiled e4m3 codes. Returns
-    (out, lse or None); lse tiled."""
+    (out, lse or None); lse tiled. ``work_order``: from build_work_order
+    (per-head lists only)."""
     info = layout_info(lay)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(lay.head_dim)
@@ -341,6 +363,7 @@ def block_sparse_attn_fwd_fp8_nat(lay: Layout, q: torch.Tensor, k: torch.Tensor,
     _check_lists(lay, info, kv_idx, kv_cnt)
     if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
         raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
+    _check_order(lay, info, kv_idx, work_order)
     if out is None:
         out = torch.empty(_natural_shape(lay, info), dtype=torch.bfloat16, device=q.device)
     _want(out, "out", torch.bfloat16, _natural_shape(lay, info))
@@ -358,7 +381,7 @@ def block_sparse_attn_fwd_fp8_nat(lay: Layout, q: torch.Tensor, k: torch.Tensor,
     check(lib().vsa_block_sparse_attn_fwd_fp8_nat(
         ctypes.byref(c), VSA_FP8_E4M3_VOP if v_operand else VSA_FP8_E4M3, _ptr(q), _ptr(k), _ptr(v),
         _ptr(qs), _ptr(ks), _ptr(vs), _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode,
-        float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+        _ptr(work_order), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 
@@ -369,7 +392,7 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
                           scales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                           want_lse: bool = False, out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None, stream=None, v_operand: bool = False,
-                          per_tile_walk: bool = False):
+                          per_tile_walk: bool = False, work_order: Optional[torch.Tensor] = None):
     """Block-sparse attention forward (vsa_block_sparse_attn_fwd).
 
     q/k/v tiled; float32 -> float32 out, bfloat16 -> bfloat16 out, uint8 e4m3
@@ -378,6 +401,8 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     kv_idx 2-D [n_tiles, max_kv] = one shared table; 4-D [B, heads, n_tiles,
     max_kv] = per-(b, head) lists; None = dense. ``per_tile_walk`` (2-D
     tables only): each query tile walks its own list (list_mode 2).
+    ``work_order`` (per-head lists only): the dealing order from
+    build_work_order; the output is the same with or without it.
     Returns (out, lse or None).
     """
     info = layout_info(lay)
@@ -390,6 +415,7 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     _check_lists(lay, info, kv_idx, kv_cnt)
     if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
         raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
+    _check_order(lay, info, kv_idx, work_order)
     if q.dtype == torch.uint8:
         dtype, odt = VSA_FP8_E4M3, torch.bfloat16
         if scales is None:
@@ -421,8 +447,8 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
     c = lay.c()
     check(lib().vsa_block_sparse_attn_fwd(
         ctypes.byref(c), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs),
-        _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode, float(softmax_scale), _ptr(out),
-        _ptr(lse), _stream(stream)))
+        _ptr(kv_idx), _ptr(kv_cnt), int(max_kv), list_mode, _ptr(work_order), float(softmax_scale),
+        _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 
@@ -555,7 +581,8 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
                               kv_cnt: Optional[torch.Tensor] = None,
                               softmax_scale: Optional[float] = None, want_lse: bool = False,
                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                              stream=None, per_tile_walk: bool = False):
+                              stream=None, per_tile_walk: bool = False,
+                              work_order: Optional[torch.Tensor] = None):
     """Forward with natural-order Q in and O out (vsa_block_sparse_attn_fwd_nat):
     q_nat and the returned out are [B, T*H*W, heads, d]; k and v tiled.
     Returns (out, lse or None); lse in the tiled order."""
@@ -569,6 +596,7 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
     _check_lists(lay, info, kv_idx, kv_cnt)
     if per_tile_walk and kv_idx is not None and kv_idx.dim() != 2:
         raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
+    _check_order(lay, info, kv_idx, work_order)
     dtype = _DT.get(q_nat.dtype, -1)
     if out is None:
         out = torch.empty_like(q_nat)
@@ -586,5 +614,6 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
     c = lay.c()
     check(lib().vsa_block_sparse_attn_fwd_nat(
         ctypes.byref(c), dtype, _ptr(q_nat), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt),
-        int(max_kv), list_mode, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+        int(max_kv), list_mode, _ptr(work_order), float(softmax_scale), _ptr(out), _ptr(lse),
+        _stream(stream)))
     return out, lse

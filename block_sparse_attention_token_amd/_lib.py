@@ -34,7 +34,7 @@ EXPORTED = (
     "vsa_quant_fp8_tiles_grouped", "vsa_tile_permute_pool", "vsa_build_mask_topk_pooled",
     "vsa_build_transposed_lists", "vsa_block_sparse_attn_bwd_workspace",
     "vsa_block_sparse_attn_bwd", "vsa_block_sparse_attn_bwd_noalloc", "vsa_quant_fp8_tiles_nat",
-    "vsa_block_sparse_attn_fwd_fp8_nat", "vsa_status_string",
+    "vsa_block_sparse_attn_fwd_fp8_nat", "vsa_build_work_order", "vsa_status_string",
     "vsa_last_error", "vsa_version",
 )
 
@@ -82,8 +82,9 @@ def lib() -> ctypes.CDLL:
     L.vsa_build_mask_topk_workspace.restype = SZ
     L.vsa_quant_fp8_tiles.argtypes = [LP, P, P, P, P]
     L.vsa_quant_fp8_tiles_v.argtypes = [LP, P, P, P, P]
-    L.vsa_block_sparse_attn_fwd.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, F32, P, P, P]
-    L.vsa_block_sparse_attn_fwd_nat.argtypes = [LP, I32, P, P, P, P, P, I32, I32, F32, P, P, P]
+    L.vsa_block_sparse_attn_fwd.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, P, F32, P, P, P]
+    L.vsa_block_sparse_attn_fwd_nat.argtypes = [LP, I32, P, P, P, P, P, I32, I32, P, F32, P, P, P]
+    L.vsa_build_work_order.argtypes = [LP, P, P, P]
     L.vsa_build_mask_window_grouped.argtypes = [LP, I32, I32, I32, I32, I32, I32, I32, P, P, P]
     L.vsa_quant_fp8_tiles_grouped.argtypes = [LP, I32, I32, I32, P, P, P, I32, P]
     L.vsa_build_transposed_lists.argtypes = [LP, P, P, I32, I32, P, P, P]
@@ -95,8 +96,8 @@ def lib() -> ctypes.CDLL:
                                                     F32, P, P, P, P]
     L.vsa_tile_permute_pool.argtypes = [LP, P, P, P, P]
     L.vsa_quant_fp8_tiles_nat.argtypes = [LP, P, P, P, P, I32, P]
-    L.vsa_block_sparse_attn_fwd_fp8_nat.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, F32, P,
-                                                    P, P]
+    L.vsa_block_sparse_attn_fwd_fp8_nat.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, P, F32,
+                                                    P, P, P]
     L.vsa_build_mask_topk_pooled.argtypes = [LP, P, P, F32, I32, F32, I32, I32, P, P, P, P, SZ, P]
     for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window",
                  "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
@@ -105,7 +106,7 @@ def lib() -> ctypes.CDLL:
                  "vsa_tile_permute_pool", "vsa_build_mask_topk_pooled",
                  "vsa_build_transposed_lists", "vsa_block_sparse_attn_bwd",
                  "vsa_block_sparse_attn_bwd_noalloc", "vsa_quant_fp8_tiles_nat",
-                 "vsa_block_sparse_attn_fwd_fp8_nat"):
+                 "vsa_block_sparse_attn_fwd_fp8_nat", "vsa_build_work_order"):
         getattr(L, name).restype = I32
     L.vsa_status_string.argtypes = [I32]
     L.vsa_status_string.restype = ctypes.c_char_p

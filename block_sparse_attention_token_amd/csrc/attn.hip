@@ -102,8 +102,12 @@ __device__ __forceinline__ WaveWork wave_work(const DevLayout& L, const AttnArgs
   WaveWork w;
   // shared lists: contiguous ranges (query tiles sharing K/V share an L2);
   // per-head lists: chunks dealt round the XCDs (per-head work differs)
-  const int item = a.kv_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
-                                                 : xcd_remap(blockIdx.x, n_work);
+  int item = a.kv_idx && a.list_mode == 1 ? xcd_chunked(blockIdx.x, n_work, 64)
+                                           : xcd_remap(blockIdx.x, n_work);
+  // a work order deals the items heavy-first (per-head lists, one query tile
+  // per workgroup); entries are clamped so that a bad order cannot address
+  // outside the tensors
+  if (QPW == 1 && a.work_order) item = min(max(a.work_order[item], 0), n_work - 1);
   const int wg_per_bh = (L.n_tiles + QPW - 1) / QPW;
   w.bh = item / wg_per_bh;
   w.slot = wave / WPQ;

@@ -372,12 +372,40 @@ static vsa_status check_slice(const vsa::DevLayout& L, int32_t dtype) {
   return VSA_OK;
 }
 
+// A work order only applies to per-head lists, which are walked one query
+// tile per workgroup.
+static vsa_status check_order(const int32_t* work_order, const int32_t* kv_idx, int32_t list_mode) {
+  if (!work_order) return VSA_OK;
+  if (!kv_idx || list_mode != 1) return fail(VSA_ERR_INVALID, "work_order needs per-head lists (list_mode 1)");
+  if ((uintptr_t)work_order & 3u) return fail(VSA_ERR_INVALID, "work_order must be 4-byte aligned");
+  return VSA_OK;
+}
+
+vsa_status vsa_build_work_order(const vsa_layout* layout, const int32_t* kv_cnt, int32_t* order,
+                                void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!kv_cnt || !order) return fail(VSA_ERR_INVALID, "kv_cnt and order must be non-NULL");
+  if (((uintptr_t)kv_cnt & 3u) || ((uintptr_t)order & 3u))
+    return fail(VSA_ERR_INVALID, "kv_cnt and order must be 4-byte aligned");
+  const long long items = (long long)L.B * L.heads * L.n_tiles;
+  if (items > 0x7FFFFFFFll) return fail(VSA_ERR_UNSUPPORTED, "too many query tiles");
+  if (vsa::work_order_lds_bytes(L) > 65536)
+    return fail(VSA_ERR_UNSUPPORTED, "n_tiles + batch * heads must be at most 16,384");
+  const char* c0 = reinterpret_cast<const char*>(kv_cnt);
+  const char* o0 = reinterpret_cast<const char*>(order);
+  if (c0 < o0 + items * 4 && o0 < c0 + items * 4) return fail(VSA_ERR_INVALID, "kv_cnt and order must not overlap");
+  return hip_status(vsa::launch_work_order(L, kv_cnt, order, static_cast<hipStream_t>(stream)),
+                    "vsa_build_work_order");
+}
+
 vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, const void* q,
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,
                                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_kv,
-                                     int32_t list_mode, float softmax_scale, void* out, float* lse,
-                                     void* stream) {
+                                     int32_t list_mode, const int32_t* work_order,
+                                     float softmax_scale, void* out, float* lse, void* stream) {
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
   if (st != VSA_OK) return st;
@@ -388,6 +416,8 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
     return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
   if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
   if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
+  st = check_order(work_order, kv_idx, list_mode);
+  if (st != VSA_OK) return st;
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
   if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP)
     return fail(VSA_ERR_INVALID, "unknown dtype %d", dtype);
@@ -413,6 +443,7 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
   a.kv_cnt = kv_cnt;
   a.max_kv = kv_idx ? max_kv : L.n_tiles;
   a.list_mode = list_mode;
+  a.work_order = work_order;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
@@ -550,7 +581,8 @@ vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t d
                                              const void* k, const void* v, const float* q_scale,
                                              const float* k_scale, const float* v_scale,
                                              const int32_t* kv_idx, const int32_t* kv_cnt,
-                                             int32_t max_kv, int32_t list_mode, float softmax_scale,
+                                             int32_t max_kv, int32_t list_mode,
+                                             const int32_t* work_order, float softmax_scale,
                                              void* out, float* lse, void* stream) {
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
@@ -565,6 +597,8 @@ vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t d
     return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
   if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
   if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
+  st = check_order(work_order, kv_idx, list_mode);
+  if (st != VSA_OK) return st;
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
   if (L.C != 64 || L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "fp8 attention needs 64-token tiles and head_dim 128");
   const long long work = (long long)L.B * L.heads * L.n_tiles;
@@ -582,6 +616,7 @@ vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t d
   a.kv_cnt = kv_cnt;
   a.max_kv = kv_idx ? max_kv : L.n_tiles;
   a.list_mode = list_mode;
+  a.work_order = work_order;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
@@ -593,7 +628,8 @@ vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t d
 vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,
                                          const void* k, const void* v, const int32_t* kv_idx,
                                          const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
-                                         float softmax_scale, void* out, float* lse, void* stream) {
+                                         const int32_t* work_order, float softmax_scale, void* out,
+                                         float* lse, void* stream) {
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
   if (st != VSA_OK) return st;
@@ -609,6 +645,8 @@ vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype
     return fail(VSA_ERR_INVALID, "kv_idx and kv_cnt must both be set or both be NULL");
   if (kv_idx && max_kv < 1) return fail(VSA_ERR_INVALID, "max_kv must be >= 1");
   if (list_mode < 0 || list_mode > 2) return fail(VSA_ERR_INVALID, "list_mode must be 0, 1 or 2");
+  st = check_order(work_order, kv_idx, list_mode);
+  if (st != VSA_OK) return st;
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
   if (L.C != 32 && L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "attention needs 32- or 64-token tiles");
   if (L.d != 64 && L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "attention needs head_dim 64 or 128");
@@ -624,6 +662,7 @@ vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype
   a.kv_cnt = kv_cnt;
   a.max_kv = kv_idx ? max_kv : L.n_tiles;
   a.list_mode = list_mode;
+  a.work_order = work_order;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;

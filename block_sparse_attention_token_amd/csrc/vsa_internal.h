@@ -161,8 +161,15 @@ struct AttnArgs {
   void* out;
   float* lse;
   int natural_io;          // out written to [B, T*H*W, heads, d]; bf16/f32 also read q from it
+  const int32_t* work_order;   // list_mode 1 only (one query tile per workgroup): item dealt
+                               // at position p is work_order[p]; null: index order
 };
 hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStream_t s);
+
+// Heavy-first order of the (b, head, query tile) items of per-head lists:
+// heads by total pairs, then query tiles by list length, both descending.
+size_t work_order_lds_bytes(const DevLayout& L);
+hipError_t launch_work_order(const DevLayout& L, const int32_t* kv_cnt, int32_t* order, hipStream_t s);
 
 // For every key tile j (per list head): the ascending query tiles whose
 // list holds j. q_idx [LH, n_tiles, n_tiles], q_cnt [LH, n_tiles].

@@ -288,6 +288,12 @@ vsa_status vsa_quant_fp8_tiles_nat(const vsa_layout* layout, const void* x_nat, 
  *     windows); the result is the same.
  *     Both NULL: dense attention (every tile). Indices must lie in
  *     [0, n_tiles) and counts in [0, max_kv]; the kernel does not re-check them.
+ *   work_order (optional, may be NULL; list_mode 1 only, VSA_ERR_INVALID
+ *     otherwise): int32 [B * heads * n_tiles] from vsa_build_work_order, the
+ *     order in which the (b, head, query tile) walks are dealt to the
+ *     workgroups. It changes only the schedule: the output is bit-identical
+ *     with or without it. Entries are clamped into range; an array that is
+ *     not a permutation leaves some tiles unwritten but cannot fault.
  *   out: [B, heads, n_padded, d]; pad query rows and rows with an empty list
  *     are written as 0.
  *   lse (optional, may be NULL): float [B, heads, n_padded], natural-log
@@ -301,8 +307,22 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
                                      const void* k, const void* v, const float* q_scale,
                                      const float* k_scale, const float* v_scale,
                                      const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_kv,
-                                     int32_t list_mode, float softmax_scale, void* out, float* lse,
-                                     void* stream);
+                                     int32_t list_mode, const int32_t* work_order,
+                                     float softmax_scale, void* out, float* lse, void* stream);
+
+/* vsa_build_work_order: S6's heavy-first dealing of routed work (FVAttn
+ * summary, Summary and Abstract: Top-p routing makes the work per head, and
+ * per query tile, uneven). From the counts kv_cnt int32 [B, heads, n_tiles]
+ * of per-head lists (list_mode 1) writes order int32 [B * heads * n_tiles],
+ * a permutation of the items b * heads * n_tiles + head * n_tiles + t:
+ *   (b, head) slices by their total max(cnt, 0) (each count clamped to
+ *   n_tiles), descending, equal totals in index order; within a slice, query
+ *   tiles by count, descending, equal counts in index order.
+ * Deterministic (integer keys and ranks). Needs n_tiles + B * heads <=
+ * 16,384 (VSA_ERR_UNSUPPORTED otherwise); kv_cnt and order 4-byte aligned
+ * and not overlapping. */
+vsa_status vsa_build_work_order(const vsa_layout* layout, const int32_t* kv_cnt, int32_t* order,
+                                void* stream);
 
 /* vsa_block_sparse_attn_fwd_nat: vsa_block_sparse_attn_fwd with the tile
  * permute of Q and the inverse permute of O fused into the kernel (one
@@ -313,15 +333,17 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
  * forward. Every real token of out is written; the result equals the
  * forward's followed by vsa_tile_permute(inverse). dtype VSA_F32 or
  * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise, and when one batch of q exceeds
- * 2 GiB); lists, list_mode and scale as for vsa_block_sparse_attn_fwd. */
+ * 2 GiB); lists, list_mode, work_order and scale as for
+ * vsa_block_sparse_attn_fwd. */
 vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,
                                          const void* k, const void* v, const int32_t* kv_idx,
                                          const int32_t* kv_cnt, int32_t max_kv, int32_t list_mode,
-                                         float softmax_scale, void* out, float* lse, void* stream);
+                                         const int32_t* work_order, float softmax_scale, void* out,
+                                         float* lse, void* stream);
 
 /* vsa_block_sparse_attn_fwd_fp8_nat: the fp8 forward (dtype VSA_FP8_E4M3 or
- * VSA_FP8_E4M3_VOP; q, k, v tiled codes with their scales, lists, list_mode
- * and scale as for vsa_block_sparse_attn_fwd) with the inverse tile permute
+ * VSA_FP8_E4M3_VOP; q, k, v tiled codes with their scales, lists, list_mode,
+ * work_order and scale as for vsa_block_sparse_attn_fwd) with the inverse tile permute
  * of O folded into the kernel's last store: out is bf16 in the natural order
  * [B, T*H*W, heads, d], every real token written (FVAttn summary:
  * video-aware block organisation). lse, if given, is tiled as for the
@@ -332,7 +354,8 @@ vsa_status vsa_block_sparse_attn_fwd_fp8_nat(const vsa_layout* layout, int32_t d
                                              const void* k, const void* v, const float* q_scale,
                                              const float* k_scale, const float* v_scale,
                                              const int32_t* kv_idx, const int32_t* kv_cnt,
-                                             int32_t max_kv, int32_t list_mode, float softmax_scale,
+                                             int32_t max_kv, int32_t list_mode,
+                                             const int32_t* work_order, float softmax_scale,
                                              void* out, float* lse, void* stream);
 
 /* ----- S6 backward: gradients of the block-sparse attention -------------------

@@ -84,19 +84,19 @@ def test_argument_errors_before_launch():
     # unsupported head_dim / tile size
     args = [FAKE, FAKE, FAKE, None, None, None]
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, None, 8, 0,
-                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+                   None, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 3,
-                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+                   None, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_FP8_E4M3, *args, FAKE, FAKE, 8, 0,
-                   ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
+                   None, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_INVALID
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_BF16, *args, FAKE, FAKE, 8, 0,
-                   ctypes.c_float(float("nan")), FAKE, None, None) == B.VSA_ERR_INVALID
+                   None, ctypes.c_float(float("nan")), FAKE, None, None) == B.VSA_ERR_INVALID
     lay96 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=96).c()
     assert _status("vsa_block_sparse_attn_fwd", ctypes.byref(lay96), B.VSA_BF16, *args, None, None,
-                   0, 0, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
+                   0, 0, None, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
     lay27 = vsa.Layout(T=21, H=30, W=52, heads=2, head_dim=128, tile=(3, 3, 3)).c()
     assert _status("vsa_block_sparse_attn_fwd", ctypes.byref(lay27), B.VSA_BF16, *args, None, None,
-                   0, 0, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
+                   0, 0, None, ctypes.c_float(0.1), FAKE, None, None) == B.VSA_ERR_UNSUPPORTED
     # quantiser: null scales
     assert _status("vsa_quant_fp8_tiles", L, FAKE, FAKE, None, None) == B.VSA_ERR_INVALID
 
@@ -182,17 +182,17 @@ def test_natural_forward_argument_errors_before_launch():
     f = "vsa_block_sparse_attn_fwd_nat"
     q, k, v, o = (_fake(i) for i in range(4))
     # fp8 codes cannot be read in the natural order; null q; bad list_mode; NaN scale
-    assert _status(f, L, B.VSA_FP8_E4M3, q, k, v, None, None, 0, 0, ctypes.c_float(0.1), o, None,
+    assert _status(f, L, B.VSA_FP8_E4M3, q, k, v, None, None, 0, 0, None, ctypes.c_float(0.1), o, None,
                    None) == B.VSA_ERR_UNSUPPORTED
-    assert _status(f, L, B.VSA_BF16, None, k, v, None, None, 0, 0, ctypes.c_float(0.1), o, None,
+    assert _status(f, L, B.VSA_BF16, None, k, v, None, None, 0, 0, None, ctypes.c_float(0.1), o, None,
                    None) == B.VSA_ERR_INVALID
-    assert _status(f, L, B.VSA_BF16, q, k, v, _fake(8), _fake(9), 8, 3, ctypes.c_float(0.1), o, None,
+    assert _status(f, L, B.VSA_BF16, q, k, v, _fake(8), _fake(9), 8, 3, None, ctypes.c_float(0.1), o, None,
                    None) == B.VSA_ERR_INVALID
-    assert _status(f, L, B.VSA_BF16, q, k, v, None, None, 0, 0, ctypes.c_float(float("nan")), o, None,
+    assert _status(f, L, B.VSA_BF16, q, k, v, None, None, 0, 0, None, ctypes.c_float(float("nan")), o, None,
                    None) == B.VSA_ERR_INVALID
     # one batch of natural Q past 2 GiB (f32, 40 heads, d = 128, 120k tokens)
     big = vsa.Layout(T=30, H=64, W=64, heads=40, head_dim=128).c()
-    assert _status(f, ctypes.byref(big), B.VSA_F32, q, k, v, None, None, 0, 0, ctypes.c_float(0.1), o,
+    assert _status(f, ctypes.byref(big), B.VSA_F32, q, k, v, None, None, 0, 0, None, ctypes.c_float(0.1), o,
                    None, None) == B.VSA_ERR_UNSUPPORTED
 
 
@@ -229,7 +229,7 @@ def test_slice_over_2gib_rejected_before_launch():
     far = [ctypes.c_void_p((i + 1) << 33) for i in range(12)]    # 8 GiB apart: no overlaps
     q, k, v, o = far[:4]
     assert _status("vsa_block_sparse_attn_fwd", L, B.VSA_F32, q, k, v, None, None, None, None, None,
-                   0, 0, ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+                   0, 0, None, ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
     assert b"2 GiB" in B.lib().vsa_last_error()
     ws = B.lib().vsa_block_sparse_attn_bwd_workspace(L)
     assert _status("vsa_block_sparse_attn_bwd", L, B.VSA_F32, q, k, v, o, far[4], far[5], None, None,
@@ -269,9 +269,36 @@ def test_fused_natural_calls_argument_errors_before_launch():
     assert _status(f, ctypes.byref(big), x, c, s, None, 0, None) == B.VSA_ERR_UNSUPPORTED    # tile too big
     g = "vsa_block_sparse_attn_fwd_fp8_nat"
     q, k, v, o = _fake(5), _fake(6), _fake(7), _fake(8)
-    args = lambda dt, sc: (L, dt, q, k, v, sc, sc, sc, None, None, 0, 0, ctypes.c_float(0.1), o, None, None)
+    args = lambda dt, sc: (L, dt, q, k, v, sc, sc, sc, None, None, 0, 0, None, ctypes.c_float(0.1), o, None, None)
     assert _status(g, *args(B.VSA_BF16, s)) == B.VSA_ERR_UNSUPPORTED
     assert _status(g, *args(B.VSA_FP8_E4M3, None)) == B.VSA_ERR_INVALID
     lay64 = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=64).c()
     assert _status(g, ctypes.byref(lay64), B.VSA_FP8_E4M3, q, k, v, s, s, s, None, None, 0, 0,
-                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+                   None, ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+
+
+def test_work_order_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=45, W=80, heads=40, head_dim=128).c()
+    L = ctypes.byref(lay)
+    f = "vsa_build_work_order"
+    assert _status(f, L, None, _fake(1), None) == B.VSA_ERR_INVALID
+    assert _status(f, L, ctypes.c_void_p(0x400002), _fake(1), None) == B.VSA_ERR_INVALID   # misaligned
+    assert _status(f, L, _fake(1), _fake(1), None) == B.VSA_ERR_INVALID                    # overlap
+    big = vsa.Layout(T=64, H=128, W=128, heads=2, head_dim=128).c()                      # 16,384 tiles
+    assert _status(f, ctypes.byref(big), _fake(1), _fake(2), None) == B.VSA_ERR_UNSUPPORTED
+    # the attention takes an order only with per-head lists
+    q, k, v, o, wo = (_fake(i) for i in range(3, 8))
+    g = "vsa_block_sparse_attn_fwd"
+    assert _status(g, L, B.VSA_BF16, q, k, v, None, None, None, _fake(9), _fake(10), 8, 0, wo,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_INVALID
+    assert _status(g, L, B.VSA_BF16, q, k, v, None, None, None, None, None, 0, 1, wo,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_INVALID
+    assert _status(g, L, B.VSA_BF16, q, k, v, None, None, None, _fake(9), _fake(10), 8, 1,
+                   ctypes.c_void_p(0x400002), ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_INVALID
+    assert b"work_order" in B.lib().vsa_last_error()
+    n = "vsa_block_sparse_attn_fwd_nat"
+    assert _status(n, L, B.VSA_BF16, q, k, v, _fake(9), _fake(10), 8, 2, wo, ctypes.c_float(0.1), o,
+                   None, None) == B.VSA_ERR_INVALID
+    p = "vsa_block_sparse_attn_fwd_fp8_nat"
+    assert _status(p, L, B.VSA_FP8_E4M3, q, k, v, o, o, o, _fake(9), _fake(10), 8, 0, wo,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_INVALID

@@ -141,3 +141,11 @@ def test_fp8_natural_out_topp_720p():
     used = slot[None, None, None, :] < cnt[..., None]          # slots past a count are unspecified
     assert torch.equal(torch.where(used, idx2, 0), torch.where(used, idx, 0))
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    # the heavy-first dealing the bench uses changes nothing in the output
+    from tests.test_gpu_h_work_order import host_order
+    order = vsa.build_work_order(blay, cnt2)
+    out2, _ = vsa.block_sparse_attn_fwd_fp8_nat(blay, qc2, kc2, vc2, (qs2, ks2, vs2), idx2, cnt2, v_operand=True,
+                                                work_order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), host_order(cnt2.cpu().numpy(), cnt2.shape[-1]))
+    assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
