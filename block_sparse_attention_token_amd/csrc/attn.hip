@@ -176,22 +176,13 @@ __device__ int build_schedule(const DevLayout& L, const WaveWork& w, uint32_t* m
   return len;
 }
 
-// Bit (16*mb + r) set iff the kv token this lane holds in register r of S^T
-// block mb (token tok0 + 32*mb + 8*(r/4) + 4*half + r%4 of the tile) is a
-// real token, for a block known to hold padding.
+// Bit t set iff token tok0 + t (t < 32 * MB) of the tile is a real token,
+// for a block known to hold padding; the same value in every lane.
 template <int MB>
-__device__ __forceinline__ uint32_t kv_pad_bits(const DevLayout& L, int tile, int tok0, int lane,
-                                                int half) {
+__device__ __forceinline__ unsigned long long kv_pad_ballot(const DevLayout& L, int tile, int tok0,
+                                                            int lane) {
   const TileValid tv = tile_valid(L, tile);
-  const bool v = lane < 32 * MB && row_is_real(L, tv, tok0 + lane);
-  const unsigned long long vm = __ballot(v);
-  uint32_t m = 0;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      m |= (uint32_t)((vm >> (32 * mb + 8 * g + 4 * half)) & 0xFull) << (16 * mb + 4 * g);
-  return m;
+  return __ballot(lane < 32 * MB && row_is_real(L, tv, tok0 + lane));
 }
 
 // A window of 64 schedule entries held in two registers: lane i holds entry
@@ -361,16 +352,25 @@ __device__ __forceinline__ void bf_scores(const uint4* kb, const uint4 (&qf)[D /
     }
 }
 
-// Padded keys of a block (bit (16*mb + r) of `bits` clear) get score -inf,
+// Padded keys of a block (bit t of `real` clear for key t) get score -inf,
 // so the softmax below needs no mask: they add nothing to the maximum and
 // exp2 turns them into p = 0. The running maximum starts at -FLT_MAX rather
 // than -inf, so even a block whose keys are all padding yields p = 0, not NaN.
+// Register r of S^T block mb holds key 32*mb + 8*(r/4) + 4*half + r%4, so
+// the lane mask of each select comes straight from `real` (half-wave 0 tests
+// one bit, half-wave 1 the bit four above it): scalar bit extracts and one
+// vector select per register.
 template <int MB>
-__device__ __forceinline__ void mask_scores(f32x16_t (&s)[MB], uint32_t bits) {
+__device__ __forceinline__ void mask_scores(f32x16_t (&s)[MB], unsigned long long real) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[mb][r] = ((bits >> (16 * mb + r)) & 1u) ? s[mb][r] : -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * mb + 8 * (r >> 2) + (r & 3);
+      const unsigned long long lo = ((real >> j) & 1ull) ? 0xFFFFFFFFull : 0ull;
+      const unsigned long long hi = ((real >> (j + 4)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull;
+      s[mb][r] = __builtin_amdgcn_inverse_ballot_w64(lo | hi) ? s[mb][r] : -INFINITY;
+    }
 }
 
 // Row maximum of the raw scores (this lane's query row, both half-waves)
@@ -640,11 +640,11 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   };
   const int k_lane = l32 * IO::KS_ + half;
   const int v_lane = l32 * IO::VS_ + half;
-  // pad mask of block s: bit (16*mb + r) set for real keys, `full` when all are
-  auto block_bits = [&](int s, bool& full) -> uint32_t {
+  // pad mask of block s: bit t set for real key t, `full` when all are
+  auto block_bits = [&](int s, bool& full) -> unsigned long long {
     full = ((win.flags(s / SUB) >> (s % SUB)) & 1) == 0;
-    if (full) return 0xFFFFFFFFu;
-    return kv_pad_bits<MB>(L, win.tile(s / SUB), (s % SUB) * KVH, lane, half);
+    if (full) return ~0ull;
+    return kv_pad_ballot<MB>(L, win.tile(s / SUB), (s % SUB) * KVH, lane);
   };
   // running-max update from a block's row maximum and the (rare) rescale of O
   auto update_max = [&](float hi) __attribute__((always_inline)) {
@@ -713,7 +713,7 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
       io.load_v(rv, block_off(s + LV), tid);
       rescale_o();
       bool full;
-      const uint32_t bits = block_bits(s, full);
+      const unsigned long long bits = block_bits(s, full);
       if (!full) {
         mask_scores<MB>(scur, bits);
         hi = bf_row_max<MB>(scur);
@@ -779,7 +779,7 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
         f32x16_t sc[MB];
         bf_scores<KVH, D>(k_lds[P] + k_lane, qf, sc);
         bool full;
-        const uint32_t bits = block_bits(s, full);
+        const unsigned long long bits = block_bits(s, full);
         if (!full) mask_scores<MB>(sc, bits);
         update_max(bf_row_max<MB>(sc));
         bf_block_pv<KVH, D>(v_lds[P] + v_lane, sc, sl2, m_run, l_run, oacc);
@@ -1142,13 +1142,9 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
     l_run = fmaf(MSUM ? f8_rowsum(rsel, pk) : psum, rd(ips_v, s), l_run);
     return pk;
   };
-  // pad mask of block s applied to its scores; returns their row maximum
-  auto mask_max = [&](int s, f32x16_t (&sc)[MB], float hi) __attribute__((always_inline)) {
-    if ((win.flags(s) & 1) != 0) {
-      mask_scores<MB>(sc, kv_pad_bits<MB>(L, win.tile(s), 0, lane, half));
-      hi = bf_row_max<MB>(sc);
-    }
-    return hi;
+  // pad mask of block s (s < steps) applied to its scores
+  auto mask_block = [&](int s, f32x16_t (&sc)[MB]) __attribute__((always_inline)) {
+    if ((win.flags(s) & 1) != 0) mask_scores<MB>(sc, kv_pad_ballot<MB>(L, win.tile(s), 0, lane));
   };
 
   if (shared) {
@@ -1177,6 +1173,7 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
       }
       __syncthreads();
       f8_scores(k_buf(0) + k_lane, qf, s_a);
+      mask_block(0, s_a);
       hi = bf_row_max<MB>(s_a);
       __syncthreads();                   // K buffer 0 is refilled during step 0
     }
@@ -1191,10 +1188,10 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
         io.load_k(rk, tile_off(s + 2), tid);
         io.load_v(rv, tile_off(s + 1), tid);
       }
-      hi = mask_max(s, scur, hi);
       f8_scores(k_buf(P ^ 1) + k_lane, qf, snext);
       const i32x8_t pk = softmax(s, scur, hi);
       f8_pv(v_buf(P) + v_lane, pk, oacc);
+      if (s + 1 < steps) mask_block(s + 1, snext);   // masked before its maximum is taken
       hi = bf_row_max<MB>(snext);
       interleave_hint<8, 2, 8>();
       __builtin_amdgcn_sched_barrier(0);  // the staging stores (copies) wait for their loads here
@@ -1230,7 +1227,8 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
       if ((win.flags(s) >> (8 + ww.slot)) & 1) {
         f32x16_t sc[MB];
         f8_scores(k_buf(P) + k_lane, qf, sc);
-        const float hi = mask_max(s, sc, bf_row_max<MB>(sc));
+        mask_block(s, sc);
+        const float hi = bf_row_max<MB>(sc);
         const i32x8_t pk = softmax(s, sc, hi);
         f8_pv(v_buf(P) + v_lane, pk, oacc);
       }
