@@ -110,15 +110,20 @@ __device__ __forceinline__ uint32_t float_order(float f) {
 
 // Coarse scores and selection fused, one workgroup per (b, head, R query
 // tiles): the R rows of scores stay in LDS (R * n_tiles floats), so no
-// n_tiles^2 buffer exists. Scores first (all 256 threads), then each wave
+// n_tiles^2 buffer exists. Scores first (all waves), then each wave
 // selects for its rows from LDS on its own, with no barrier.
 //
 // Scores: s_ij = coarse_scale * <qbar_i, kbar_j> on the fp32 matrix core
 // (v_mfma_f32_16x16x4_f32, products of 16 query tiles x 16 key tiles, 4
 // channels per step, fp32 accumulation in a fixed order), -inf for key tiles
-// without real tokens. Each lane holds its qbar operands for the whole row
-// block in registers and loads its kbar operands straight from memory, one
-// block of 16 key tiles ahead; the 8 waves take the key blocks in turn.
+// without real tokens. The channel that lane group g of step t contracts is
+// chosen so that each lane's operands for four consecutive steps are four
+// consecutive channels: the kbar operands then come straight from memory as
+// one 16-byte load per lane and four steps, with no staging through LDS, and
+// the qbar operands of the same channels stay in registers for the whole
+// row block. The waves take the key blocks in turn, loading each block two
+// blocks before it is multiplied. The key tiles' real-token flags are taken
+// once per workgroup, not per row.
 //
 // Selection of row i among the real key tiles, by (score desc, index asc):
 // lane l holds tiles l, l + 64, ...; each tile's 32-bit order key (larger
@@ -130,12 +135,13 @@ __device__ __forceinline__ uint32_t float_order(float f) {
 //           mass of a key set is a fixed-order sum (per lane in increasing j,
 //           then a butterfly over the lanes); then the count is raised to
 //           k_floor (capped at #real) by a count search as for top-k.
-// Tiles with key > T are kept; among tiles with key == T (equal scores) the
-// lower indices are kept first, as many as the count (or the mass) needs.
+// Once at most 64 tiles remain between the decided bits (checked every
+// fourth bit) they are gathered one per lane and the remaining bits test one
+// value per lane; a mass is then the gathered tiles' fixed-order sum added to
+// the mass of the tiles above them. Tiles with key > T are kept; among tiles with key == T
+// (equal scores) the lower indices are kept first, as many as the count (or
+// the mass) needs.
 // The kept tiles are written in ascending order through ballots.
-constexpr int kRouteThreads = 512;        // 8 waves
-constexpr int kRouteMaxK = 64;            // channel groups of 4 (head_dim <= 256)
-constexpr int kRouteRow = 132;            // LDS floats per staged kbar row (128 channels + 4 pad)
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // Wave-wide sum / max, the same value in every lane and the same order on
@@ -166,8 +172,8 @@ __device__ __forceinline__ float wave_sum(float x) { return wave_reduce<0>(x); }
 __device__ __forceinline__ float wave_max(float x) { return wave_reduce<1>(x); }
 __device__ __forceinline__ float wave_min(float x) { return wave_reduce<2>(x); }
 
-template <int R, int MT, int KG>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const float* __restrict__ q_pooled,
+template <int R, int MT, int NCH, int THREADS>
+__global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float* __restrict__ q_pooled,
                                                               const float* __restrict__ k_pooled,
                                                               float coarse_scale, int top_k, float top_p,
                                                               int k_floor, int max_kv,
@@ -175,8 +181,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
                                                               int32_t* __restrict__ kv_cnt,
                                                               float* __restrict__ scores) {
   static_assert(R == 4 || R == 8 || R == 16, "4, 8 or 16 query tiles per workgroup");
-  extern __shared__ float sc[];                     // [R][n] scores of this workgroup's rows, then
-                                                    // each wave's [16][kRouteRow] kbar staging
+  extern __shared__ float sc[];                     // [R][n] scores of this workgroup's rows
   const int n = L.n_tiles, d = L.d;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -186,71 +191,96 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
   const float* qb = q_pooled + bh * n * d;
   const float* kb = k_pooled + bh * n * d;
 
-  // A operand (16 x 4 per step): lane l holds qbar[i0 + l % 16][4 ks + l / 16]
-  // (zero past the block's rows); B operand: kbar[j0 + l % 16][4 ks + l / 16],
-  // read from the wave's own LDS copy of the block's 16 rows of kbar, which
-  // the wave fills 128 channels at a time with coalesced 16-byte loads (the
-  // next chunk's loads are in flight while the current one is used).
+  // Step t (0..31) of channel chunk cq: lane l (m16 = l % 16, g = l / 16)
+  // contracts channel 128 cq + 16 (t / 4) + 4 g + t % 4 of query tile
+  // i0 + m16 (A operand) and of key tile j0 + m16 (B operand); channels past
+  // d are zero on both sides.
+  constexpr int NW = THREADS / 64;
   const int m16 = lane & 15, k4 = lane >> 4;
-  float qa[KG];
+  float qa[NCH][32];
 #pragma unroll
-  for (int ks = 0; ks < KG; ++ks)
-    qa[ks] = (m16 < rows && 4 * ks < d) ? qb[(long long)(i0 + m16) * d + 4 * ks + k4] : 0.0f;
-  float* kS = sc + R * n + wave * (16 * kRouteRow);      // this wave's [16][kRouteRow] floats
-  const int nblk = (n + 15) / 16;
-  const int nch = (d + 127) / 128;                          // 128-channel chunks per row
-  constexpr int NW = kRouteThreads / 64;
-  float4 kr[8];
-  // chunk q of this wave's work: block wave + NW * (q / nch), channels 128 * (q % nch) ..
-  auto load_chunk = [&](int q) {
-    const int blk = wave + NW * (q / nch), c0 = 128 * (q % nch);
+  for (int cq = 0; cq < NCH; ++cq)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = 64 * u + lane, jj = c >> 5, e = c0 + 4 * (c & 31);
-      const int j = min(16 * blk + jj, n - 1);
-      kr[u] = e < d ? *reinterpret_cast<const float4*>(kb + (long long)j * d + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int e = 128 * cq + 16 * u + 4 * k4;
+      const float4 v = (m16 < rows && e < d) ? *reinterpret_cast<const float4*>(qb + (long long)(i0 + m16) * d + e)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      qa[cq][4 * u + 0] = v.x;
+      qa[cq][4 * u + 1] = v.y;
+      qa[cq][4 * u + 2] = v.z;
+      qa[cq][4 * u + 3] = v.w;
+    }
+  const int nblk = (n + 15) / 16;
+  auto load_blk = [&](int blk, float4 (&kr)[NCH][8]) {
+    const int j = min(16 * blk + m16, n - 1);
+#pragma unroll
+    for (int cq = 0; cq < NCH; ++cq)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 128 * cq + 16 * u + 4 * k4;
+        kr[cq][u] = e < d ? *reinterpret_cast<const float4*>(kb + (long long)j * d + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  };
+  auto score_blk = [&](int blk, const float4 (&kr)[NCH][8]) {
+    f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cq = 0; cq < NCH; ++cq)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (128 * cq + 16 * u >= d) continue;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 0], kr[cq][u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 1], kr[cq][u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 2], kr[cq][u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 3], kr[cq][u].w, acc, 0, 0, 0);
+      }
+    // lane l holds rows 4 (l / 16) .. +3 of key tile 16 blk + l % 16
+    const int j = 16 * blk + m16;
+    if (j < n) {
+      const bool real = real_rows(L, tile_valid(L, j)) > 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * k4 + t;
+        if (r >= rows) continue;
+        const float v = real ? coarse_scale * acc[t] : -INFINITY;
+        sc[r * n + j] = v;
+        if (scores) scores[(bh * n + i0 + r) * n + j] = v;
+      }
     }
   };
-  const int my_blocks = wave < nblk ? (nblk - wave + NW - 1) / NW : 0;
-  const int nq = my_blocks * nch;
-  if (nq > 0) load_chunk(0);
-  f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int q = 0; q < nq; ++q) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = 64 * u + lane;
-      *reinterpret_cast<float4*>(kS + (c >> 5) * kRouteRow + 4 * (c & 31)) = kr[u];
-    }
-    if (q + 1 < nq) load_chunk(q + 1);
-    const int cq = q % nch;
-    if (cq == 0) acc = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-      const int ks = 32 * cq + kk;
-      if (ks < KG && 4 * ks < d)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[ks], kS[m16 * kRouteRow + 4 * kk + k4], acc, 0, 0, 0);
-    }
-    if (cq == nch - 1) {
-      // lane l holds rows 4 (l / 16) .. +3 of key tile 16 blk + l % 16
-      const int blk = wave + NW * (q / nch);
-      const int j = 16 * blk + m16;
-      if (j < n) {
-        const bool real = real_rows(L, tile_valid(L, j)) > 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * k4 + t;
-          if (r >= rows) continue;
-          const float v = real ? coarse_scale * acc[t] : -INFINITY;
-          sc[r * n + j] = v;
-          if (scores) scores[(bh * n + i0 + r) * n + j] = v;
-        }
-      }
+  {
+    // three block buffers: the loads of a block are issued two blocks ahead
+    float4 ka[NCH][8], kc[NCH][8], ke[NCH][8];
+    int blk = wave;
+    if (blk < nblk) load_blk(blk, ka);
+    if (blk + NW < nblk) load_blk(blk + NW, kc);
+    while (blk < nblk) {
+      if (blk + 2 * NW < nblk) load_blk(blk + 2 * NW, ke);
+      score_blk(blk, ka);
+      blk += NW;
+      if (blk >= nblk) break;
+      if (blk + 2 * NW < nblk) load_blk(blk + 2 * NW, ka);
+      score_blk(blk, kc);
+      blk += NW;
+      if (blk >= nblk) break;
+      if (blk + 2 * NW < nblk) load_blk(blk + 2 * NW, kc);
+      score_blk(blk, ke);
+      blk += NW;
     }
   }
   __syncthreads();
 
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = wave; r < rows; r += kRouteThreads / 64) {
+  // which of this lane's key tiles hold real tokens (the same for every row)
+  unsigned long long vbits = 0ull;
+  int n_valid = 0;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int j = lane + 64 * m;
+    const bool valid = j < n && real_rows(L, tile_valid(L, j)) > 0;
+    vbits |= (unsigned long long)valid << m;
+    n_valid += __popcll(__ballot(valid));
+  }
+  for (int r = wave; r < rows; r += THREADS / 64) {
     const int i = i0 + r;
     int32_t* out_idx = kv_idx + (bh * n + i) * max_kv;
     if (real_rows(L, tile_valid(L, i)) == 0) {    // query tile without real tokens
@@ -259,15 +289,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
     }
     uint32_t key[MT];
     float sv[MT];
-    int n_valid = 0;
     float smax = -INFINITY, smin = INFINITY;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int j = lane + 64 * m;
-      const bool valid = j < n && real_rows(L, tile_valid(L, j)) > 0;
-      sv[m] = valid ? sc[r * n + j] : -INFINITY;
+      const bool valid = (vbits >> m) & 1ull;
+      sv[m] = valid ? sc[r * n + lane + 64 * m] : -INFINITY;
       key[m] = valid ? float_order(sv[m]) : 0u;
-      n_valid += __popcll(__ballot(valid));
       smax = fmaxf(smax, sv[m]);
       smin = valid ? fminf(smin, sv[m]) : smin;
     }
@@ -278,28 +305,72 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
       continue;
     }
     // counts of real tiles with key >= t / key > t, and the threshold search by counts
-    auto count_ge = [&](uint32_t t) {
+    auto count_ge = [&](uint32_t t) __attribute__((always_inline)) {
       int c = 0;
 #pragma unroll
       for (int m = 0; m < MT; ++m) c += __popcll(__ballot(key[m] >= t && key[m] != 0u));
       return c;
     };
-    auto count_gt = [&](uint32_t t) { return t == 0xFFFFFFFFu ? 0 : count_ge(t + 1u); };
+    auto count_gt = [&](uint32_t t) __attribute__((always_inline)) { return t == 0xFFFFFFFFu ? 0 : count_ge(t + 1u); };
     // Every threshold searched for lies in [key of smin, key of smax], so it
     // shares their common leading bits; the search runs over the bits below.
     const uint32_t kmax = float_order(smax), kmin = float_order(smin);
     const int hb = (kmin ^ kmax) ? 31 - __builtin_clz(kmin ^ kmax) : -1;
     const uint32_t T0 = hb < 0 ? kmax : hb == 31 ? 0u : kmax & ~((2u << hb) - 1u);
-    auto search = [&](auto pred) {              // largest T in range with pred(T)
+    // The largest T in that range with weight(key >= T) >= goal, bit by bit
+    // from the top (weight: the tiles' masses, or 1 each for counts). Once
+    // at most 64 tiles are left whose keys share T's decided leading bits
+    // (checked every fourth bit), they are gathered one per lane through this
+    // row's LDS slots, whose scores are already in registers; the tiles
+    // above that range add their weight once, and the remaining bits test
+    // one value per lane.
+    uint32_t* gk = reinterpret_cast<uint32_t*>(sc + r * n);   // gathered keys (64), then weights (64)
+    float* gw = sc + r * n + 64;
+    auto search = [&](auto weight_ge, auto weight_of, float goal) __attribute__((always_inline)) {
       uint32_t T = T0;
-      for (int bit = hb; bit >= 0; --bit) {
+      int bit = hb;
+      for (; bit >= 0; --bit) {
+        if (MT > 4 && ((hb - bit) & 3) == 0) {
+          const uint32_t pre = bit == 31 ? 0u : ~((2u << bit) - 1u);
+          int left = 0;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) left += __popcll(__ballot(key[m] != 0u && (key[m] & pre) == (T & pre)));
+          if (left <= 64) break;
+        }
         const uint32_t cand = T | (1u << bit);
-        if (pred(cand)) T = cand;
+        if (weight_ge(cand) >= goal) T = cand;
       }
+      if (bit < 0) return T;
+      const uint32_t pre = bit == 31 ? 0u : ~((2u << bit) - 1u);
+      float above = 0.0f;
+      int base = 0;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bool in = key[m] != 0u && (key[m] & pre) == (T & pre);
+        above += (key[m] != 0u && (key[m] & pre) > (T & pre)) ? weight_of(m) : 0.0f;
+        const unsigned long long msk = __ballot(in);
+        if (in) {
+          const int p = base + __popcll(msk & below);
+          gk[p] = key[m];
+          gw[p] = weight_of(m);
+        }
+        base += __popcll(msk);
+      }
+      const float A = wave_sum(above);
+      __builtin_amdgcn_wave_barrier();
+      const bool have = lane < base;
+      const uint32_t ck = have ? gk[lane] : 0u;
+      const float cw = have ? gw[lane] : 0.0f;
+      for (; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        if (A + wave_sum(have && ck >= cand ? cw : 0.0f) >= goal) T = cand;
+      }
+      __builtin_amdgcn_wave_barrier();
       return T;
     };
-    auto search_count = [&](int want) {         // largest T with #(key >= T) >= want (want >= 1)
-      return search([&](uint32_t t) { return count_ge(t) >= want; });
+    auto search_count = [&](int want) __attribute__((always_inline)) {   // largest T with #(key >= T) >= want (want >= 1)
+      return search([&](uint32_t t) __attribute__((always_inline)) { return (float)count_ge(t); },
+                    [&](int) __attribute__((always_inline)) { return 1.0f; }, (float)want);
     };
     int count;
     uint32_t T;
@@ -313,13 +384,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
         zl += ev[m];
       }
       const float target = top_p * wave_sum(zl);
-      auto mass_ge = [&](uint32_t t) {
+      auto mass_ge = [&](uint32_t t) __attribute__((always_inline)) {
         float ms = 0.0f;
 #pragma unroll
         for (int m = 0; m < MT; ++m) ms += key[m] >= t ? ev[m] : 0.0f;
         return wave_sum(ms);
       };
-      T = search([&](uint32_t t) { return mass_ge(t) >= target; });
+      T = search(mass_ge, [&](int m) __attribute__((always_inline)) { return ev[m]; }, target);
       // the crossing key T: keys above it, then tied tiles in index order until the mass is reached
       const int above = count_gt(T);
       const int tied = count_ge(T) - above;
@@ -365,35 +436,41 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(DevLayout L, const
 }
 
 // R query tiles per workgroup (scores of the rows in LDS: R * n * 4 bytes),
-// MT key tiles per lane in the selection, KG channel groups of 4.
-template <int R, int MT>
+// MT key tiles per lane in the selection, NCH chunks of 128 channels.
+template <int R, int MT, int NCH, int THREADS>
 static hipError_t launch_route_rm(const DevLayout& L, const float* qp, const float* kp, float coarse_scale,
                                   int top_k, float top_p, int k_floor, int max_kv, int32_t* kv_idx,
                                   int32_t* kv_cnt, float* scores, hipStream_t s) {
-  const size_t lds = ((size_t)R * L.n_tiles + (kRouteThreads / 64) * 16 * kRouteRow) * sizeof(float);
+  const size_t lds = (size_t)R * L.n_tiles * sizeof(float);
   dim3 grid((L.n_tiles + R - 1) / R, L.heads, L.B);
-  if (L.d <= 128)
-    hipLaunchKernelGGL((route_kernel<R, MT, 32>), grid, dim3(kRouteThreads), lds, s, L, qp, kp,
-                       coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
-  else
-    hipLaunchKernelGGL((route_kernel<R, MT, kRouteMaxK>), grid, dim3(kRouteThreads), lds, s, L, qp, kp,
-                       coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
+  hipLaunchKernelGGL((route_kernel<R, MT, NCH, THREADS>), grid, dim3(THREADS), lds, s, L, qp, kp, coarse_scale,
+                     top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
   return hipGetLastError();
+}
+
+// Rows per workgroup and key tiles per lane by n_tiles (LDS: R * n * 4 <= 160 KB);
+// sixteen waves where the registers allow (head_dim <= 128, up to 1,536 tiles), else eight.
+template <int NCH, int TH>
+static hipError_t route_by_n(const DevLayout& L, const float* qp, const float* kp, float coarse_scale,
+                             int top_k, float top_p, int k_floor, int max_kv, int32_t* kv_idx,
+                             int32_t* kv_cnt, float* scores, hipStream_t s) {
+  const int n = L.n_tiles;
+  if (n <= 256)
+    return launch_route_rm<16, 4, NCH, TH>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
+  if (n <= 1536)
+    return launch_route_rm<16, 24, NCH, TH>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
+  if (n <= 2560)
+    return launch_route_rm<16, 48, NCH, 512>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
+  return launch_route_rm<8, 64, NCH, 512>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
 }
 
 static hipError_t route_from_pooled(const DevLayout& L, const float* qp, const float* kp,
                                     float coarse_scale, int top_k, float top_p, int k_floor,
                                     int max_kv, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
                                     hipStream_t s) {
-  const int n = L.n_tiles;
-  if (n <= 256)
-    return launch_route_rm<16, 4>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
-  // LDS: R * n * 4 bytes of scores + 8 waves x 16 rows x 132 floats of staging (66 KB) <= 160 KB
-  if (n <= 1504)
-    return launch_route_rm<16, 24>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
-  if (n <= 3008)
-    return launch_route_rm<8, 48>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
-  return launch_route_rm<4, 64>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
+  if (L.d <= 128)
+    return route_by_n<1, 512>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
+  return route_by_n<2, 512>(L, qp, kp, coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores, s);
 }
 
 }  // namespace
