@@ -162,7 +162,7 @@ vsa_status vsa_build_mask_window_grouped(const vsa_layout* layout, int32_t gt, i
  * Steps, per (b, head):
  *   pooled tile means over real (non-pad) tokens, in fp32;
  *   s_ij = coarse_scale * <qbar_i, kbar_j> (fp32, the products accumulated
- *   in increasing channel order);
+ *   in a fixed channel order, the same on every call);
  *   top_p <= 0: keep the top_k highest-scoring key tiles (ties: lower index);
  *   top_p  > 0: p_ij = softmax_j(s_ij); keep the shortest prefix of the
  *               descending order whose mass reaches top_p, then at least
