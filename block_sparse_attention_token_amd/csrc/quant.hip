@@ -4,8 +4,10 @@
 // Per (batch, head, tile): a = absmax over real rows and all channels,
 // scale = fl32(a / 448), code = RNE_e4m3(fl32(x * fl32(448 / a))) saturating
 // at +-448, sign taken from the fp32 sign bit. Every step is a correctly
-// rounded fp32 operation or exact integer work, so codes are reproducible
-// bit for bit.
+// rounded fp32 operation, a round-to-nearest-even conversion or exact
+// integer work, so codes are reproducible bit for bit.
+#include <float.h>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -35,6 +37,32 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
     code = (uint32_t)m;                             // 0..8 (8 is the smallest normal)
   }
   return code | sign;
+}
+
+// Codes of the 8 bf16 values in ws (4 dwords, low half first) times inv,
+// byte i of the result = value i. With a finite, non-zero tile absmax every
+// |value * inv| is at most 448 (1 + 2^-23), inside the e4m3 range, and the
+// matrix core's conversion (v_cvt_pk_fp8_f32, round to nearest even, sign
+// kept) gives the same codes as e4m3_rne at one instruction per pair; a tile
+// with an infinite or NaN absmax takes e4m3_rne for its saturation and NaN
+// codes.
+__device__ __forceinline__ uint2 encode8(const uint32_t (&ws)[4], float inv, bool hw) {
+  if (hw) {
+    int w0 = 0, w1 = 0;
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(bf16_lo(ws[0]), inv), __fmul_rn(bf16_hi(ws[0]), inv), w0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(bf16_lo(ws[1]), inv), __fmul_rn(bf16_hi(ws[1]), inv), w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(bf16_lo(ws[2]), inv), __fmul_rn(bf16_hi(ws[2]), inv), w1, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(bf16_lo(ws[3]), inv), __fmul_rn(bf16_hi(ws[3]), inv), w1, true);
+    return make_uint2((uint32_t)w0, (uint32_t)w1);
+  }
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
+    const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
+    packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
+  }
+  return make_uint2(packed[0], packed[1]);
 }
 
 // VOP: 64-token tiles of d = 128 only. The tile's codes are gathered in LDS
@@ -94,14 +122,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
     if (a != 0.0f && row_is_real(L, tv, r)) {
       const uint4 w = x[off];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
-        const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
-        packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
-      }
-      out = make_uint2(packed[0], packed[1]);
+      out = encode8(ws, inv, a <= FLT_MAX);
     }
     if constexpr (VOP) tl[idx] = out;
     else codes[off] = out;
@@ -192,14 +213,7 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
     uint2 out = make_uint2(0u, 0u);
     if (a != 0.0f) {
       const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
-      uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t c0 = e4m3_rne(__fmul_rn(bf16_lo(ws[e]), inv));
-        const uint32_t c1 = e4m3_rne(__fmul_rn(bf16_hi(ws[e]), inv));
-        packed[e >> 1] |= (c0 | (c1 << 8)) << ((e & 1) * 16);
-      }
-      out = make_uint2(packed[0], packed[1]);
+      out = encode8(ws, inv, a <= FLT_MAX);
     }
     if constexpr (VOP) tl[r * chunks + ch] = out;
     else codes[(row0 + r) * chunks + ch] = out;
