@@ -173,3 +173,34 @@ def unpermute(x_tiled: np.ndarray, lay: Layout) -> np.ndarray:
     real = order >= 0
     out[:, order[real], :, :] = np.transpose(x_tiled[:, :, real, :], (0, 2, 1, 3))
     return out
+
+
+def v_operand_order_bf16() -> np.ndarray:
+    """Token of a 32-token block held at each position p (0..31) of the bf16
+    P.V operand.
+
+    Layout reading (the pages are silent on layouts; the P.V product of the
+    flash-style forward takes V transposed): in each 16-position group ps,
+    position 16 ps + 8 h + i holds token 16 ps + 8 (i div 4) + 4 h + (i mod 4),
+    with h in 0..1 and i in 0..7.
+    """
+    tok = np.empty(32, dtype=np.int64)
+    for ps in range(2):
+        for h in range(2):
+            for i in range(8):
+                tok[16 * ps + 8 * h + i] = 16 * ps + 8 * (i // 4) + 4 * h + (i % 4)
+    return tok
+
+
+def v_operand_layout_bf16(x_tiled: np.ndarray, lay: Layout) -> np.ndarray:
+    """A tiled tensor [B, heads, N_pad, d] of 64-token tiles stored, per tile,
+    as two 32-token blocks each channel-major in the bf16 P.V operand order:
+    element (block k, channel c, position p) of tile j sits at
+    ((2 j + k) * d + c) * 32 + p of its (b, head) slice and holds channel c of
+    token 32 k + v_operand_order_bf16()[p] of the tile.
+    """
+    assert lay.tile_tokens == 64
+    B, d = x_tiled.shape[0], lay.head_dim
+    x = np.asarray(x_tiled).reshape(B, lay.heads, lay.n_tiles, 2, 32, d)
+    x = np.swapaxes(x[:, :, :, :, v_operand_order_bf16(), :], -1, -2)   # [.., block, channel, position]
+    return np.ascontiguousarray(x).reshape(B, lay.heads, lay.n_padded, d)

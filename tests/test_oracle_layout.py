@@ -97,3 +97,36 @@ def test_permute_unpermute_identity_and_zero_pads(name):
     # spot check the gather direction on a few positions
     for p in np.nonzero(order >= 0)[0][:50]:
         assert np.array_equal(xt[1, 0, p], x[1, order[p], 0])
+
+
+def test_bf16_v_operand_order_golden_and_bijection():
+    tok = L.v_operand_order_bf16()
+    for line in read_golden("bf16_v_operand_order.txt"):
+        p, t = (int(x) for x in line.split(":"))
+        assert tok[p] == t
+    assert sorted(tok.tolist()) == list(range(32))
+    # each half-wave's 8 positions of a group are two runs of 4 consecutive tokens
+    for ps in range(2):
+        for h in range(2):
+            run = tok[16 * ps + 8 * h: 16 * ps + 8 * h + 8]
+            assert list(run[:4]) == list(range(run[0], run[0] + 4))
+            assert list(run[4:]) == list(range(run[4], run[4] + 4))
+            assert run[4] - run[0] == 8
+
+
+def test_bf16_v_operand_layout_places_every_element():
+    lay = L.Layout(T=5, H=9, W=13, heads=2, head_dim=16, tile=(4, 4, 4))
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, lay.heads, lay.n_padded, lay.head_dim))
+    y = L.v_operand_layout_bf16(x, lay)
+    assert y.shape == x.shape
+    tok = L.v_operand_order_bf16()
+    yy = y.reshape(2, lay.heads, lay.n_tiles, 2, lay.head_dim, 32)
+    for (b, h, j, k, c, p) in [(0, 0, 0, 0, 0, 0), (1, 1, lay.n_tiles - 1, 1, 15, 31), (0, 1, 3, 1, 7, 9),
+                               (1, 0, 5, 0, 12, 22)]:
+        assert yy[b, h, j, k, c, p] == x[b, h, 64 * j + 32 * k + tok[p], c]
+    # the layout is a permutation of each tile's elements
+    for j in range(lay.n_tiles):
+        a = np.sort(x[:, :, 64 * j: 64 * (j + 1)].reshape(2, lay.heads, -1), axis=-1)
+        bb = np.sort(y[:, :, 64 * j: 64 * (j + 1)].reshape(2, lay.heads, -1), axis=-1)
+        assert np.array_equal(a, bb)
