@@ -121,6 +121,12 @@ def build_workload(name, torch, np, vsa):
     log(f"{name}: inputs ready in {time.time() - t0:.1f}s")
     C, d, n = info.tile_tokens, cfg.head_dim, info.n_tiles
     state = {"cfg": cfg, "lay": lay, "info": info}
+    # bf16 layers over 64-token tiles store V in the P.V operand order, which the
+    # attention kernel stages with whole 16-byte copies (same output bits)
+    vop = cfg.dtype == "bf16" and C == 64
+
+    def permute_v(x):
+        return vsa.tile_permute_v(lay, x) if vop else vsa.tile_permute(lay, x)
 
     if cfg.mask in ("window", "skiparse"):
         radius = cfg.window if cfg.mask == "window" else (0, 0, 0)
@@ -133,15 +139,18 @@ def build_workload(name, torch, np, vsa):
         if cfg.mask in ("window", "skiparse"):
             # fixed lists: Q is read and O written in the natural order by the
             # attention kernel itself; only K and V are permuted
-            tk, tv = (timer.run("permute", lambda x=x: vsa.tile_permute(lay, x)) for x in nat[1:])
+            tk = timer.run("permute", lambda: vsa.tile_permute(lay, nat[1]))
+            tv = timer.run("permute_v" if vop else "permute", lambda: permute_v(nat[2]))
             if dense:
-                timer.run("attn_dense", lambda: vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv))
+                timer.run("attn_dense", lambda: vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv,
+                                                                              v_operand=vop))
             else:
                 # 3D windows differ between neighbouring query tiles: each tile walks its
                 # own list (list_mode 2); Skiparse tiles of a group share one list and
                 # walk it four at a time
                 timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(
-                    lay, nat[0], tk, tv, kv_idx, kv_cnt, per_tile_walk=cfg.mask == "window"))
+                    lay, nat[0], tk, tv, kv_idx, kv_cnt, per_tile_walk=cfg.mask == "window",
+                    v_operand=vop))
             return
         if cfg.mask == "topk":
             # routed bf16 layer: the tile means of Q come from a pass that writes no
@@ -150,11 +159,12 @@ def build_workload(name, torch, np, vsa):
             # natural order by the attention kernel
             _, qp = timer.run("pool", lambda: vsa.tile_permute_pool(lay, nat[0], means_only=True))
             tk, kp = timer.run("permute_pool", lambda: vsa.tile_permute_pool(lay, nat[1]))
-            tv = timer.run("permute", lambda: vsa.tile_permute(lay, nat[2]))
+            tv = timer.run("permute_v" if vop else "permute", lambda: permute_v(nat[2]))
             idx, cnt, _ = timer.run("route", lambda: vsa.build_mask_topk_pooled(
                 lay, qp, kp, top_k=cfg.top_k))
             state["cnt"] = cnt
-            timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv, idx, cnt))
+            timer.run("attn", lambda: vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv, idx, cnt,
+                                                                    v_operand=vop))
         else:
             # fp8 top-p layer: each tensor goes from the natural order to tiled e4m3
             # codes in one pass (Q and K with the routing's tile means, V in the P.V
@@ -206,7 +216,7 @@ def build_workload(name, torch, np, vsa):
         (evicts the 256 MB MALL and the L2s); returns the mean launch time in ms."""
         if cfg.mask not in ("window", "skiparse"):
             return None
-        tk, tv = (vsa.tile_permute(lay, x) for x in nat[1:])
+        tk, tv = vsa.tile_permute(lay, nat[1]), permute_v(nat[2])
         scratch = torch.empty(scratch_mb << 20, dtype=torch.uint8, device="cuda")
         total = 0.0
         for i in range(reps):
@@ -214,7 +224,7 @@ def build_workload(name, torch, np, vsa):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             vsa.block_sparse_attn_fwd_nat(lay, nat[0], tk, tv, kv_idx, kv_cnt,
-                                          per_tile_walk=cfg.mask == "window")
+                                          per_tile_walk=cfg.mask == "window", v_operand=vop)
             e1.record()
             torch.cuda.synchronize()
             total += e0.elapsed_time(e1)
@@ -229,7 +239,7 @@ def build_workload(name, torch, np, vsa):
         row = cfg.heads * d
         nat_b, til_b = info.n_tokens * row * es, info.n_padded * row * es
         means = n * row * 4
-        out = {"permute": nat_b + til_b, "unpermute": nat_b + til_b,
+        out = {"permute": nat_b + til_b, "permute_v": nat_b + til_b, "unpermute": nat_b + til_b,
                "permute_pool": nat_b + til_b + means, "pool": nat_b + means}
         if cfg.fp8:
             codes, scales = info.n_padded * row, n * cfg.heads * 4

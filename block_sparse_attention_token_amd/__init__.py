@@ -20,17 +20,18 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import (EXPORTED, VSA_BF16, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP, VSA_SKIPARSE2D,
-                   VSA_TILE3D, VsaError, VsaLayout, VsaLayoutInfo, check, lib)
+from ._lib import (EXPORTED, VSA_BF16, VSA_BF16_VOP, VSA_F32, VSA_FP8_E4M3, VSA_FP8_E4M3_VOP,
+                   VSA_SKIPARSE2D, VSA_TILE3D, VsaError, VsaLayout, VsaLayoutInfo, check, lib)
 
 __all__ = [
-    "Layout", "layout_info", "tile_permute", "tile_permute_pool", "build_mask_window",
+    "Layout", "layout_info", "tile_permute", "tile_permute_v", "tile_permute_pool", "build_mask_window",
     "build_mask_topk", "build_mask_topk_pooled",
     "quant_fp8_tiles", "quant_fp8_tiles_nat", "block_sparse_attn_fwd", "block_sparse_attn_fwd_nat",
     "block_sparse_attn_fwd_fp8_nat", "build_mask_window_grouped",
     "quant_fp8_tiles_grouped", "build_transposed_lists", "bwd_workspace_bytes",
     "block_sparse_attn_bwd", "block_sparse_attn_bwd_noalloc", "VsaError", "EXPORTED",
-    "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_TILE3D", "VSA_SKIPARSE2D",
+    "VSA_F32", "VSA_BF16", "VSA_FP8_E4M3", "VSA_FP8_E4M3_VOP", "VSA_BF16_VOP", "VSA_TILE3D",
+    "VSA_SKIPARSE2D",
 ]
 
 
@@ -140,6 +141,22 @@ def tile_permute(lay: Layout, src: torch.Tensor, inverse: bool = False,
     c = lay.c()
     check(lib().vsa_tile_permute(ctypes.byref(c), _DT.get(src.dtype, -1), _ptr(src), _ptr(out),
                                  1 if inverse else 0, _stream(stream)))
+    return out
+
+
+def tile_permute_v(lay: Layout, src: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """bf16 natural [B, T*H*W, heads, d] -> tiled V in the bf16 P.V operand
+    layout [B, heads, n_padded, d] (vsa_tile_permute_v), for the forwards'
+    ``v_operand=True``."""
+    info = layout_info(lay)
+    nat, tiled = _natural_shape(lay, info), _tiled_shape(lay, info)
+    _want(src, "src", torch.bfloat16, nat)
+    if out is None:
+        out = torch.empty(tiled, dtype=torch.bfloat16, device=src.device)
+    _want(out, "out", torch.bfloat16, tiled)
+    c = lay.c()
+    check(lib().vsa_tile_permute_v(ctypes.byref(c), _ptr(src), _ptr(out), _stream(stream)))
     return out
 
 
@@ -397,7 +414,8 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
 
     q/k/v tiled; float32 -> float32 out, bfloat16 -> bfloat16 out, uint8 e4m3
     codes (with ``scales`` = (q_scale, k_scale, v_scale)) -> bfloat16 out;
-    ``v_operand``: v holds codes from quant_fp8_tiles(..., v_operand=True).
+    ``v_operand``: v holds codes from quant_fp8_tiles(..., v_operand=True),
+    or (bf16) the output of tile_permute_v.
     kv_idx 2-D [n_tiles, max_kv] = one shared table; 4-D [B, heads, n_tiles,
     max_kv] = per-(b, head) lists; None = dense. ``per_tile_walk`` (2-D
     tables only): each query tile walks its own list (list_mode 2).
@@ -424,10 +442,12 @@ def block_sparse_attn_fwd(lay: Layout, q: torch.Tensor, k: torch.Tensor, v: torc
             _want(t, nm, torch.float32, (lay.batch, lay.heads, info.n_tiles))
         if v_operand:
             dtype = VSA_FP8_E4M3_VOP
-    elif v_operand:
-        raise ValueError("v_operand applies to fp8 codes only")
     elif scales is not None:
         raise ValueError("scales apply to fp8 codes only")
+    elif v_operand:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("v_operand applies to bf16 tensors or fp8 codes")
+        dtype, odt = VSA_BF16_VOP, q.dtype
     else:
         dtype, odt = _DT.get(q.dtype, -1), q.dtype
     if out is None:
@@ -582,9 +602,10 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
                               softmax_scale: Optional[float] = None, want_lse: bool = False,
                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                               stream=None, per_tile_walk: bool = False,
-                              work_order: Optional[torch.Tensor] = None):
+                              work_order: Optional[torch.Tensor] = None, v_operand: bool = False):
     """Forward with natural-order Q in and O out (vsa_block_sparse_attn_fwd_nat):
-    q_nat and the returned out are [B, T*H*W, heads, d]; k and v tiled.
+    q_nat and the returned out are [B, T*H*W, heads, d]; k and v tiled
+    (``v_operand``: bf16 v from tile_permute_v).
     Returns (out, lse or None); lse in the tiled order."""
     info = layout_info(lay)
     if softmax_scale is None:
@@ -598,6 +619,10 @@ def block_sparse_attn_fwd_nat(lay: Layout, q_nat: torch.Tensor, k: torch.Tensor,
         raise ValueError("per_tile_walk applies to a shared [n_tiles, max_kv] table only")
     _check_order(lay, info, kv_idx, work_order)
     dtype = _DT.get(q_nat.dtype, -1)
+    if v_operand:
+        if q_nat.dtype != torch.bfloat16:
+            raise ValueError("v_operand applies to bf16 tensors")
+        dtype = VSA_BF16_VOP
     if out is None:
         out = torch.empty_like(q_nat)
     if want_lse and lse is None:

@@ -23,12 +23,14 @@ VSA_F32 = 0
 VSA_BF16 = 1
 VSA_FP8_E4M3 = 2
 VSA_FP8_E4M3_VOP = 3
+VSA_BF16_VOP = 4
 
 VSA_TILE3D = 0
 VSA_SKIPARSE2D = 1
 
 EXPORTED = (
-    "vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window", "vsa_build_mask_topk",
+    "vsa_layout_query", "vsa_tile_permute", "vsa_tile_permute_v", "vsa_build_mask_window",
+    "vsa_build_mask_topk",
     "vsa_build_mask_topk_workspace", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
     "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat", "vsa_build_mask_window_grouped",
     "vsa_quant_fp8_tiles_grouped", "vsa_tile_permute_pool", "vsa_build_mask_topk_pooled",
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
     LP = ctypes.POINTER(VsaLayout)
     L.vsa_layout_query.argtypes = [LP, ctypes.POINTER(VsaLayoutInfo)]
     L.vsa_tile_permute.argtypes = [LP, I32, P, P, I32, P]
+    L.vsa_tile_permute_v.argtypes = [LP, P, P, P]
     L.vsa_build_mask_window.argtypes = [LP, I32, I32, I32, I32, P, P, P]
     L.vsa_build_mask_topk.argtypes = [LP, P, P, F32, I32, F32, I32, I32, P, P, P, P, SZ, P]
     L.vsa_build_mask_topk_workspace.argtypes = [LP]
@@ -99,7 +102,7 @@ def lib() -> ctypes.CDLL:
     L.vsa_block_sparse_attn_fwd_fp8_nat.argtypes = [LP, I32, P, P, P, P, P, P, P, P, I32, I32, P, F32,
                                                     P, P, P]
     L.vsa_build_mask_topk_pooled.argtypes = [LP, P, P, F32, I32, F32, I32, I32, P, P, P, P, SZ, P]
-    for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_build_mask_window",
+    for name in ("vsa_layout_query", "vsa_tile_permute", "vsa_tile_permute_v", "vsa_build_mask_window",
                  "vsa_build_mask_topk", "vsa_quant_fp8_tiles", "vsa_quant_fp8_tiles_v",
                  "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_fwd_nat",
                  "vsa_build_mask_window_grouped", "vsa_quant_fp8_tiles_grouped",

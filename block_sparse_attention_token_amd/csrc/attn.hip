@@ -254,8 +254,12 @@ struct SchedWindow {
 // Every LDS row is padded by 16 bytes: the 16 rows a half-wave reads at one
 // column then start 16 bytes apart, which spreads them over all banks, and
 // each fragment address is one base register plus an immediate offset.
-template <int KVH, int D, int THREADS, bool F32IN>
+// VOP: bf16 V already stored in that order (each 32-token block channel-major,
+// positions in the order above), so V^T rows are filled by whole 16-byte
+// chunks copied from contiguous loads.
+template <int KVH, int D, int THREADS, bool F32IN, bool VOP = false>
 struct BfTile {
+  static_assert(!(VOP && F32IN), "the V operand layout is bf16");
   static constexpr int ES = F32IN ? 4 : 2;
   static constexpr int CPR_K = D / 8;               // 16-byte chunks per K row
   static constexpr int CPR_V = KVH / 8;             // 16-byte chunks per V^T row
@@ -266,6 +270,9 @@ struct BfTile {
   static constexpr int PAIRS = KVH / 2;
   static constexpr int V_PIECES = PAIRS * (D / 8);
   static constexpr int V_PER_T = (V_PIECES + THREADS - 1) / THREADS;
+  static constexpr int V_CHUNKS = KVH * D / 8;      // VOP: 16-byte chunks per block
+  static constexpr int V_CH_PER_T = (V_CHUNKS + THREADS - 1) / THREADS;
+  static_assert(!VOP || V_CH_PER_T <= 2 * V_PER_T, "VOP chunks fit the staging registers");
   static constexpr int K_LDS = KVH * KS_;           // uint4 per K buffer
   static constexpr int V_LDS = D * VS_;             // uint4 per V^T buffer
   uint4 kreg[K_PER_T];
@@ -289,6 +296,15 @@ struct BfTile {
     }
   }
   __device__ __forceinline__ void load_v(rsrc_t rv, uint32_t block_off, int tid) {
+    if constexpr (VOP) {
+#pragma unroll
+      for (int k = 0; k < V_CH_PER_T; ++k) {
+        const int c = tid + k * THREADS;
+        if (V_CHUNKS % THREADS == 0 || c < V_CHUNKS)
+          vreg[k >> 1][k & 1] = bload8<false>(rv, tid * 16, block_off + k * THREADS * 16);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
@@ -308,6 +324,19 @@ struct BfTile {
     }
   }
   __device__ __forceinline__ void store_v(uint4* v_lds, int tid) const {
+    if constexpr (VOP) {
+      // chunk c of the block: 32-token block c / (4 D), channel (c / 4) % D,
+      // positions 8 (c % 4) .. + 7 of that block
+#pragma unroll
+      for (int k = 0; k < V_CH_PER_T; ++k) {
+        const int c = tid + k * THREADS;
+        if (V_CHUNKS % THREADS == 0 || c < V_CHUNKS) {
+          const int kb = c / (4 * D), ch = (c >> 2) - kb * D;
+          v_lds[ch * VS_ + 4 * kb + (c & 3)] = vreg[k >> 1][k & 1];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + i * THREADS;
@@ -558,7 +587,8 @@ constexpr float kLazyBf16 = 8.0f;
 // NAT: Q is read from and O written to the natural order [B, T*H*W, heads, d]
 // (the tile permute of Q and the inverse permute of O fused into the
 // kernel's first load and last store); K and V stay tiled.
-template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF, bool NAT>
+// VOP: bf16 V in the P.V operand layout (whole-chunk staging).
+template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF, bool NAT, bool VOP>
 __global__ __launch_bounds__(64 * QPW * (TILE / 32)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int WPQ = TILE / 32;         // waves per query tile
@@ -566,8 +596,9 @@ void attn_bf16_kernel(DevLayout L, AttnArgs a, int n_work) {
   constexpr int MB = KVH / 32;
   constexpr int NPS = KVH / 16;
   constexpr int THREADS = 64 * QPW * WPQ;
-  using IO = BfTile<KVH, D, THREADS, F32IN>;
+  using IO = BfTile<KVH, D, THREADS, F32IN, VOP>;
   static_assert(TILE == 32 || TILE == 64, "tiles of 32 or 64 tokens");
+  static_assert(!VOP || TILE == 64, "the V operand layout has 64-token tiles");
 
   static_assert(NBUF == 2 || NBUF == 4, "two or four K/V buffers");
   __shared__ uint4 k_lds[NBUF][IO::K_LDS];
@@ -1271,15 +1302,15 @@ void attn_fp8_kernel(DevLayout L, AttnArgs a, int n_work) {
 }
 
 // ---------------------------------------------------------------------------
-template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF = 2>
+template <int TILE, int KVH, int D, int QPW, bool F32IN, int NBUF = 2, bool VOP = false>
 hipError_t launch_bf16(const DevLayout& L, const AttnArgs& a, hipStream_t s) {
   const int n_work = L.B * L.heads * ((L.n_tiles + QPW - 1) / QPW);
   const size_t dyn = QPW > 1 ? (size_t)L.n_tiles * sizeof(int) : 0;
   if (a.natural_io)
-    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, true>), dim3(n_work),
+    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, true, VOP>), dim3(n_work),
                        dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, false>), dim3(n_work),
+    hipLaunchKernelGGL((attn_bf16_kernel<TILE, KVH, D, QPW, F32IN, NBUF, false, VOP>), dim3(n_work),
                        dim3(64 * QPW * (TILE / 32)), dyn, s, L, a, n_work);
   return hipGetLastError();
 }
@@ -1313,6 +1344,14 @@ hipError_t launch_attn(const DevLayout& L, int dtype, const AttnArgs& a, hipStre
   // shared tables the caller marks as walked per tile (list_mode 2): one
   // query tile per workgroup.
   const bool grouped = (a.kv_idx == nullptr || a.list_mode == 0) && L.n_tiles <= 4096;
+  if (dtype == 4) {   // bf16 with V in the P.V operand layout
+    if (L.C != 64 || (L.d != 128 && L.d != 64)) return hipErrorInvalidValue;
+    if (L.d == 128)
+      return grouped ? launch_bf16<64, 64, 128, 4, false, 4, true>(L, a, s)
+                     : launch_bf16<64, 32, 128, 1, false, 2, true>(L, a, s);
+    return grouped ? launch_bf16<64, 64, 64, 4, false, 4, true>(L, a, s)
+                   : launch_bf16<64, 32, 64, 1, false, 2, true>(L, a, s);
+  }
   if (dtype == 3) {   // e4m3 with V codes in the P.V operand layout
     if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
     return grouped ? launch_fp8<4, true>(L, a, s) : launch_fp8<1, true>(L, a, s);

@@ -146,6 +146,25 @@ vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void*
                                         static_cast<hipStream_t>(stream)), "vsa_tile_permute");
 }
 
+vsa_status vsa_tile_permute_v(const vsa_layout* layout, const void* src, void* dst, void* stream) {
+  vsa::DevLayout L;
+  vsa_status st = derive(layout, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (!src || !dst) return fail(VSA_ERR_INVALID, "src and dst must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(VSA_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (L.C != 64) return fail(VSA_ERR_UNSUPPORTED, "the V operand layout needs 64-token tiles");
+  if (L.d % 8 || L.d > 256) return fail(VSA_ERR_UNSUPPORTED, "head_dim must be <= 256 and a multiple of 8");
+  if (L.heads > 65535 || L.B > 65535)
+    return fail(VSA_ERR_UNSUPPORTED, "grid too large for one launch");
+  const long long sb = (long long)L.B * L.n_tokens * L.heads * L.d * 2;
+  const long long db = (long long)L.B * L.heads * L.n_padded * L.d * 2;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + db && d0 < s0 + sb) return fail(VSA_ERR_INVALID, "src and dst must not overlap");
+  return hip_status(vsa::launch_permute_vop(L, src, dst, static_cast<hipStream_t>(stream)),
+                    "vsa_tile_permute_v");
+}
+
 vsa_status vsa_tile_permute_pool(const vsa_layout* layout, const void* src, void* dst,
                                  float* pooled, void* stream) {
   vsa::DevLayout L;
@@ -366,7 +385,7 @@ vsa_status vsa_quant_fp8_tiles_nat(const vsa_layout* layout, const void* x_nat, 
 // The attention kernels address one (batch, head) slice of a tiled tensor
 // through a buffer resource with 32-bit offsets.
 static vsa_status check_slice(const vsa::DevLayout& L, int32_t dtype) {
-  const long long es = dtype == VSA_F32 ? 4 : (dtype == VSA_BF16 ? 2 : 1);
+  const long long es = dtype == VSA_F32 ? 4 : (dtype == VSA_BF16 || dtype == VSA_BF16_VOP ? 2 : 1);
   if ((long long)L.n_padded * L.d * es > 0x7FFFFFFFll)
     return fail(VSA_ERR_UNSUPPORTED, "one (batch, head) slice of a tiled tensor must stay below 2 GiB");
   return VSA_OK;
@@ -419,8 +438,11 @@ vsa_status vsa_block_sparse_attn_fwd(const vsa_layout* layout, int32_t dtype, co
   st = check_order(work_order, kv_idx, list_mode);
   if (st != VSA_OK) return st;
   if (!isfinite(softmax_scale)) return fail(VSA_ERR_INVALID, "softmax_scale must be finite");
-  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP)
+  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_FP8_E4M3 && dtype != VSA_FP8_E4M3_VOP &&
+      dtype != VSA_BF16_VOP)
     return fail(VSA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype == VSA_BF16_VOP && L.C != 64)
+    return fail(VSA_ERR_UNSUPPORTED, "the bf16 V operand layout needs 64-token tiles");
   if (dtype == VSA_FP8_E4M3 || dtype == VSA_FP8_E4M3_VOP) {
     if (!q_scale || !k_scale || !v_scale) return fail(VSA_ERR_INVALID, "fp8 needs q_scale, k_scale and v_scale");
     if (L.C != 64 || L.d != 128) return fail(VSA_ERR_UNSUPPORTED, "fp8 attention needs 64-token tiles and head_dim 128");
@@ -633,8 +655,10 @@ vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype
   vsa::DevLayout L;
   vsa_status st = derive(layout, &L, nullptr);
   if (st != VSA_OK) return st;
-  if (dtype != VSA_F32 && dtype != VSA_BF16)
-    return fail(VSA_ERR_UNSUPPORTED, "natural-order attention takes VSA_F32 or VSA_BF16");
+  if (dtype != VSA_F32 && dtype != VSA_BF16 && dtype != VSA_BF16_VOP)
+    return fail(VSA_ERR_UNSUPPORTED, "natural-order attention takes VSA_F32, VSA_BF16 or VSA_BF16_VOP");
+  if (dtype == VSA_BF16_VOP && L.C != 64)
+    return fail(VSA_ERR_UNSUPPORTED, "the bf16 V operand layout needs 64-token tiles");
   const long long es = dtype == VSA_F32 ? 4 : 2;
   if ((long long)L.n_tokens * L.heads * L.d * es > 0x7FFFFFFFll)
     return fail(VSA_ERR_UNSUPPORTED, "one batch of natural Q must stay below 2 GiB");

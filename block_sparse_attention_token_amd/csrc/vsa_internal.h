@@ -123,6 +123,8 @@ __device__ __forceinline__ int xcd_chunked(int i, int n, int G) {
 // ----- launchers (return hipError_t of the launch) -----
 hipError_t launch_permute(const DevLayout& L, int esize, const void* src, void* dst, int inverse,
                           hipStream_t s);
+// natural bf16 -> tiled V in the bf16 P.V operand layout (64-token tiles, d % 8 == 0, d <= 256)
+hipError_t launch_permute_vop(const DevLayout& L, const void* src, void* dst, hipStream_t s);
 hipError_t launch_mask_window(const DevLayout& L, int rt, int rh, int rw, int max_kv,
                               int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
 hipError_t launch_route(const DevLayout& L, const void* q, const void* k, float coarse_scale,

@@ -63,7 +63,10 @@ typedef enum vsa_dtype {
   VSA_FP8_E4M3 = 2,  /* OCP FP8 E4M3 ("fn": bias 7, max 448, no inf) codes + fp32 tile scales */
   /* As VSA_FP8_E4M3, with the V codes in the P.V operand layout written by
    * vsa_quant_fp8_tiles_v (attention only; Q and K codes as before). */
-  VSA_FP8_E4M3_VOP = 3
+  VSA_FP8_E4M3_VOP = 3,
+  /* As VSA_BF16, with V in the bf16 P.V operand layout written by
+   * vsa_tile_permute_v (attention forwards only; Q and K tiled as before). */
+  VSA_BF16_VOP = 4
 } vsa_dtype;
 
 /* ----- token layouts ------------------------------------------------------ */
@@ -118,6 +121,20 @@ vsa_status vsa_layout_query(const vsa_layout* layout, vsa_layout_info* info);
  * The result is a pure data movement: bit-exact. src and dst must not overlap. */
 vsa_status vsa_tile_permute(const vsa_layout* layout, int32_t dtype, const void* src, void* dst,
                             int32_t inverse, void* stream);
+
+/* vsa_tile_permute_v: the tile permutation of a bf16 V (FVAttn summary:
+ * video-aware block organisation), stored in the order the bf16 P.V product
+ * of the forward consumes it, so the kernel stages V with whole 16-byte
+ * copies. src bf16 natural [B, T*H*W, heads, d] -> dst bf16 [B, heads,
+ * n_padded, d]: tile j of (b, head) occupies elements [64*d*j, 64*d*(j+1))
+ * of its slice as two 32-token blocks kb = 0, 1 of 32*d elements; element
+ * 32*c + p of block kb holds channel c of the tile's token
+ * 32*kb + 16*A + 8*(i / 4) + 4*h + i % 4, where p = 16*A + 8*h + i
+ * (A, h in 0..1; i in 0..7). Pad tokens are written as zeros. A pure data
+ * movement (bit-exact). Needs tile_tokens 64 and head_dim <= 256 and a
+ * multiple of 8 (VSA_ERR_UNSUPPORTED otherwise); 16-byte aligned pointers;
+ * src and dst must not overlap. Pass the result as v with dtype VSA_BF16_VOP. */
+vsa_status vsa_tile_permute_v(const vsa_layout* layout, const void* src, void* dst, void* stream);
 
 /* ----- S2: fixed block masks -------------------------------------------------
  * FPSAttention, Approach and window ablation (sliding tile window);
@@ -278,7 +295,9 @@ vsa_status vsa_quant_fp8_tiles_nat(const vsa_layout* layout, const void* x_nat, 
  *     dtype VSA_FP8_E4M3: uint8 codes in with q_scale / k_scale / v_scale
  *       float [B, heads, n_tiles] from vsa_quant_fp8_tiles; bf16 out;
  *     dtype VSA_FP8_E4M3_VOP: the same, with v from vsa_quant_fp8_tiles_v
- *       (no byte transposition of V inside the kernel; identical output).
+ *       (no byte transposition of V inside the kernel; identical output);
+ *     dtype VSA_BF16_VOP: as VSA_BF16, with v from vsa_tile_permute_v
+ *       (64-token tiles; output identical to VSA_BF16's).
  *   kv_idx / kv_cnt: lists as written by vsa_build_mask_window (list_mode 0:
  *     one table [n_tiles, max_kv] shared by every batch and head) or by
  *     vsa_build_mask_topk (list_mode 1: [B, heads, n_tiles, max_kv]).
@@ -331,8 +350,8 @@ vsa_status vsa_build_work_order(const vsa_layout* layout, const int32_t* kv_cnt,
  * [B, T*H*W, heads, d]; k and v stay tiled [B, heads, n_padded, d] (from
  * vsa_tile_permute); lse, if given, is in the tiled order as for the
  * forward. Every real token of out is written; the result equals the
- * forward's followed by vsa_tile_permute(inverse). dtype VSA_F32 or
- * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise, and when one batch of q exceeds
+ * forward's followed by vsa_tile_permute(inverse). dtype VSA_F32, VSA_BF16
+ * or VSA_BF16_VOP (VSA_ERR_UNSUPPORTED otherwise, and when one batch of q exceeds
  * 2 GiB); lists, list_mode, work_order and scale as for
  * vsa_block_sparse_attn_fwd. */
 vsa_status vsa_block_sparse_attn_fwd_nat(const vsa_layout* layout, int32_t dtype, const void* q,

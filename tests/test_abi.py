@@ -302,3 +302,30 @@ def test_work_order_argument_errors_before_launch():
     p = "vsa_block_sparse_attn_fwd_fp8_nat"
     assert _status(p, L, B.VSA_FP8_E4M3, q, k, v, o, o, o, _fake(9), _fake(10), 8, 0, wo,
                    ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_INVALID
+
+
+def test_bf16_v_operand_argument_errors_before_launch():
+    lay = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=128).c()
+    L = ctypes.byref(lay)
+    f = "vsa_tile_permute_v"
+    assert _status(f, L, None, _fake(1), None) == B.VSA_ERR_INVALID
+    assert _status(f, L, ctypes.c_void_p(0x400008), _fake(1), None) == B.VSA_ERR_INVALID   # misaligned
+    assert _status(f, L, _fake(1), _fake(2), None) == B.VSA_ERR_INVALID                     # overlap
+    c32 = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=128, tile=(2, 4, 4)).c()
+    assert _status(f, ctypes.byref(c32), _fake(1), _fake(2), None) == B.VSA_ERR_UNSUPPORTED
+    wide = vsa.Layout(T=21, H=45, W=80, heads=2, head_dim=264).c()
+    assert _status(f, ctypes.byref(wide), _fake(1), _fake(2), None) == B.VSA_ERR_UNSUPPORTED
+    # the forwards take the layout with 64-token tiles only
+    q, k, v, o = (_fake(i) for i in range(3, 7))
+    g = "vsa_block_sparse_attn_fwd"
+    assert _status(g, ctypes.byref(c32), B.VSA_BF16_VOP, q, k, v, None, None, None, None, None, 0, 0,
+                   None, ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+    n = "vsa_block_sparse_attn_fwd_nat"
+    assert _status(n, ctypes.byref(c32), B.VSA_BF16_VOP, q, k, v, None, None, 0, 0, None,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED
+    assert b"64-token" in B.lib().vsa_last_error()
+    # fp8 natural-order output does not take it
+    p = "vsa_block_sparse_attn_fwd_fp8_nat"
+    s = _fake(9)
+    assert _status(p, L, B.VSA_BF16_VOP, q, k, v, s, s, s, None, None, 0, 0, None,
+                   ctypes.c_float(0.1), o, None, None) == B.VSA_ERR_UNSUPPORTED

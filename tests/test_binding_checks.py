@@ -97,7 +97,15 @@ def test_fp8_forward_checks():
             scales=(s, s, f32((1, 2, N_T + 1))))
     _raises("k_scale must have dtype", vsa.block_sparse_attn_fwd, LAY, c, c, c,
             scales=(s, bf((1, 2, N_T)), s))
-    _raises("v_operand applies", vsa.block_sparse_attn_fwd, LAY, bf(TILED), bf(TILED), bf(TILED),
+    _raises("v_operand applies", vsa.block_sparse_attn_fwd, LAY, f32(TILED), f32(TILED), f32(TILED),
+            v_operand=True)
+
+
+def test_bf16_v_operand_checks():
+    _raises("src must have dtype", vsa.tile_permute_v, LAY, f32(NAT))
+    _raises("src must have shape", vsa.tile_permute_v, LAY, bf(TILED))
+    _raises("out must have shape", vsa.tile_permute_v, LAY_PAD, bf((1, 192, 2, 64)), out=bf((1, 2, 192, 64)))
+    _raises("v_operand applies", vsa.block_sparse_attn_fwd_nat, LAY, f32(NAT), f32(TILED), f32(TILED),
             v_operand=True)
 
 

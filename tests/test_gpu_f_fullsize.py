@@ -4,6 +4,7 @@ against the fp64 oracle.
 
 * 768p Skiparse sparse layer (OSP-Next card, Model Summary: Skiparse-2D along
   H and W): natural-order Q in, natural-order O out (vsa_block_sparse_attn_fwd_nat),
+  V in the bf16 P.V operand layout (vsa_tile_permute_v) as the bench runs it,
   Skiparse lists from vsa_build_mask_window, 40 heads; the oracle checks every
   one of the 1,260 query tiles of one head.
 * 768p dense layer (OSP-Next wiki TL;DR: hybrid full + sparse): 256 query
@@ -60,7 +61,8 @@ def _skiparse_case():
     _, blay = layouts(cfg)
     q, k, v = inputs(cfg.name)
     qn = to_device(q, "bf16")
-    kt, vt = (vsa.tile_permute(blay, to_device(x, "bf16")) for x in (k, v))
+    kt = vsa.tile_permute(blay, to_device(k, "bf16"))
+    vt = vsa.tile_permute_v(blay, to_device(v, "bf16"))       # V in the P.V operand layout
     return cfg, blay, (q, k, v), qn, kt, vt
 
 
@@ -69,7 +71,7 @@ def test_skiparse_768p_sparse_every_tile_of_one_head():
     h = 17
     announce("full-size: 768p Skiparse sparse layer, natural-order I/O, head 17, all 1,260 tiles")
     idx, cnt = vsa.build_mask_window(blay, (0, 0, 0))
-    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt, want_lse=True)
+    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt, want_lse=True, v_operand=True)
     torch.cuda.synchronize()
     olay1, qo = _one_head(cfg, q, h)
     _, ko = _one_head(cfg, k, h)
@@ -85,7 +87,7 @@ def test_skiparse_768p_dense_256_tiles_of_one_head():
     cfg, blay, (q, k, v), qn, kt, vt = _skiparse_case()
     h = 29
     announce("full-size: 768p dense layer, natural-order I/O, head 29, 256 query tiles")
-    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, want_lse=True)
+    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, want_lse=True, v_operand=True)
     torch.cuda.synchronize()
     olay1, qo = _one_head(cfg, q, h)
     _, ko = _one_head(cfg, k, h)
@@ -160,9 +162,11 @@ def test_window_480p_per_tile_walk_every_tile_of_one_head():
     h = 5
     announce("full-size: 480p window layer walked per query tile, head 5, all 624 tiles")
     qn = to_device(q, "bf16")
-    kt, vt = (vsa.tile_permute(blay, to_device(x, "bf16")) for x in (k, v))
+    kt = vsa.tile_permute(blay, to_device(k, "bf16"))
+    vt = vsa.tile_permute_v(blay, to_device(v, "bf16"))
     idx, cnt = vsa.build_mask_window(blay, cfg.window)
-    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt, want_lse=True, per_tile_walk=True)
+    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt, want_lse=True, per_tile_walk=True,
+                                             v_operand=True)
     torch.cuda.synchronize()
     olay1, qo = _one_head(cfg, q, h)
     _, ko = _one_head(cfg, k, h)
