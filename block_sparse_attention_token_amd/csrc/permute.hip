@@ -43,47 +43,45 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(DevLayout L, int row_
 }
 
 // Natural bf16 -> tiled V in the bf16 P.V operand layout (64-token tiles):
-// the tile's rows of one head are gathered into LDS (pad rows as zeros), then
-// written as two 32-token blocks, each channel-major with the block's tokens
-// in the order the P.V product consumes them: position 16 ps + 8 h + i of a
-// channel row holds token 16 ps + 8 (i / 4) + 4 h + i % 4 of the block.
-// Output chunk q (16 bytes, 8 positions) of the tile is block q / (4 d),
-// channel (q / 4) % d, positions 8 (q % 4) .. + 7: consecutive threads write
-// consecutive chunks.
+// each 32-token block kb of a tile is stored channel-major, position
+// 16 A + 8 h + i of a channel row holding token 16 A + 8 (i / 4) + 4 h + i % 4
+// of the block. Output chunk (kb, channel c, part) is 16 bytes: positions
+// 8 part .. +7 of channel c, i.e. tokens 32 kb + 16 A + 8 (i / 4) + 4 h + i % 4
+// (part = 2 A + h, i = 0..7). One thread takes such an octet of tokens for 8
+// channels: 8 16-byte loads (pad tokens read as zeros), an 8 x 8 transpose of
+// 16-bit values with byte permutes, 8 16-byte stores. Lanes with consecutive
+// channel groups read consecutive 16 bytes of a token row; the four parts of
+// one channel are adjacent lanes' stores (64 contiguous bytes).
 __global__ __launch_bounds__(kThreads) void permute_vop_kernel(DevLayout L, const uint4* __restrict__ src,
                                                                uint4* __restrict__ dst) {
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
   const int b = blockIdx.z;
-  const int chunks = L.d >> 3;                       // 16-byte chunks per bf16 row
-  __shared__ uint4 rows[64 * 32];                    // the tile, token-major (d <= 256)
-  for (int idx = threadIdx.x; idx < 64 * chunks; idx += kThreads) {
-    const int r = idx / chunks;
-    const int ch = idx - r * chunks;
-    const int nat = natural_index(L, tile, r);
-    rows[idx] = nat < 0 ? make_uint4(0u, 0u, 0u, 0u)
-                        : src[(((long long)b * L.n_tokens + nat) * L.heads + head) * chunks + ch];
-  }
-  __syncthreads();
-  const uint16_t* el = reinterpret_cast<const uint16_t*>(rows);
+  const int chunks = L.d >> 3;                       // 16-byte chunks per bf16 row = channel groups
   const long long out0 = ((long long)(b * L.heads + head) * L.n_padded + (long long)tile * 64) * chunks;
-  for (int q = threadIdx.x; q < 64 * chunks; q += kThreads) {
-    const int kb = q / (4 * L.d);
-    const int c = (q >> 2) - kb * L.d;
-    const int p0 = 8 * (q & 3);
-    uint32_t w[4];
+  for (int item = threadIdx.x; item < 8 * chunks; item += blockDim.x) {
+    const int part = (item / chunks) & 3, kb = item / (4 * chunks), cg = item % chunks;
+    const int t0 = 32 * kb + 16 * (part >> 1) + 4 * (part & 1);
+    uint4 x[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t two = 0u;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int p = p0 + 2 * e + k;
-        const int t = 16 * (p >> 4) + 8 * ((p >> 2) & 1) + 4 * ((p >> 3) & 1) + (p & 3);
-        two |= (uint32_t)el[(32 * kb + t) * L.d + c] << (16 * k);
-      }
-      w[e] = two;
+    for (int i = 0; i < 8; ++i) {
+      const int nat = natural_index(L, tile, t0 + 8 * (i >> 2) + (i & 3));
+      x[i] = nat < 0 ? make_uint4(0u, 0u, 0u, 0u)
+                     : src[(((long long)b * L.n_tokens + nat) * L.heads + head) * chunks + cg];
     }
-    dst[out0 + q] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // channel 8 cg + j: half j % 2 of word j / 2 of every token; positions
+      // 2 k, 2 k + 1 are tokens x[2 k], x[2 k + 1]
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (&x[2 * k].x)[j >> 1], hi = (&x[2 * k + 1].x)[j >> 1];
+        w[k] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      dst[out0 + ((long long)(kb * L.d + 8 * cg + j) << 2) + part] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -92,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void permute_vop_kernel(DevLayout L, cons
 hipError_t launch_permute_vop(const DevLayout& L, const void* src, void* dst, hipStream_t s) {
   if (L.C != 64 || L.d % 8 || L.d > 256) return hipErrorInvalidValue;
   dim3 grid(L.n_tiles, L.heads, L.B);
-  hipLaunchKernelGGL(permute_vop_kernel, grid, dim3(kThreads), 0, s, L, static_cast<const uint4*>(src),
+  const int threads = min(kThreads, (L.d + 63) / 64 * 64);     // one thread per (token octet, channel group)
+  hipLaunchKernelGGL(permute_vop_kernel, grid, dim3(threads), 0, s, L, static_cast<const uint4*>(src),
                      static_cast<uint4*>(dst));
   return hipGetLastError();
 }
