@@ -172,7 +172,9 @@ __device__ __forceinline__ float wave_sum(float x) { return wave_reduce<0>(x); }
 __device__ __forceinline__ float wave_max(float x) { return wave_reduce<1>(x); }
 __device__ __forceinline__ float wave_min(float x) { return wave_reduce<2>(x); }
 
-template <int R, int MT, int NCH, int THREADS>
+// FULL: d == 128 * NCH, so every channel step is real and the loads and
+// products need no per-step test.
+template <int R, int MT, int NCH, int THREADS, bool FULL>
 __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float* __restrict__ q_pooled,
                                                               const float* __restrict__ k_pooled,
                                                               float coarse_scale, int top_k, float top_p,
@@ -203,8 +205,9 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = 128 * cq + 16 * u + 4 * k4;
-      const float4 v = (m16 < rows && e < d) ? *reinterpret_cast<const float4*>(qb + (long long)(i0 + m16) * d + e)
-                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = (m16 < rows && (FULL || e < d))
+                           ? *reinterpret_cast<const float4*>(qb + (long long)(i0 + m16) * d + e)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
       qa[cq][4 * u + 0] = v.x;
       qa[cq][4 * u + 1] = v.y;
       qa[cq][4 * u + 2] = v.z;
@@ -218,7 +221,8 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = 128 * cq + 16 * u + 4 * k4;
-        kr[cq][u] = e < d ? *reinterpret_cast<const float4*>(kb + (long long)j * d + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (FULL) kr[cq][u] = *reinterpret_cast<const float4*>(kb + (long long)j * d + e);
+        else kr[cq][u] = e < d ? *reinterpret_cast<const float4*>(kb + (long long)j * d + e) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
   };
   auto score_blk = [&](int blk, const float4 (&kr)[NCH][8]) {
@@ -227,23 +231,29 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
     for (int cq = 0; cq < NCH; ++cq)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (128 * cq + 16 * u >= d) continue;
+        if (!FULL && 128 * cq + 16 * u >= d) continue;
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 0], kr[cq][u].x, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 1], kr[cq][u].y, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 2], kr[cq][u].z, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[cq][4 * u + 3], kr[cq][u].w, acc, 0, 0, 0);
       }
-    // lane l holds rows 4 (l / 16) .. +3 of key tile 16 blk + l % 16
+    // lane l holds rows 4 (l / 16) .. +3 of key tile 16 blk + l % 16; the
+    // selection masks key tiles without real tokens itself, so only the
+    // optional score output needs the -inf
     const int j = 16 * blk + m16;
     if (j < n) {
-      const bool real = real_rows(L, tile_valid(L, j)) > 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 4 * k4 + t;
-        if (r >= rows) continue;
-        const float v = real ? coarse_scale * acc[t] : -INFINITY;
-        sc[r * n + j] = v;
-        if (scores) scores[(bh * n + i0 + r) * n + j] = v;
+        if (r < rows) sc[r * n + j] = coarse_scale * acc[t];
+      }
+      if (scores) {
+        const bool real = real_rows(L, tile_valid(L, j)) > 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * k4 + t;
+          if (r < rows) scores[(bh * n + i0 + r) * n + j] = real ? coarse_scale * acc[t] : -INFINITY;
+        }
       }
     }
   };
@@ -443,8 +453,12 @@ static hipError_t launch_route_rm(const DevLayout& L, const float* qp, const flo
                                   int32_t* kv_cnt, float* scores, hipStream_t s) {
   const size_t lds = (size_t)R * L.n_tiles * sizeof(float);
   dim3 grid((L.n_tiles + R - 1) / R, L.heads, L.B);
-  hipLaunchKernelGGL((route_kernel<R, MT, NCH, THREADS>), grid, dim3(THREADS), lds, s, L, qp, kp, coarse_scale,
-                     top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
+  if (L.d == 128 * NCH)
+    hipLaunchKernelGGL((route_kernel<R, MT, NCH, THREADS, true>), grid, dim3(THREADS), lds, s, L, qp, kp,
+                       coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
+  else
+    hipLaunchKernelGGL((route_kernel<R, MT, NCH, THREADS, false>), grid, dim3(THREADS), lds, s, L, qp, kp,
+                       coarse_scale, top_k, top_p, k_floor, max_kv, kv_idx, kv_cnt, scores);
   return hipGetLastError();
 }
 
