@@ -10,7 +10,7 @@ FlashAttention-compatible sparse attention).
 * every bf16 forward with ``v_operand`` gives the same bits as with
   token-major V: dense, shared windows (grouped and per-tile walks), routed
   per-head lists with and without a work order, tiled and natural-order Q/O,
-  head_dim 64 and 128; at full size the 768p Skiparse layer, the 480p
+  head_dim 64 and 128, 3D tiles and Skiparse groups with a padded last tile; at full size the 768p Skiparse layer, the 480p
   window layer (both walks) and the routed top-32 layer.
 """
 import numpy as np
@@ -58,14 +58,16 @@ def test_permute_v_matches_oracle_layout(grid, heads, d, kind, stride):
     assert np.array_equal(got.view(torch.int16).cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_forwards_identical_with_v_operand(d):
+@pytest.mark.parametrize("d,kind,grid", [(128, "tile3d", (9, 14, 22)), (64, "tile3d", (9, 14, 22)),
+                                          (128, "skiparse2d", (3, 12, 20))])
+def test_forwards_identical_with_v_operand(d, kind, grid):
     _gpu()
-    B, heads, T, H, W = 2, 3, 9, 14, 22
-    lay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, batch=B)
+    B, heads = 2, 3
+    T, H, W = grid
+    lay = vsa.Layout(T=T, H=H, W=W, heads=heads, head_dim=d, kind=kind, batch=B)
     info = vsa.layout_info(lay)
     n = info.n_tiles
-    announce(f"bf16 V operand: forwards d={d}")
+    announce(f"bf16 V operand: forwards d={d} kind={kind} grid={grid}")
     rng = np.random.default_rng(42)
     x = [round_to_bf16(rng.standard_normal((B, info.n_tokens, heads, d)).astype(np.float32))
          for _ in range(3)]
