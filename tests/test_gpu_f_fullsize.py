@@ -17,6 +17,12 @@ against the fp64 oracle.
   oracle's routing (exact up to near-ties), its output and lse for every query
   tile against the oracle of the fp8 method on those lists.
 * 480p window layer walked per query tile (list_mode 2), every tile of one head.
+* top-32 layer through the bench's calls (VSA page, Research Type row: a
+  coarse stage picks key blocks per query block): means of Q without a
+  tiled copy, permute + pool of K, V into the bf16 operand layout, routing
+  from the means, one-tile walks with natural-order Q and O; one head's lists
+  against the oracle's routing (near-ties excepted) and every query tile of
+  it against the oracle on the GPU's lists.
 """
 import math
 
@@ -32,7 +38,7 @@ from oracle import masks as OM
 from oracle import routing as OR
 from synth import CONFIGS
 from tests.gpu_util import announce, errors, inputs, layouts, to_device
-from tests.test_gpu_b_quant_route import _accept_topp
+from tests.test_gpu_b_quant_route import _accept_topk, _accept_topp
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +183,34 @@ def test_window_480p_per_tile_walk_every_tile_of_one_head():
     real = OL.token_order(olay1) >= 0
     _gate(g[0, 0, real], O[0, 0, real], lse[0, h].cpu().numpy()[real], L[0, 0, real],
           "480p window per-tile walk head 5")
+
+
+def test_topk32_bench_pipeline_every_tile_of_one_head():
+    cfg = CONFIGS["topk32_16x32x32"]
+    _, blay = layouts(cfg)
+    q, k, v = inputs(cfg.name)
+    h = 7
+    announce("full-size: top-32 layer through the bench's calls, head 7, all 256 tiles")
+    qn, kn, vn = (to_device(x, "bf16") for x in (q, k, v))
+    _, qp = vsa.tile_permute_pool(blay, qn, means_only=True)
+    kt, kp = vsa.tile_permute_pool(blay, kn)
+    vt = vsa.tile_permute_v(blay, vn)
+    idx, cnt, _ = vsa.build_mask_topk_pooled(blay, qp, kp, top_k=cfg.top_k)
+    out, lse = vsa.block_sparse_attn_fwd_nat(blay, qn, kt, vt, idx, cnt, want_lse=True, v_operand=True)
+    torch.cuda.synchronize()
+    olay1, qo = _one_head(cfg, q, h)
+    _, ko = _one_head(cfg, k, h)
+    _, vo = _one_head(cfg, v, h)
+    sigma = 1.0 / math.sqrt(cfg.head_dim)
+    s = OR.coarse_scores(OR.pool_tiles(qo, olay1), OR.pool_tiles(ko, olay1), sigma)
+    ridx, rcnt = OR.select_lists_vectorized(s, top_k=cfg.top_k)
+    gi, gc = idx[0, h].cpu().numpy(), cnt[0, h].cpu().numpy()
+    lists = [sorted(gi[t, :gc[t]].tolist()) for t in range(olay1.n_tiles)]
+    bad = [t for t in range(olay1.n_tiles)
+           if not _accept_topk(lists[t], ridx[0, 0, t, :rcnt[0, 0, t]].tolist(), s[0, 0, t], cfg.top_k)]
+    assert not bad, f"head {h}: {len(bad)} lists differ beyond near-ties"
+    O, L = OA.attention(qo, ko, vo, olay1, OA.shared_lists(lists), sigma)
+    g = OL.permute(out[:, :, [h]].float().cpu().numpy(), olay1)
+    real = OL.token_order(olay1) >= 0
+    _gate(g[0, 0, real], O[0, 0, real], lse[0, h].cpu().numpy()[real], L[0, 0, real],
+          "top-32 bench pipeline head 7")
