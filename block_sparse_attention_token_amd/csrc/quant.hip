@@ -159,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(DevLayout L, const uint
 // t / chunks + groups * m (groups = 256 / chunks), at most kNatRows rows.
 constexpr int kNatRows = 8;
 
-template <bool VOP, bool POOL>
+// CT, DT: tile tokens and head_dim fixed at compile time (0: taken from L),
+// so that the common 64-token, 128-channel tile runs without per-row tests.
+template <bool VOP, bool POOL, int CT = 0, int DT = 0>
 __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const uint4* __restrict__ x,
                                                              uint2* __restrict__ codes,
                                                              float* __restrict__ scales,
@@ -167,15 +169,16 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
   const int b = blockIdx.z;
-  const int chunks = L.d >> 3;
+  const int C = CT ? CT : L.C, d = DT ? DT : L.d;
+  const int chunks = d >> 3;
   const int groups = kThreads / chunks;
   const int ch = threadIdx.x % chunks;
   const int rg = threadIdx.x / chunks;
   const long long bh = (long long)b * L.heads + head;
-  const long long row0 = bh * L.n_padded + (long long)tile * L.C;
+  const long long row0 = bh * L.n_padded + (long long)tile * C;
   // natural position of each row of the tile, found once per row
   __shared__ int nat_of[kThreads * kNatRows];           // C <= 8 * groups <= 2048 rows
-  for (int r = threadIdx.x; r < L.C; r += kThreads) nat_of[r] = natural_index(L, tile, r);
+  for (int r = threadIdx.x; r < C; r += kThreads) nat_of[r] = natural_index(L, tile, r);
   __syncthreads();
   uint4 xr[kNatRows];
   float amax = 0.0f;
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
   for (int m = 0; m < kNatRows; ++m) {
     const int r = rg + groups * m;
     xr[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (rg < groups && r < L.C) {
+    if (rg < groups && r < C) {
       const int nat = nat_of[r];
       if (nat >= 0) xr[m] = x[(((long long)b * L.n_tokens + nat) * L.heads + head) * chunks + ch];
     }
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
 #pragma unroll
   for (int m = 0; m < kNatRows; ++m) {
     const int r = rg + groups * m;
-    if (rg >= groups || r >= L.C) continue;
+    if (rg >= groups || r >= C) continue;
     uint2 out = make_uint2(0u, 0u);
     if (a != 0.0f) {
       const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
 #pragma unroll
     for (int m = 0; m < kNatRows; ++m) {
       const int r = rg + groups * m;
-      if (rg >= groups || r >= L.C || nat_of[r] < 0) continue;
+      if (rg >= groups || r >= C || nat_of[r] < 0) continue;
       const uint32_t ws[4] = {xr[m].x, xr[m].y, xr[m].z, xr[m].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -238,11 +241,11 @@ __global__ __launch_bounds__(kThreads) void quant_nat_kernel(DevLayout L, const 
     for (int e = 0; e < 8; ++e) part[threadIdx.x * 8 + e] = acc[e];
     __syncthreads();
     const int n = real_rows(L, tile_valid(L, tile));
-    for (int c = threadIdx.x; c < L.d; c += kThreads) {
+    for (int c = threadIdx.x; c < d; c += kThreads) {
       const int cch = c >> 3, ce = c & 7;
       float sum = 0.0f;
       for (int g = 0; g < groups; ++g) sum += part[(g * chunks + cch) * 8 + ce];
-      pooled[(bh * L.n_tiles + tile) * L.d + c] = n > 0 ? sum / (float)n : 0.0f;
+      pooled[(bh * L.n_tiles + tile) * d + c] = n > 0 ? sum / (float)n : 0.0f;
     }
   }
   if constexpr (VOP) {
@@ -352,10 +355,14 @@ hipError_t launch_quant_fp8_nat(const DevLayout& L, const void* x, uint8_t* code
   dim3 grid(L.n_tiles, L.heads, L.B);
   const uint4* xs = static_cast<const uint4*>(x);
   uint2* cs = reinterpret_cast<uint2*>(codes);
+  const bool c64d128 = L.C == 64 && L.d == 128;
   if (v_operand) {
-    if (L.C != 64 || L.d != 128) return hipErrorInvalidValue;
-    if (pooled) hipLaunchKernelGGL((quant_nat_kernel<true, true>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
-    else hipLaunchKernelGGL((quant_nat_kernel<true, false>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+    if (!c64d128) return hipErrorInvalidValue;
+    if (pooled) hipLaunchKernelGGL((quant_nat_kernel<true, true, 64, 128>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+    else hipLaunchKernelGGL((quant_nat_kernel<true, false, 64, 128>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+  } else if (c64d128) {
+    if (pooled) hipLaunchKernelGGL((quant_nat_kernel<false, true, 64, 128>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
+    else hipLaunchKernelGGL((quant_nat_kernel<false, false, 64, 128>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
   } else {
     if (pooled) hipLaunchKernelGGL((quant_nat_kernel<false, true>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
     else hipLaunchKernelGGL((quant_nat_kernel<false, false>), grid, dim3(kThreads), 0, s, L, xs, cs, scales, pooled);
