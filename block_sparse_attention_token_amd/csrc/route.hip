@@ -30,7 +30,8 @@ constexpr int kRowBatch = 4;      // rows whose loads a pool thread issues toget
 // also written to its tiled position in `tiled` (pad rows as zeros; no copy
 // when tiled is null), pooled is [B][heads][n_tiles][d]. Both forms give each thread the same rows and
 // chunks and sum them in the same order, so their means are bit-identical.
-template <bool MOVE>
+// CT, DT: tile tokens and head_dim fixed at compile time (0: taken from L).
+template <bool MOVE, int CT = 0, int DT = 0>
 __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4* __restrict__ q,
                                                         const uint4* __restrict__ k,
                                                         uint4* __restrict__ tiled,
@@ -41,11 +42,12 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
   const int b = MOVE ? (int)blockIdx.z : (int)(blockIdx.z >> 1);
   const int which = MOVE ? 0 : (int)(blockIdx.z & 1);
   const uint4* x = which ? k : q;
-  const int chunks = L.d >> 3;                       // 8 bf16 per chunk
+  const int C = CT ? CT : L.C, d = DT ? DT : L.d;
+  const int chunks = d >> 3;                         // 8 bf16 per chunk
   const int groups = kThreads / chunks;              // row groups summed in parallel
   const int ch = threadIdx.x % chunks;
   const int rg = threadIdx.x / chunks;
-  const long long row0 = (long long)(b * L.heads + head) * L.n_padded + (long long)tile * L.C;
+  const long long row0 = (long long)(b * L.heads + head) * L.n_padded + (long long)tile * C;
   const TileValid tv = tile_valid(L, tile);
 
   float acc[8];
@@ -54,14 +56,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
   if (rg < groups) {
     // rows rg, rg + groups, ... summed in increasing order; kRowBatch rows'
     // loads are issued before any of them is stored or summed
-    for (int r0 = rg; r0 < L.C; r0 += kRowBatch * groups) {
+    for (int r0 = rg; r0 < C; r0 += kRowBatch * groups) {
       uint4 w[kRowBatch];
       bool real[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
         const int r = r0 + u * groups;
         real[u] = false;
-        if (r >= L.C) continue;
+        if (r >= C) continue;
         if (MOVE) {
           const int nat = natural_index(L, tile, r);
           real[u] = nat >= 0;
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
         const int r = r0 + u * groups;
-        if (r >= L.C) break;
+        if (r >= C) break;
         if (MOVE && tiled) tiled[(row0 + r) * chunks + ch] = real[u] ? w[u] : make_uint4(0u, 0u, 0u, 0u);
         if (!real[u]) continue;
         const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(DevLayout L, const uint4
   __syncthreads();
   const int n = real_rows(L, tv);
   const long long out0 = (((long long)which * L.B + b) * L.heads + head) * L.n_tiles + tile;
-  for (int c = threadIdx.x; c < L.d; c += kThreads) {
+  for (int c = threadIdx.x; c < d; c += kThreads) {
     const int cch = c >> 3, ce = c & 7;
     float s = 0.0f;
     for (int g = 0; g < groups; ++g) s += part[(g * chunks + cch) * 8 + ce];
-    pooled[out0 * L.d + c] = n > 0 ? s / (float)n : 0.0f;
+    pooled[out0 * d + c] = n > 0 ? s / (float)n : 0.0f;
   }
   if (!MOVE && counts && threadIdx.x == 0 && which == 0 && b == 0 && head == 0) counts[tile] = n;
 }
@@ -516,9 +518,14 @@ hipError_t launch_route_pooled(const DevLayout& L, const float* q_pooled, const 
 
 hipError_t launch_permute_pool(const DevLayout& L, const void* src, void* dst, float* pooled,
                                hipStream_t s) {
-  hipLaunchKernelGGL(pool_kernel<true>, dim3(L.n_tiles, L.heads, L.B), dim3(kThreads), 0, s, L,
-                     static_cast<const uint4*>(src), nullptr, static_cast<uint4*>(dst), pooled,
-                     nullptr);
+  const dim3 grid(L.n_tiles, L.heads, L.B);
+  const uint4* sp = static_cast<const uint4*>(src);
+  if (L.C == 64 && L.d == 128)
+    hipLaunchKernelGGL((pool_kernel<true, 64, 128>), grid, dim3(kThreads), 0, s, L, sp, nullptr,
+                       static_cast<uint4*>(dst), pooled, nullptr);
+  else
+    hipLaunchKernelGGL((pool_kernel<true>), grid, dim3(kThreads), 0, s, L, sp, nullptr,
+                       static_cast<uint4*>(dst), pooled, nullptr);
   return hipGetLastError();
 }
 
