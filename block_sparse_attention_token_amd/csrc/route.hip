@@ -387,6 +387,7 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
     int count;
     uint32_t T;
     int need_tied;                               // tiles with key == T to keep, lowest indices first
+    int n_tied;                                  // tiles with key == T
     if (top_p > 0.0f) {
       float ev[MT];
       float zl = 0.0f;
@@ -407,6 +408,7 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
       const int above = count_gt(T);
       const int tied = count_ge(T) - above;
       need_tied = tied;
+      n_tied = tied;
       if (tied > 1) {
         float cum = T == 0xFFFFFFFFu ? 0.0f : mass_ge(T + 1u);
         need_tied = 0;
@@ -423,15 +425,29 @@ __global__ __launch_bounds__(THREADS) void route_kernel(DevLayout L, const float
       if (count < k_floor && count < n_valid) {
         count = min(k_floor, n_valid);
         T = search_count(count);
-        need_tied = count - count_gt(T);
+        const int gt = count_gt(T);
+        need_tied = count - gt;
+        n_tied = count_ge(T) - gt;
       }
     } else {
       count = min(top_k, n_valid);
       T = search_count(count);
-      need_tied = count - count_gt(T);
+      const int gt = count_gt(T);
+      need_tied = count - gt;
+      n_tied = count_ge(T) - gt;
     }
-    // write the kept tiles in ascending order
+    // write the kept tiles in ascending order; when every tile at the
+    // threshold is kept (the common case) no tie ranks are needed
     int base = 0, tied_seen = 0;
+    if (need_tied == n_tied) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bool keep = key[m] != 0u && key[m] >= T;
+        const unsigned long long kmask = __ballot(keep);
+        if (keep) out_idx[base + __popcll(kmask & below)] = lane + 64 * m;
+        base += __popcll(kmask);
+      }
+    } else
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const bool is_tied = key[m] == T && key[m] != 0u;
