@@ -544,8 +544,8 @@ def main():
                     help="also launch one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the block-sparse attention path has no multi-GPU "
-              "mode in this build; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the block-sparse attention path on "
+              "one GPU (no multi-GPU mode); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
