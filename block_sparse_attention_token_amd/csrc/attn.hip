@@ -1009,15 +1009,19 @@ __device__ __forceinline__ float f8_exp_pack(const f32x16_t (&s)[2], float cs, f
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int mb = i >> 2, r0 = 4 * (i & 3);
-    const float p0 = fast_exp2(fmaf(s[mb][r0 + 0], cs, e0));
+    const float x0 = fmaf(s[mb][r0 + 0], cs, e0);
+    const float p0 = fast_exp2(x0);
     const float p1 = fast_exp2(fmaf(s[mb][r0 + 1], cs, e0));
     const float p2 = fast_exp2(fmaf(s[mb][r0 + 2], cs, e0));
     const float p3 = fast_exp2(fmaf(s[mb][r0 + 3], cs, e0));
     if constexpr (VSUM) {
-      acc0 += p0 + p1;
-      acc1 += p2 + p3;
+      acc0 = i == 0 ? p0 + p1 : acc0 + (p0 + p1);
+      acc1 = i == 0 ? p2 + p3 : acc1 + (p2 + p3);
     }
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+    // the second conversion fills the upper half that the first leaves as it
+    // was, so the first may start from any dead word (here x0's) rather than
+    // a zero that would take a move
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(x0), false);
     pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
   }
   return acc0 + acc1;
