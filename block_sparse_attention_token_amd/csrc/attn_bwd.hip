@@ -167,15 +167,23 @@ __global__ __launch_bounds__(256) void transpose_lists_kernel(int n_tiles, const
   if (tid == 0) q_cnt[lh * n_tiles + j] = total;
 }
 
+// Row padding of the LDS blocks, in 16-byte chunks. With 32 bytes the four
+// consecutive rows that one 16-lane group of a transposed read
+// (ds_read_b64_tr_b16, 32 bytes per row) touches start 8 banks apart and do
+// not overlap; with 16 bytes they overlapped by half. Measured on the 768p
+// Skiparse backward: 118.4 -> 108.5-112.5 ms (dK/dV gains most; 48 bytes for
+// dQ is no better, 64 bytes costs 9 ms; dK/dV cannot take more than 32 and
+// keep two workgroups per CU).
+constexpr int kPadDq = 2, kPadDkv = 2;
+
 // ---------------------------------------------------------------------------
 // Register staging of one 32-token block (32 rows x D channels, row-major in
-// HBM) and its store into LDS rows padded by 16 bytes (the 16 rows a
-// half-wave reads at one column then start 16 bytes apart: all banks).
-template <int D, int THREADS, bool F32IN>
+// HBM) and its store into padded LDS rows (PAD chunks of 16 bytes per row).
+template <int D, int THREADS, bool F32IN, int PAD>
 struct RowBlock {
   static constexpr int ES = F32IN ? 4 : 2;
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int RS = CPR + 1;                // padded row stride, uint4
+  static constexpr int RS = CPR + PAD;              // padded row stride, uint4
   static constexpr int RSE = RS * 8;                // padded row stride, bf16 elements
   static constexpr int CHUNKS = 32 * CPR;
   static constexpr int PER_T = (CHUNKS + THREADS - 1) / THREADS;
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(2 * C * QPW) __attribute__((amdgpu_waves_per_eu(2, 
 void dq_kernel(DevLayout L, BwdArgs a, int n_work) {
   constexpr int WPQ = C / 32, THREADS = 64 * WPQ * QPW, SUB = C / 32;
   constexpr int ES = F32IN ? 4 : 2;
-  using RB = RowBlock<D, THREADS, F32IN>;
+  using RB = RowBlock<D, THREADS, F32IN, kPadDq>;
   __shared__ uint4 k_lds[2][RB::LDS];
   __shared__ uint4 v_lds[2][RB::LDS];
   __shared__ int sched[QPW > 1 ? 4096 : 1];
@@ -470,11 +478,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Copies of one 32-row block into padded LDS rows (RowBlock's layout) by the
 // WAVES waves of a workgroup: copy j of a wave covers LDS chunks
-// 64*(wave + WAVES*j) + lane, i.e. row p / RS, chunk p % RS (the pad chunk
-// takes a copy of the row's last chunk; it is never read).
-template <int D, int WAVES>
+// 64*(wave + WAVES*j) + lane, i.e. row p / RS, chunk p % RS (pad chunks
+// take a copy of the row's last chunk; they are never read).
+template <int D, int WAVES, int PAD>
 struct BlockCopy {
-  static constexpr int CPR = D / 8, RS = CPR + 1, CHUNKS = 32 * RS;
+  static constexpr int CPR = D / 8, RS = CPR + PAD, CHUNKS = 32 * RS;
   static constexpr int NI = (CHUNKS + 63) / 64;           // copies per block
   static constexpr int NIW0 = (NI + WAVES - 1) / WAVES;   // copies of wave 0 (the most)
   static constexpr int NIW1 = NI / WAVES;                 // of the last wave
@@ -538,8 +546,8 @@ void dkv16_kernel(DevLayout L, BwdArgs a, int n_work) {
   constexpr int NCT = D / WAVES / 16, NKT = WAVES;    // channel and key tiles of a wave's dK/dV
   constexpr int ES = F32IN ? 4 : 2;
   constexpr bool DMA = !F32IN;
-  using RB = RowBlock<D, THREADS, F32IN>;
-  using BC = BlockCopy<D, WAVES>;
+  using RB = RowBlock<D, THREADS, F32IN, kPadDkv>;
+  using BC = BlockCopy<D, WAVES, kPadDkv>;
   constexpr int RSE = RB::RSE;
   __shared__ uint4 q_s0[RB::LDS], q_s1[RB::LDS], q_s2[RB::LDS];
   __shared__ uint4 g_s0[RB::LDS], g_s1[RB::LDS], g_s2[RB::LDS];
